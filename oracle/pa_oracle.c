@@ -1,0 +1,358 @@
+/*
+ * pa_oracle.c -- plain, slow, fp64 CPU oracle for the paged KV-cache write and
+ * single-query paged decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant generator with the HIP library; it depends on
+ * libc and libm only.
+ *
+ * What it follows:
+ *  - "vLLM: Easy, Fast, and Cheap LLM Serving with PagedAttention" (Hacker News
+ *    thread), comments contrasting FlashAttention with PagedAttention: both
+ *    compute exact attention; paging only changes where keys and values live.
+ *    So the decode result is the plain definition out = softmax(scale*q.K^T).V
+ *    over the logical tokens 0..L-1 of the sequence, written out here.
+ *  - "vLLM Project Update" talk transcript, PagedAttention recap: attention that
+ *    works on fixed-size blocks of the KV cache, with per-sequence
+ *    logical->physical block maps managed like virtual memory pages.
+ *  - "[core] Multi Step Scheduling" pull request (vllm-project/vllm #7000),
+ *    review thread on ops.advance_step: the per-step GPU state is a slot
+ *    mapping, per-sequence block tables, sequence lengths and a block size.
+ *
+ * Storage convention shared with the GPU library (a format both sides must
+ * agree on, not arithmetic):
+ *   key cache   [num_blocks][num_kv_heads][block_size][head_dim]
+ *   value cache [num_blocks][num_kv_heads][head_dim][block_size]
+ *   slot s -> block s / block_size, offset s % block_size.
+ *
+ * Every floating-point step is done in double precision.  Half and bfloat16
+ * inputs are decoded from their bit patterns by the IEEE-754 / bfloat16
+ * definitions (sign, biased exponent, significand), not by any hardware
+ * conversion.  The softmax is the two-pass form: max, then exp/sum, so its
+ * arithmetic differs on purpose from an online (streaming) softmax.
+ *
+ * Parity pins (tests/test_oracle.py): contiguous brute force in numpy, the
+ * half/bfloat16 decoders against numpy/torch over all 65536 patterns, a
+ * hand-worked cache-write layout fixture, block-permutation and block-size
+ * invariance, L=1 -> V, identical keys -> mean(V), one-hot probe -> V[t*],
+ * scale 0 -> mean(V), GQA == replicated MHA.  No function here is unpinned.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_F16 1
+#define ORC_BF16 2
+
+#define ORC_OK 0
+#define ORC_ERR_ARG -1
+#define ORC_ERR_SLOT -2
+#define ORC_ERR_BLOCK -3
+#define ORC_ERR_LEN -4
+#define ORC_ERR_MEM -5
+
+/* ---- element decoding --------------------------------------------------- */
+
+/* IEEE-754 binary16: 1 sign, 5 exponent (bias 15), 10 significand bits. */
+double orc_f16_bits_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int expo = (h >> 10) & 0x1f;
+  int man = h & 0x3ff;
+  double v;
+  if (expo == 0) {
+    v = ldexp((double)man, -24); /* subnormal: man * 2^(1-15-10) */
+  } else if (expo == 31) {
+    v = man ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(man + 1024), expo - 25); /* (1.man) * 2^(expo-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* bfloat16: the upper half of an IEEE-754 binary32: 1 sign, 8 exponent
+ * (bias 127), 7 significand bits. */
+double orc_bf16_bits_to_double(uint16_t b) {
+  int sign = (b >> 15) & 1;
+  int expo = (b >> 7) & 0xff;
+  int man = b & 0x7f;
+  double v;
+  if (expo == 0) {
+    v = ldexp((double)man, -133); /* subnormal: man * 2^(1-127-7) */
+  } else if (expo == 255) {
+    v = man ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(man + 128), expo - 134); /* (1.man) * 2^(expo-127) */
+  }
+  return sign ? -v : v;
+}
+
+/* IEEE-754 binary32 decoded the same way (1/8/23). */
+double orc_f32_bits_to_double(uint32_t f) {
+  int sign = (f >> 31) & 1;
+  int expo = (f >> 23) & 0xff;
+  uint32_t man = f & 0x7fffffu;
+  double v;
+  if (expo == 0) {
+    v = ldexp((double)man, -149);
+  } else if (expo == 255) {
+    v = man ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(man + 0x800000u), expo - 150);
+  }
+  return sign ? -v : v;
+}
+
+/* 65536-entry decode tables, each entry produced by the decoder above; they
+ * only save the repeated ldexp calls on large inputs. */
+static double g_f16_table[65536];
+static double g_bf16_table[65536];
+static pthread_once_t g_tables_once = PTHREAD_ONCE_INIT;
+
+static void orc_fill_tables(void) {
+  for (uint32_t i = 0; i < 65536; ++i) {
+    g_f16_table[i] = orc_f16_bits_to_double((uint16_t)i);
+    g_bf16_table[i] = orc_bf16_bits_to_double((uint16_t)i);
+  }
+}
+
+static int orc_elem_bytes(int dtype) {
+  switch (dtype) {
+    case ORC_F32: return 4;
+    case ORC_F16: return 2;
+    case ORC_BF16: return 2;
+    default: return 0;
+  }
+}
+
+/* Element idx of an array of the given dtype, as a double. */
+static double orc_load(const void* base, int dtype, int64_t idx) {
+  if (dtype == ORC_F32) {
+    uint32_t bits;
+    memcpy(&bits, (const char*)base + idx * 4, 4);
+    return orc_f32_bits_to_double(bits);
+  }
+  uint16_t bits;
+  memcpy(&bits, (const char*)base + idx * 2, 2);
+  return dtype == ORC_F16 ? g_f16_table[bits] : g_bf16_table[bits];
+}
+
+/* ---- cache write (reshape-and-cache) ------------------------------------ */
+
+/*
+ * For every token i with slot_mapping[i] >= 0, copy its key row and value
+ * row, for every kv head, into the slot's physical block, as raw bits.
+ * Tokens are applied in increasing i.  A negative slot means "skip" (padding).
+ * k is read at k[i*k_token_stride + h*head_dim + e]; likewise v.
+ * Returns ORC_ERR_SLOT (and stops) on a slot >= num_blocks*block_size.
+ */
+int orc_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
+                    int64_t num_tokens, int64_t k_token_stride,
+                    int64_t v_token_stride, void* k_cache, void* v_cache,
+                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                    int32_t block_size, int32_t dtype) {
+  int eb = orc_elem_bytes(dtype);
+  if (!eb || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || num_tokens < 0)
+    return ORC_ERR_ARG;
+  const int64_t H = num_kv_heads, D = head_dim, BS = block_size;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    if (slot >= num_blocks * BS) return ORC_ERR_SLOT;
+    int64_t blk = slot / BS;
+    int64_t off = slot % BS;
+    for (int64_t h = 0; h < H; ++h) {
+      for (int64_t e = 0; e < D; ++e) {
+        int64_t src_k = i * k_token_stride + h * D + e;
+        int64_t src_v = i * v_token_stride + h * D + e;
+        int64_t dst_k = ((blk * H + h) * BS + off) * D + e;
+        int64_t dst_v = ((blk * H + h) * D + e) * BS + off;
+        memcpy((char*)k_cache + dst_k * eb, (const char*)k + src_k * eb, eb);
+        memcpy((char*)v_cache + dst_v * eb, (const char*)v + src_v * eb, eb);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ---- decode attention --------------------------------------------------- */
+
+typedef struct {
+  double* out;
+  const void* q;
+  int32_t q_dtype;
+  const void* k_cache;
+  const void* v_cache;
+  int32_t kv_dtype;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int64_t num_blocks;
+  int32_t block_size, max_blocks_per_seq;
+  double scale;
+  const int64_t* rows; /* b*num_q_heads + hq, or NULL for all rows */
+  int64_t n_rows;
+  int32_t n_threads;
+  int32_t thread_id;
+  int status;
+} orc_decode_job;
+
+/*
+ * One output row (b, hq): out[e] = sum_t w_t v_t[e] / sum_t w_t with
+ * s_t = scale * sum_e q[e] k_t[e], m = max_t s_t, w_t = exp(s_t - m),
+ * t over the logical positions 0..L-1, K/V rows found through the block
+ * table: position t lives in physical block block_tables[b][t / bs] at
+ * offset t % bs.  q head hq reads kv head hq / (Hq / Hkv).
+ */
+static int orc_decode_row(const orc_decode_job* J, int64_t row) {
+  const int64_t Hq = J->num_q_heads, Hkv = J->num_kv_heads, D = J->head_dim;
+  const int64_t BS = J->block_size, MB = J->max_blocks_per_seq;
+  const int64_t b = row / Hq, hq = row % Hq;
+  const int64_t group = Hq / Hkv;
+  const int64_t hk = hq / group;
+  const int64_t L = J->context_lens[b];
+  if (L < 1 || L > MB * BS) return ORC_ERR_LEN;
+
+  double* s = (double*)malloc((size_t)L * sizeof(double));
+  double* acc = (double*)malloc((size_t)D * sizeof(double));
+  if (!s || !acc) {
+    free(s);
+    free(acc);
+    return ORC_ERR_MEM;
+  }
+
+  /* scores */
+  for (int64_t t = 0; t < L; ++t) {
+    int64_t phys = J->block_tables[b * MB + t / BS];
+    if (phys < 0 || phys >= J->num_blocks) {
+      free(s);
+      free(acc);
+      return ORC_ERR_BLOCK;
+    }
+    int64_t krow = ((phys * Hkv + hk) * BS + t % BS) * D;
+    double dot = 0.0;
+    for (int64_t e = 0; e < D; ++e)
+      dot += orc_load(J->q, J->q_dtype, (b * Hq + hq) * D + e) *
+             orc_load(J->k_cache, J->kv_dtype, krow + e);
+    s[t] = J->scale * dot;
+  }
+
+  /* two-pass softmax: max, then weights and their sum (increasing t) */
+  double m = s[0];
+  for (int64_t t = 1; t < L; ++t)
+    if (s[t] > m) m = s[t];
+  double z = 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    s[t] = exp(s[t] - m);
+    z += s[t];
+  }
+
+  /* weighted sum of value rows */
+  for (int64_t e = 0; e < D; ++e) acc[e] = 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    int64_t phys = J->block_tables[b * MB + t / BS];
+    for (int64_t e = 0; e < D; ++e) {
+      int64_t vidx = ((phys * Hkv + hk) * D + e) * BS + t % BS;
+      acc[e] += s[t] * orc_load(J->v_cache, J->kv_dtype, vidx);
+    }
+  }
+  for (int64_t e = 0; e < D; ++e) J->out[row * D + e] = acc[e] / z;
+
+  free(s);
+  free(acc);
+  return ORC_OK;
+}
+
+static void* orc_decode_worker(void* arg) {
+  orc_decode_job* J = (orc_decode_job*)arg;
+  int64_t total = J->rows ? J->n_rows : (int64_t)J->num_seqs * J->num_q_heads;
+  for (int64_t i = J->thread_id; i < total; i += J->n_threads) {
+    int64_t row = J->rows ? J->rows[i] : i;
+    int st = orc_decode_row(J, row);
+    if (st != ORC_OK) {
+      J->status = st;
+      break;
+    }
+  }
+  return NULL;
+}
+
+/*
+ * Decode attention for all rows (rows == NULL) or for the listed rows
+ * (row = b*num_q_heads + hq).  out is double [num_seqs][num_q_heads][head_dim];
+ * only computed rows are written.  Rows are independent, so they are spread
+ * over n_threads POSIX threads; each row's arithmetic is sequential.
+ */
+int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
+               const void* v_cache, int32_t kv_dtype,
+               const int32_t* block_tables, const int32_t* context_lens,
+               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+               int32_t head_dim, int64_t num_blocks, int32_t block_size,
+               int32_t max_blocks_per_seq, float scale, const int64_t* rows,
+               int64_t n_rows, int32_t n_threads) {
+  if (!orc_elem_bytes(q_dtype) || !orc_elem_bytes(kv_dtype)) return ORC_ERR_ARG;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return ORC_ERR_ARG;
+  if (rows) {
+    for (int64_t i = 0; i < n_rows; ++i)
+      if (rows[i] < 0 || rows[i] >= (int64_t)num_seqs * num_q_heads)
+        return ORC_ERR_ARG;
+  }
+  pthread_once(&g_tables_once, orc_fill_tables);
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+
+  orc_decode_job jobs[256];
+  pthread_t tids[256];
+  for (int i = 0; i < n_threads; ++i) {
+    orc_decode_job* J = &jobs[i];
+    J->out = out;
+    J->q = q;
+    J->q_dtype = q_dtype;
+    J->k_cache = k_cache;
+    J->v_cache = v_cache;
+    J->kv_dtype = kv_dtype;
+    J->block_tables = block_tables;
+    J->context_lens = context_lens;
+    J->num_seqs = num_seqs;
+    J->num_q_heads = num_q_heads;
+    J->num_kv_heads = num_kv_heads;
+    J->head_dim = head_dim;
+    J->num_blocks = num_blocks;
+    J->block_size = block_size;
+    J->max_blocks_per_seq = max_blocks_per_seq;
+    J->scale = (double)scale;
+    J->rows = rows;
+    J->n_rows = n_rows;
+    J->n_threads = n_threads;
+    J->thread_id = i;
+    J->status = ORC_OK;
+  }
+  if (n_threads == 1) {
+    orc_decode_worker(&jobs[0]);
+    return jobs[0].status;
+  }
+  int started = 0;
+  for (int i = 0; i < n_threads; ++i) {
+    if (pthread_create(&tids[i], NULL, orc_decode_worker, &jobs[i]) != 0) break;
+    ++started;
+  }
+  /* any thread that failed to start: run its share here */
+  for (int i = started; i < n_threads; ++i) orc_decode_worker(&jobs[i]);
+  for (int i = 0; i < started; ++i) pthread_join(tids[i], NULL);
+  for (int i = 0; i < n_threads; ++i)
+    if (jobs[i].status != ORC_OK) return jobs[i].status;
+  return ORC_OK;
+}
+
+/* Decoders exposed in bulk for the pins: out[i] = decode(bits[i]). */
+void orc_decode_bits(const void* bits, int32_t dtype, int64_t n, double* out) {
+  pthread_once(&g_tables_once, orc_fill_tables);
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_load(bits, dtype, i);
+}

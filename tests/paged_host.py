@@ -1,0 +1,62 @@
+"""Host-side helpers for the tests: the oracle's view of a seeded workload.
+
+Builds the oracle's own paged caches (numpy raw bits, NaN-poisoned) from the
+same seeded inputs the GPU receives, and the contiguous float64 copies of each
+sequence's K/V that the brute-force pin uses.  Nothing here reads GPU results.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from pagedattention_kv_cache_amd.workloads import POISON_BITS, Workload, raw_bits
+
+_BITS_NP = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
+
+
+def poisoned_pool(wl: Workload, transposed: bool) -> np.ndarray:
+    c = wl.cfg
+    shape = ((wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size) if transposed else
+             (wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim))
+    return np.full(shape, POISON_BITS[c.dtype], dtype=_BITS_NP[c.dtype])
+
+
+class OracleState:
+    """The oracle's caches for a workload, advanced step by step like the GPU's."""
+
+    def __init__(self, wl: Workload, seqs: list[int] | None = None):
+        self.wl = wl
+        c = wl.cfg
+        self.kc = poisoned_pool(wl, transposed=False)
+        self.vc = poisoned_pool(wl, transposed=True)
+        self.q = wl.queries()
+        self.step_k, self.step_v = wl.step_kv()
+        for b in (range(c.num_seqs) if seqs is None else seqs):
+            k, v = wl.prior_kv(b)
+            if k.shape[0]:
+                oracle.cache_write(raw_bits(k), raw_bits(v), wl.prior_slots(b), self.kc, self.vc,
+                                   c.dtype)
+        self.steps_written = 0
+
+    def write_step(self, step: int) -> None:
+        c = self.wl.cfg
+        oracle.cache_write(raw_bits(self.step_k[step]), raw_bits(self.step_v[step]),
+                           self.wl.step_slots(step), self.kc, self.vc, c.dtype)
+        self.steps_written = step + 1
+
+    def decode(self, step: int, rows: np.ndarray | None = None, threads: int = 8) -> np.ndarray:
+        c = self.wl.cfg
+        return oracle.decode(raw_bits(self.q[step]), c.dtype, self.kc, self.vc, c.dtype,
+                             self.wl.block_tables, self.wl.context_lens(step), c.attn_scale(),
+                             rows=rows, threads=threads)
+
+
+def logical_kv(wl: Workload, b: int, step: int) -> tuple[np.ndarray, np.ndarray]:
+    """Contiguous float64 K, V [L][Hkv][d] of sequence b as attended at `step`
+    (decoded by torch, not by the oracle)."""
+    k, v = wl.prior_kv(b)
+    sk, sv = wl.step_kv()
+    k = torch.cat([k, sk[:step + 1, b]], 0)
+    v = torch.cat([v, sv[:step + 1, b]], 0)
+    return k.to(torch.float64).numpy(), v.to(torch.float64).numpy()
