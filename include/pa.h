@@ -1,0 +1,168 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged KV-cache library (libpa.so).
+ *
+ * Two operations make up the decode hot path of paged attention:
+ *
+ *   pa_cache_write  scatter each new token's key and value rows into
+ *                   fixed-size physical cache blocks through a slot mapping
+ *                   ("[core] Multi Step Scheduling" pull request, vllm #7000,
+ *                   review thread on ops.advance_step: the per-step state is
+ *                   slot_mapping, block_tables, seq_lens and block_size).
+ *
+ *   pa_decode       single-query attention out = softmax(scale * q.K^T).V per
+ *                   (sequence, query head), with K/V gathered block by block
+ *                   through a per-sequence block table ("vLLM Project Update"
+ *                   talk, PagedAttention recap: attention over blocks of the
+ *                   KV cache managed like virtual-memory pages).  The result is
+ *                   exact attention ("vLLM: Easy, Fast, and Cheap LLM Serving
+ *                   with PagedAttention" thread: paging changes where K/V live,
+ *                   not what is computed).  Long or uneven contexts are split
+ *                   into partitions whose partial results are merged with a
+ *                   log-sum-exp reduction (same talk, passage on the second
+ *                   PagedAttention kernel, "similar to flash decoding").
+ *
+ * Conventions
+ *   - All tensor arguments are DEVICE pointers to densely packed row-major
+ *     arrays unless a stride argument says otherwise.  The caller owns every
+ *     buffer; the library allocates no device memory and keeps no state
+ *     between calls.  Calls from several host threads are safe.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued: PA_OK means "validated and launched", nothing is waited for,
+ *     and no device->host copy is made (grids are sized from the maximum
+ *     context, max_blocks_per_seq * block_size, not from context_lens).
+ *   - Errors are reported by the return value: a negative pa_status, detected
+ *     on the host before anything is launched (or PA_ERR_HIP if a launch
+ *     fails).  No C++ exception crosses this interface.
+ *   - Cache layout (chosen for gfx950, see each kernel):
+ *       key cache   [num_blocks][num_kv_heads][block_size][head_dim]
+ *       value cache [num_blocks][num_kv_heads][head_dim][block_size]
+ *     so a token's key row is one contiguous head_dim run and, for one
+ *     dimension, a block's values for consecutive tokens are contiguous.
+ *   - Slot s addresses block s / block_size, offset s % block_size.
+ *   - Block-table entries and slots are preconditions: entries
+ *     block_tables[b][0 .. ceil(L_b/block_size)-1] must lie in
+ *     [0, num_blocks); slots must be < num_blocks * block_size.  Entries past a
+ *     sequence's last block are never read and may hold anything (e.g. -1).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,  /* IEEE binary32 */
+  PA_DTYPE_F16 = 1,  /* IEEE binary16 */
+  PA_DTYPE_BF16 = 2  /* bfloat16 */
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  PA_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
+  PA_ERR_UNSUPPORTED = -4, /* head_dim / block_size / group size not built */
+  PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  PA_ERR_HIP = -6          /* a HIP launch failed */
+} pa_status;
+
+/* pa_decode flags: which decode kernel family to use. */
+#define PA_DECODE_AUTO 0u      /* library picks */
+#define PA_DECODE_FORCE_VALU 1u /* vector-ALU kernel (all dtypes) */
+#define PA_DECODE_FORCE_MFMA 2u /* matrix-core kernel (f16/bf16 KV only) */
+
+/*
+ * pa_cache_write -- for every token i in [0, num_tokens) whose
+ * slot_mapping[i] >= 0, copy k[i][h][:] into
+ * k_cache[slot / block_size][h][slot % block_size][:] and v[i][h][:] into
+ * v_cache[slot / block_size][h][:][slot % block_size], for all kv heads h, as
+ * raw bits.  Tokens with a negative slot are skipped (padding).  All other
+ * cache bytes are left unchanged.
+ *
+ *   k, v            device, dtype, token i / head h / dim e at
+ *                   k[i * k_token_stride + h * head_dim + e]; the heads of a
+ *                   token are packed (stride head_dim), tokens may be strided
+ *                   (k_token_stride >= num_kv_heads * head_dim, in elements)
+ *   slot_mapping    device int64 [num_tokens]
+ *   k_cache,v_cache device, dtype, layouts above
+ *   dtype           pa_dtype of k, v and both caches (must match)
+ *   head_dim        64, 128 or 256;  block_size: 8, 16, 32 or 64
+ * Duplicate non-negative slots within one call race (undefined which wins).
+ * num_tokens == 0 is a valid no-op.
+ */
+int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int64_t num_tokens, int64_t k_token_stride,
+                   int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
+                   int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * pa_decode -- out[b][hq][:] = sum_t softmax_t(scale * q[b][hq] . K_t) V_t
+ * over the logical positions t in [0, context_lens[b]) of sequence b, where
+ * position t is found in physical block block_tables[b][t / block_size] at
+ * offset t % block_size, and query head hq reads kv head
+ * hq / (num_q_heads / num_kv_heads).
+ *
+ *   out            device [num_seqs][num_q_heads][head_dim], out_dtype
+ *                  (f32, or the kv dtype)
+ *   q              device [num_seqs][num_q_heads][head_dim], q_dtype
+ *                  (f32, or the kv dtype)
+ *   k_cache,v_cache device, kv_dtype, layouts above, num_blocks blocks
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   device int32 [num_seqs]; 1 <= L <= max_blocks_per_seq *
+ *                  block_size (a sequence with L == 0 gets an all-zero row)
+ *   scale          softmax scale (typically 1/sqrt(head_dim))
+ *   block_size     8, 16, 32 or 64
+ *   partition_size 0: the library picks (see pa_decode_partition_size);
+ *                  > 0: positions are processed in partitions of this many
+ *                  tokens (a multiple of block_size), merged by a
+ *                  log-sum-exp reduction; a value >= max_blocks_per_seq *
+ *                  block_size means one pass per (sequence, kv head) with no
+ *                  reduction and no workspace
+ *   head_dim       64 or 128;  num_q_heads % num_kv_heads == 0
+ *   workspace      device scratch of at least pa_decode_workspace_size(...)
+ *                  bytes for the same arguments (may be NULL when that is 0);
+ *                  its contents on entry do not matter
+ *   flags          PA_DECODE_AUTO or a PA_DECODE_FORCE_* kernel choice
+ * The result does not depend on partition_size or on the kernel family beyond
+ * floating-point rounding (fp32 accumulation throughout).
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int32_t block_size, int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+              int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
+              void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * The partition size pa_decode uses when called with partition_size == 0 and
+ * the same arguments (a pure function of them; no device query).  Returns a
+ * negative pa_status for invalid arguments.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int32_t kv_dtype, uint32_t flags);
+
+/*
+ * Workspace bytes pa_decode needs for these arguments (partition_size as
+ * passed to pa_decode, 0 allowed).  0 when a single pass suffices.  Returns 0
+ * for invalid arguments as well; pa_decode reports those.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t partition_size, int32_t kv_dtype, uint32_t flags);
+
+/* Static, library-owned text for a pa_status value. */
+const char* pa_status_string(int32_t status);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,153 @@
+"""Python binding of libpa.so, the MI355X paged KV-cache library (include/pa.h).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+sizes, and the call goes to the C ABI on torch's current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  If libpa.so is missing, :func:`lib` raises -- build it with
+``python -m pagedattention_kv_cache_amd.build`` (or ``__graft_entry__.build()``).
+
+    cache_write(k, v, slot_mapping, k_cache, v_cache)
+    decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+           block_size, partition_size=0, workspace=None, flags=AUTO)
+
+Cache tensors: ``k_cache`` [num_blocks][num_kv_heads][block_size][head_dim],
+``v_cache`` [num_blocks][num_kv_heads][head_dim][block_size].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK = 0
+AUTO, FORCE_VALU, FORCE_MFMA = 0, 1, 2
+_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pa status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: the HIP library has not been built")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                 ctypes.c_size_t)
+        L.pa_cache_write.restype = ctypes.c_int
+        L.pa_cache_write.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i64, i32, i32, vp]
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, i32,
+                                i32, i64, i32, i32, i32, i32, vp, sz, u32, vp]
+        L.pa_decode_partition_size.restype = i32
+        L.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, u32]
+        L.pa_decode_workspace_size.restype = sz
+        L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, u32]
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_status_string.argtypes = [i32]
+        L.pa_abi_version.restype = i32
+        L.pa_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PAError(status, status_string(status))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE:
+        raise PAError(-3, f"unsupported dtype {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise PAError(-2, msg)
+
+
+def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Scatter k/v [T][Hkv][d] (token dim may be strided) into the caches."""
+    _require(k.dim() == 3 and v.dim() == 3 and k.shape == v.shape, "k, v must be [T][Hkv][d]")
+    T, H, d = k.shape
+    _require(k_cache.dim() == 4 and v_cache.dim() == 4, "caches must be 4-D")
+    NB, H2, bs, d2 = k_cache.shape
+    _require((H2, d2) == (H, d) and tuple(v_cache.shape) == (NB, H, d, bs),
+             "cache shapes do not match k/v")
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    for t in (k, v):
+        _require(t.stride(2) == 1 and t.stride(1) == d, "heads of a token must be packed")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,)
+             and slot_mapping.is_contiguous(), "slot_mapping must be contiguous int64 [T]")
+    _require(k.dtype == v.dtype == k_cache.dtype == v_cache.dtype, "dtype mismatch")
+    _check(lib().pa_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                k_cache.data_ptr(), v_cache.data_ptr(), T, k.stride(0),
+                                v.stride(0), H, d, NB, bs, _dt(k), _stream(k_cache.device)))
+
+
+def decode_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          block_size: int, max_blocks_per_seq: int, kv_dtype: torch.dtype,
+                          flags: int = AUTO) -> int:
+    p = lib().pa_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, _DTYPE[kv_dtype], flags)
+    _check(min(p, 0))
+    return p
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          block_size: int, max_blocks_per_seq: int, partition_size: int,
+                          kv_dtype: torch.dtype, flags: int = AUTO) -> int:
+    return lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          block_size, max_blocks_per_seq, partition_size,
+                                          _DTYPE[kv_dtype], flags)
+
+
+def decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+           block_size: int, partition_size: int = 0, workspace: torch.Tensor | None = None,
+           flags: int = AUTO) -> None:
+    """out[b][hq] = softmax(scale * q[b][hq] . K^T) V over the paged context of b."""
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
+    B, Hq, d = q.shape
+    _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
+    NB, Hkv, bs, d2 = k_cache.shape
+    _require(bs == block_size and d2 == d, "k_cache shape does not match block_size / head_dim")
+    _require(tuple(v_cache.shape) == (NB, Hkv, d, bs), "v_cache shape does not match")
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(),
+             "block_tables must be contiguous int32 [B][max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
+             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
+    MB = block_tables.shape[1]
+    kvd = k_cache.dtype
+    need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, kvd, flags)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+                           block_size, partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(k_cache),
+                           _dt(out), ws_ptr, ws_bytes, flags, _stream(q.device)))

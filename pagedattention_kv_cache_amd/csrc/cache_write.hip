@@ -1,0 +1,84 @@
+// cache_write.hip -- the paged KV-cache slot write (reshape-and-cache).
+//
+// Every new token's key and value rows go to the slot the caller assigned
+// ("[core] Multi Step Scheduling" pull request, advance_step review thread:
+// slot_mapping next to block_tables and block_size).  A bit copy, no
+// arithmetic on values.
+//
+// Thread mapping: one thread moves one 16-byte chunk of one (token, kv head)
+// row.  Keys: the chunk lands contiguously in the token's key row, so the
+// head_dim*elem/16 threads of a row write one contiguous run (256 B for a
+// 128-wide bf16 head) -- full cache lines.  Values: the value cache is
+// [block][head][dim][block_size], so the chunk's elements go to consecutive
+// dims of one offset, block_size elements apart.
+#include "pa_device.hpp"
+#include "pa_launch.hpp"
+
+namespace pa {
+namespace {
+
+template <int EB>
+__global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int chunks_per_row) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)a.num_kv_heads * chunks_per_row;
+  const int64_t total = a.num_tokens * per_token;
+  if (gid >= total) return;
+  const int64_t t = gid / per_token;
+  const int rem = (int)(gid - t * per_token);
+  const int h = rem / chunks_per_row;
+  const int c = rem - h * chunks_per_row;
+  const int64_t slot = a.slots[t];
+  // negative = padding; a slot past the pool breaks the caller's contract and
+  // is dropped rather than written out of bounds
+  if (slot < 0 || slot >= a.num_blocks * a.block_size) return;
+  const int64_t blk = slot / a.block_size;
+  const int off = (int)(slot - blk * a.block_size);
+  constexpr int EPC = 16 / EB;  // elements per chunk
+  const int64_t D = a.head_dim;
+  const int e0 = c * EPC;
+
+  const char* ksrc = reinterpret_cast<const char*>(a.k) + ((t * a.k_stride) + h * D + e0) * EB;
+  const char* vsrc = reinterpret_cast<const char*>(a.v) + ((t * a.v_stride) + h * D + e0) * EB;
+  const uint4 kraw = ld16(ksrc);
+  const uint4 vraw = ld16(vsrc);
+
+  const int64_t head_base = blk * a.num_kv_heads + h;
+  char* kdst = reinterpret_cast<char*>(a.k_cache) + ((head_base * a.block_size + off) * D + e0) * EB;
+  *reinterpret_cast<uint4*>(kdst) = kraw;
+
+  char* vrow = reinterpret_cast<char*>(a.v_cache) + ((head_base * D + e0) * a.block_size + off) * EB;
+  const int64_t vstep = (int64_t)a.block_size * EB;
+  if constexpr (EB == 4) {
+    const uint32_t w[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(vrow + i * vstep) = w[i];
+  } else {
+    const uint32_t w[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint16_t*>(vrow + (2 * i) * vstep) = (uint16_t)(w[i] & 0xffffu);
+      *reinterpret_cast<uint16_t*>(vrow + (2 * i + 1) * vstep) = (uint16_t)(w[i] >> 16);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const int chunks = a.head_dim * a.elem_bytes / 16;
+  const int64_t total = a.num_tokens * a.num_kv_heads * chunks;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.elem_bytes == 4) {
+    hipLaunchKernelGGL(cache_write_kernel<4>, dim3((unsigned)blocks), dim3(threads), 0, stream, a,
+                       chunks);
+  } else {
+    hipLaunchKernelGGL(cache_write_kernel<2>, dim3((unsigned)blocks), dim3(threads), 0, stream, a,
+                       chunks);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

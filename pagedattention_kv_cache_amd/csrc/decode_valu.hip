@@ -1,0 +1,249 @@
+// decode_valu.hip -- paged single-query decode attention on the vector ALUs.
+//
+// One wave (64 lanes) handles one work item: a (sequence, kv head, partition)
+// with all the query heads of that kv head's group (or a chunk of at most 8 of
+// them), so every key/value byte of the item is read from HBM once.  Tokens
+// are walked in tiles of 16 through the block table ("vLLM Project Update"
+// talk, PagedAttention recap: attention over fixed-size blocks of the KV
+// cache); a partition covers partition_size tokens and long or uneven contexts
+// are split into several partitions merged later by log-sum-exp (same talk,
+// second PagedAttention kernel, "similar to flash decoding").
+//
+// Per tile:
+//  * scores: a key row (head_dim * elem bytes) is spread over RL = row/16
+//    lanes holding one 16-byte chunk each, TPI = 64/RL tokens per load
+//    instruction; each lane forms partial dots for every head of the group
+//    and a DPP butterfly within the row completes them;
+//  * online softmax in the exp2 domain (scale * log2 e folded into the
+//    scores): the tile max is made wave-uniform, so the running max m, the
+//    rescale factor and the accumulator rescale are uniform per head;
+//  * the tile's probabilities go through LDS (broadcast reads) and each lane
+//    accumulates p * v for head_dim/64 output dims from the value cache's
+//    [dim][block_size] rows: 16 consecutive tokens of one dim are one
+//    contiguous run.
+// Masking is by selection (score -inf, value term skipped), never by
+// multiplying by zero, so unused cache slots may hold anything (even NaN).
+#include "pa_device.hpp"
+#include "pa_launch.hpp"
+
+namespace pa {
+namespace {
+
+constexpr int kTile = 16;
+
+template <Elem KV, int D, int G>
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
+  constexpr int EB = ElemTraits<KV>::bytes;
+  constexpr int EPL = 16 / EB;     // elements per 16-byte chunk
+  constexpr int RL = D * EB / 16;  // lanes per key row
+  constexpr int TPI = 64 / RL;     // tokens per key load instruction
+  constexpr int NI = kTile / TPI;  // key load instructions per tile
+  constexpr int DPL = D / 64;      // value dims per lane
+  constexpr int SEG = 8;           // tokens per value load segment
+  constexpr int NSEG = kTile / SEG;
+  constexpr int VL = SEG * EB / 16;  // 16-byte loads per segment and dim
+  static_assert(RL >= 8 && RL <= 64 && 64 % RL == 0, "row layout");
+  static_assert(TPI <= SEG, "a key load instruction stays inside one block");
+
+  const int part = blockIdx.x;
+  const int b = blockIdx.z;
+  const int chunks = a.group / G;
+  const int h = blockIdx.y / chunks;
+  const int hq0 = h * a.group + (blockIdx.y % chunks) * G;
+  const int lane = threadIdx.x;
+  const int c = lane % RL;    // 16-byte chunk of the key row
+  const int row = lane / RL;  // token within a key load instruction
+
+  const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
+  const int P = a.partition_size;
+  if (L <= 0) {
+    if (part == 0) {
+      for (int g = 0; g < G; ++g)
+        for (int e = lane; e < D; e += 64)
+          store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
+    }
+    return;
+  }
+  const int n_parts = (L + P - 1) / P;
+  if (part >= n_parts) return;
+  const int t_begin = part * P;
+  const int t_end = min(t_begin + P, L);
+  const int lbs = a.log2_block_size;
+  const int bs = a.block_size;
+  const int last_blk = (L - 1) >> lbs;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+  const int64_t Hkv = a.num_kv_heads;
+
+  // query chunk for every head of the group, widened to fp32
+  float qf[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t qb = ((int64_t)b * a.num_q_heads + hq0 + g) * D + c * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[g][e] = load_elem_f32(a.q, qb + e, a.q_dtype);
+  }
+
+  __shared__ float p_lds[G][kTile];
+
+  float m[G], lrow[G], acc[G][DPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    lrow[g] = 0.0f;
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) acc[g][dd] = 0.0f;
+  }
+
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+    // ---- issue the tile's key and value loads --------------------------
+    uint4 kraw[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int tok0 = t0 + i * TPI;
+      const int64_t phys = clamp_block(bt[min(tok0 >> lbs, last_blk)], a.num_blocks);
+      const int off = (tok0 & (bs - 1)) + row;
+      kraw[i] = ld16(kc + (((phys * Hkv + h) * bs + off) * D + c * EPL) * EB);
+    }
+    uint4 vraw[DPL][NSEG][VL];
+#pragma unroll
+    for (int sgm = 0; sgm < NSEG; ++sgm) {
+      const int tok0 = t0 + sgm * SEG;
+      const int64_t phys = clamp_block(bt[min(tok0 >> lbs, last_blk)], a.num_blocks);
+      const int off = tok0 & (bs - 1);
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) {
+        const int e = lane * DPL + dd;
+        const char* p = vc + (((phys * Hkv + h) * D + e) * bs + off) * EB;
+#pragma unroll
+        for (int j = 0; j < VL; ++j) vraw[dd][sgm][j] = ld16(p + 16 * j);
+      }
+    }
+
+    // ---- scores ----------------------------------------------------------
+    float s[G][NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float kf[EPL];
+      widen16<KV>(kraw[i], kf);
+      const bool valid = (t0 + i * TPI + row) < t_end;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float part_dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) part_dot = fmaf(qf[g][e], kf[e], part_dot);
+        const float dot = group_sum<RL>(part_dot);
+        s[g][i] = valid ? dot * a.scale_log2 : -INFINITY;
+      }
+    }
+
+    // ---- online softmax (wave-uniform max per head) ---------------------
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = s[g][0];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[g][i]);
+      mx = across_groups_max<RL>(mx);
+      const float m_new = fmaxf(m[g], mx);
+      const float alpha = fast_exp2(m[g] - m_new);
+      m[g] = m_new;
+      float psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        s[g][i] = fast_exp2(s[g][i] - m_new);
+        psum += s[g][i];
+      }
+      lrow[g] = lrow[g] * alpha + psum;
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) acc[g][dd] *= alpha;
+    }
+    if (c == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) p_lds[g][i * TPI + row] = s[g][i];
+    }
+    __syncthreads();
+
+    // ---- p . V -------------------------------------------------------------
+    const int nv = min(kTile, t_end - t0);  // valid tokens in this tile
+#pragma unroll
+    for (int sgm = 0; sgm < NSEG; ++sgm) {
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) {
+        float vf[SEG];
+#pragma unroll
+        for (int j = 0; j < VL; ++j) widen16<KV>(vraw[dd][sgm][j], vf + j * (16 / EB));
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) {
+          const int t = sgm * SEG + j;
+          if (t < nv) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(p_lds[g][t], vf[j], acc[g][dd]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- finish the work item ------------------------------------------------
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float l = across_groups_sum<RL>(lrow[g]);
+    const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
+    if (n_parts == 1) {
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd)
+        store_elem(a.out, row_id * D + lane * DPL + dd, acc[g][dd] * inv, a.out_dtype);
+    } else {
+      const int64_t slot = row_id * a.max_partitions + part;
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) a.ws_acc[slot * D + lane * DPL + dd] = acc[g][dd];
+      if (lane == 0) {
+        a.ws_ml[slot * 2] = m[g];
+        a.ws_ml[slot * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+template <Elem KV, int D>
+hipError_t dispatch_g(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.heads_per_item) {
+#define PA_CASE(GG)                                                                   \
+  case GG:                                                                            \
+    hipLaunchKernelGGL((decode_valu_kernel<KV, D, GG>), grid, dim3(64), 0, s, a);     \
+    break;
+    PA_CASE(1) PA_CASE(2) PA_CASE(3) PA_CASE(4) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(8)
+#undef PA_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <Elem KV>
+hipError_t dispatch_d(const DecodeArgs& a, int head_dim, dim3 grid, hipStream_t s) {
+  if (head_dim == 64) return dispatch_g<KV, 64>(a, grid, s);
+  if (head_dim == 128) return dispatch_g<KV, 128>(a, grid, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s) {
+  const int chunks = a.group / a.heads_per_item;
+  dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * chunks), (unsigned)a.num_seqs);
+  switch (kv_dtype) {
+    case 0: return dispatch_d<Elem::F32>(a, head_dim, grid, s);
+    case 1: return dispatch_d<Elem::F16>(a, head_dim, grid, s);
+    case 2: return dispatch_d<Elem::BF16>(a, head_dim, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

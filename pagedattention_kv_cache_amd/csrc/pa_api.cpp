@@ -1,0 +1,226 @@
+// pa_api.cpp -- the C ABI declared in include/pa.h: argument validation,
+// partition-size policy, workspace sizing and kernel launches on the caller's
+// stream.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_launch.hpp"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_DTYPE_F32: return 4;
+    case PA_DTYPE_F16: return 2;
+    case PA_DTYPE_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool valid_block_size(int32_t bs) { return bs == 8 || bs == 16 || bs == 32 || bs == 64; }
+
+int log2_exact(int32_t v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest divisor of g that is <= cap: the q heads one work item handles.
+int32_t heads_per_item(int32_t g, int32_t cap) {
+  for (int32_t h = cap < g ? cap : g; h >= 1; --h)
+    if (g % h == 0) return h;
+  return 1;
+}
+
+struct DecodeShape {
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
+  int32_t kv_dtype;
+  uint32_t flags;
+};
+
+int check_shape(const DecodeShape& s) {
+  if (s.num_seqs < 0 || s.num_q_heads <= 0 || s.num_kv_heads <= 0 || s.max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (s.num_q_heads % s.num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!elem_bytes(s.kv_dtype)) return PA_ERR_DTYPE;
+  if (s.head_dim != 64 && s.head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!valid_block_size(s.block_size)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)s.max_blocks_per_seq * s.block_size > (int64_t)1 << 30) return PA_ERR_SHAPE;
+  if (s.flags > PA_DECODE_FORCE_MFMA) return PA_ERR_UNSUPPORTED;
+  if (s.flags == PA_DECODE_FORCE_MFMA) return PA_ERR_UNSUPPORTED;  // no matrix-core kernel built
+  return PA_OK;
+}
+
+// Partition policy for partition_size == 0.  Each partition adds
+// (head_dim*4 + 8) bytes of fp32 partial results per q head, written once and
+// read once by the merge; its key/value bytes per kv head are
+// 2 * partition * head_dim * elem.  Partitions of 256 tokens per two q heads
+// of the group keep the merge traffic near 1-3% of the KV stream while
+// leaving thousands of work items for long contexts.
+int32_t pick_partition(const DecodeShape& s) {
+  const int32_t g = s.num_q_heads / s.num_kv_heads;
+  int32_t p = 256;
+  while (p < 2048 && p * 2 <= 256 * ((g + 1) / 2)) p *= 2;
+  if (p % s.block_size) p = ((p + s.block_size - 1) / s.block_size) * s.block_size;
+  const int64_t max_ctx = (int64_t)s.max_blocks_per_seq * s.block_size;
+  if (max_ctx <= p) return (int32_t)max_ctx;  // one pass
+  return p;
+}
+
+int64_t n_partitions(const DecodeShape& s, int32_t p) {
+  const int64_t max_ctx = (int64_t)s.max_blocks_per_seq * s.block_size;
+  return (max_ctx + p - 1) / p;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t workspace_bytes_for(const DecodeShape& s, int32_t p) {
+  const int64_t np = n_partitions(s, p);
+  if (np <= 1) return 0;
+  const size_t rows = (size_t)s.num_seqs * s.num_q_heads * (size_t)np;
+  return round_up(rows * 2 * sizeof(float)) + round_up(rows * s.head_dim * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return kAbiVersion; }
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "a size is out of range, inconsistent or misaligned";
+    case PA_ERR_DTYPE: return "unknown dtype or unsupported dtype combination";
+    case PA_ERR_UNSUPPORTED: return "head_dim, block_size, group size or kernel choice not supported";
+    case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_size()";
+    case PA_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown pa_status";
+  }
+}
+
+int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int64_t num_tokens, int64_t k_token_stride,
+                   int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
+                   int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (!valid_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row) return PA_ERR_SHAPE;
+  if ((k_token_stride * eb) % 16 || (v_token_stride * eb) % 16) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_SHAPE;
+  const int64_t threads = num_tokens * num_kv_heads * ((int64_t)head_dim * eb / 16);
+  if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
+  pa::CacheWriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.slots = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_tokens = num_tokens;
+  a.num_blocks = num_blocks;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.elem_bytes = eb;
+  return pa::launch_cache_write(a, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int32_t kv_dtype, uint32_t flags) {
+  DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                kv_dtype, flags};
+  const int st = check_shape(s);
+  if (st != PA_OK) return st;
+  return pick_partition(s);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t partition_size, int32_t kv_dtype, uint32_t flags) {
+  DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                kv_dtype, flags};
+  if (check_shape(s) != PA_OK) return 0;
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size)) return 0;
+  return workspace_bytes_for(s, partition_size ? partition_size : pick_partition(s));
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int32_t block_size, int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+              int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
+              void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                kv_dtype, flags};
+  int st = check_shape(s);
+  if (st != PA_OK) return st;
+  if (num_blocks <= 0) return PA_ERR_SHAPE;
+  if (!elem_bytes(q_dtype) || !elem_bytes(out_dtype)) return PA_ERR_DTYPE;
+  if (q_dtype != kv_dtype && q_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
+  if (out_dtype != kv_dtype && out_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
+
+  const int64_t max_ctx = (int64_t)max_blocks_per_seq * block_size;
+  int32_t p = partition_size ? partition_size : pick_partition(s);
+  if (p > max_ctx) p = (int32_t)max_ctx;
+  const int64_t np = n_partitions(s, p);
+  const size_t need = workspace_bytes_for(s, p);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PA_ERR_WORKSPACE;
+  if (np > 65535 || (int64_t)num_seqs > 65535) return PA_ERR_SHAPE;
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
+  a.ws_ml = need ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.ws_acc = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                             round_up(rows * 2 * sizeof(float)))
+                  : nullptr;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.heads_per_item = heads_per_item(a.group, 8);
+  a.block_size = block_size;
+  a.log2_block_size = log2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.partition_size = p;
+  a.max_partitions = (int32_t)np;
+  a.q_dtype = q_dtype;
+  a.out_dtype = out_dtype;
+
+  hipStream_t hs = (hipStream_t)stream;
+  if (pa::launch_decode_valu(a, kv_dtype, head_dim, hs) != hipSuccess) return PA_ERR_HIP;
+  if (np > 1 && pa::launch_decode_reduce(a, head_dim, hs) != hipSuccess) return PA_ERR_HIP;
+  return PA_OK;
+}
+
+}  // extern "C"

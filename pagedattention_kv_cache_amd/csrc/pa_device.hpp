@@ -1,0 +1,147 @@
+// pa_device.hpp -- gfx950 device helpers shared by the paged-attention kernels.
+//
+// Element types are carried as raw bits (uint16_t for f16/bf16, float for
+// f32) and widened to fp32 with exact conversions; all accumulation is fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum class Elem : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+template <Elem E> struct ElemTraits;
+template <> struct ElemTraits<Elem::F32> { static constexpr int bytes = 4; };
+template <> struct ElemTraits<Elem::F16> { static constexpr int bytes = 2; };
+template <> struct ElemTraits<Elem::BF16> { static constexpr int bytes = 2; };
+
+// ---- exact widening of the two 16-bit elements packed in one dword --------
+template <Elem E> __device__ __forceinline__ float lo_to_f32(uint32_t w);
+template <Elem E> __device__ __forceinline__ float hi_to_f32(uint32_t w);
+
+template <> __device__ __forceinline__ float lo_to_f32<Elem::BF16>(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+template <> __device__ __forceinline__ float hi_to_f32<Elem::BF16>(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+template <> __device__ __forceinline__ float lo_to_f32<Elem::F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <> __device__ __forceinline__ float hi_to_f32<Elem::F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Widen the 16 bytes held in `raw` into fp32: 4 values for f32, 8 for 16-bit.
+template <Elem E>
+__device__ __forceinline__ void widen16(const uint4& raw, float* out) {
+  if constexpr (E == Elem::F32) {
+    out[0] = __uint_as_float(raw.x);
+    out[1] = __uint_as_float(raw.y);
+    out[2] = __uint_as_float(raw.z);
+    out[3] = __uint_as_float(raw.w);
+  } else {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = lo_to_f32<E>(w[i]);
+      out[2 * i + 1] = hi_to_f32<E>(w[i]);
+    }
+  }
+}
+
+// One element of type E (at element index i of p) as fp32.
+__device__ __forceinline__ float load_elem_f32(const void* p, int64_t i, int dtype) {
+  if (dtype == 0) return reinterpret_cast<const float*>(p)[i];
+  const uint16_t b = reinterpret_cast<const uint16_t*>(p)[i];
+  if (dtype == 1) return (float)__builtin_bit_cast(_Float16, b);
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Store fp32 as dtype (round to nearest even for the 16-bit types).
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float x, int dtype) {
+  if (dtype == 0) {
+    reinterpret_cast<float*>(p)[i] = x;
+  } else if (dtype == 1) {
+    reinterpret_cast<_Float16*>(p)[i] = (_Float16)x;
+  } else {
+    reinterpret_cast<__bf16*>(p)[i] = (__bf16)x;
+  }
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---- cross-lane reductions -----------------------------------------------
+// DPP row (16-lane) butterflies: after the four steps every lane of a row
+// holds the row's total.  Control codes are the GFX9 DPP encodings:
+// quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32, 64); every
+// lane of a group gets the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);
+  if constexpr (N >= 4) x += dpp<0x4E>(x);
+  if constexpr (N >= 8) x += dpp<0x141>(x);
+  if constexpr (N >= 16) x += dpp<0x140>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Max / sum across the 64/N groups of a wave for values that are already
+// uniform within each group of N lanes.
+template <int N>
+__device__ __forceinline__ float across_groups_max(float x) {
+  if constexpr (N <= 16) {
+    if constexpr (N <= 8) x = fmaxf(x, __shfl_xor(x, 8));
+    if constexpr (N <= 4) x = fmaxf(x, __shfl_xor(x, 4));
+    if constexpr (N <= 2) x = fmaxf(x, __shfl_xor(x, 2));
+    if constexpr (N <= 1) x = fmaxf(x, __shfl_xor(x, 1));
+    x = fmaxf(x, __shfl_xor(x, 16));
+  }
+  if constexpr (N <= 32) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float across_groups_sum(float x) {
+  if constexpr (N <= 16) {
+    if constexpr (N <= 8) x += __shfl_xor(x, 8);
+    if constexpr (N <= 4) x += __shfl_xor(x, 4);
+    if constexpr (N <= 2) x += __shfl_xor(x, 2);
+    if constexpr (N <= 1) x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 16);
+  }
+  if constexpr (N <= 32) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Context length as the kernels use it: clamped to what the block table can
+// address, so a length beyond the contract never walks past the table.
+__device__ __forceinline__ int clamp_len(int L, int max_blocks_per_seq, int block_size) {
+  const int cap = max_blocks_per_seq * block_size;
+  return L < cap ? L : cap;
+}
+
+// A block-table entry clamped into the pool: entries inside a sequence's
+// context must already be valid; the clamp only keeps a broken table from
+// turning into an out-of-bounds access.
+__device__ __forceinline__ int64_t clamp_block(int32_t phys, int64_t num_blocks) {
+  int64_t p = phys < 0 ? 0 : (int64_t)phys;
+  return p < num_blocks ? p : num_blocks - 1;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace pa

@@ -1,0 +1,63 @@
+// pa_launch.hpp -- host-side launch interface between the C ABI (pa_api.cpp)
+// and the kernel translation units.  Arguments are validated before any of
+// these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct CacheWriteArgs {
+  const void* k;
+  const void* v;
+  const int64_t* slots;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_tokens;
+  int64_t k_stride;  // elements between tokens of k
+  int64_t v_stride;
+  int64_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t elem_bytes;
+};
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+
+// Everything a decode kernel needs; passed by value as the kernel argument.
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_ml;   // [B][Hq][P][2] running max (log2 domain) and sum
+  float* ws_acc;  // [B][Hq][P][D] unnormalised partial outputs
+  float scale_log2;  // scale * log2(e)
+  int64_t num_blocks;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;       // num_q_heads / num_kv_heads
+  int32_t heads_per_item;  // q heads handled by one work item
+  int32_t block_size;
+  int32_t log2_block_size;
+  int32_t max_blocks_per_seq;
+  int32_t partition_size;  // tokens per partition
+  int32_t max_partitions;  // ceil(max_blocks_per_seq * block_size / partition_size)
+  int32_t q_dtype;
+  int32_t out_dtype;
+};
+
+// Vector-ALU decode kernel: any kv dtype, head_dim 64/128, 1..8 q heads per
+// work item.  grid = (max_partitions, num_kv_heads * head_chunks, num_seqs).
+hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s);
+
+// Log-sum-exp merge of the partitions of every (sequence, q head) that has
+// more than one.
+hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t s);
+
+}  // namespace pa

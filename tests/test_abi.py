@@ -1,0 +1,152 @@
+"""Host-side checks of libpa.so (CPU only; no kernel is ever launched here).
+
+The library must load without a GPU, export every function include/pa.h
+declares, and reject invalid arguments with the documented pa_status before
+any HIP call.  The pointers passed are never dereferenced: every call here is
+rejected by validation.  These tests are skipped where a GPU is visible so a
+validation bug can never turn into a launch with fake pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import pagedattention_kv_cache_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+F32, F16, BF16 = 0, 1, 2
+FAKE = 0x10000  # a 16-byte aligned non-null value; never dereferenced
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-validation tests use fake pointers; CPU only")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = pa.lib()
+    names = _declared_functions()
+    assert {"pa_cache_write", "pa_decode", "pa_decode_workspace_size",
+            "pa_decode_partition_size", "pa_status_string", "pa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libpa.so does not export {n}"
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    L = pa.lib()
+    assert L.pa_abi_version() == 1
+    fallback = pa.status_string(-99)
+    assert fallback == "unknown pa_status"
+    texts = [pa.status_string(st) for st in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP)]
+    assert all(t and t != fallback for t in texts)
+    assert len(set(texts)) == len(texts)
+
+
+def _cw(**kw):
+    args = dict(k=FAKE, v=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, T=4, ks=512, vs=512, H=4, d=128,
+                NB=10, bs=16, dtype=BF16)
+    args.update(kw)
+    return pa.lib().pa_cache_write(args["k"], args["v"], args["slots"], args["kc"], args["vc"],
+                                   args["T"], args["ks"], args["vs"], args["H"], args["d"],
+                                   args["NB"], args["bs"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), EDTYPE),
+    (dict(T=-1), ESHAPE),
+    (dict(H=0), ESHAPE),
+    (dict(NB=0), ESHAPE),
+    (dict(d=96), EUNSUP),
+    (dict(bs=12), EUNSUP),
+    (dict(bs=128), EUNSUP),
+    (dict(ks=100), ESHAPE),
+    (dict(vs=513), ESHAPE),
+    (dict(k=None), ENULL),
+    (dict(slots=None), ENULL),
+    (dict(vc=None), ENULL),
+    (dict(k=FAKE + 2), ESHAPE),
+    (dict(kc=FAKE + 8), ESHAPE),
+])
+def test_cache_write_validation(kw, status):
+    assert _cw(**kw) == status
+
+
+def test_cache_write_zero_tokens_is_noop():
+    assert _cw(T=0, k=None, v=None, slots=None, kc=None, vc=None) == OK
+
+
+def _dec(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, bs=16, P=0, B=4,
+             Hq=32, Hkv=8, d=128, NB=100, MB=64, qd=BF16, kvd=BF16, od=F32, ws=None, wsb=0,
+             flags=pa.FORCE_VALU)
+    a.update(kw)
+    return pa.lib().pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"],
+                              a["bs"], a["P"], a["B"], a["Hq"], a["Hkv"], a["d"], a["NB"], a["MB"],
+                              a["qd"], a["kvd"], a["od"], a["ws"], a["wsb"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ESHAPE),
+    (dict(Hq=0), ESHAPE),
+    (dict(Hkv=0), ESHAPE),
+    (dict(Hq=30), ESHAPE),
+    (dict(MB=0), ESHAPE),
+    (dict(NB=0), ESHAPE),
+    (dict(d=96), EUNSUP),
+    (dict(d=256), EUNSUP),
+    (dict(bs=4), EUNSUP),
+    (dict(bs=24), EUNSUP),
+    (dict(kvd=5), EDTYPE),
+    (dict(qd=F16), EDTYPE),
+    (dict(od=F16), EDTYPE),
+    (dict(od=9), EDTYPE),
+    (dict(P=-16), ESHAPE),
+    (dict(P=24), ESHAPE),
+    (dict(flags=7), EUNSUP),
+    (dict(out=None), ENULL),
+    (dict(q=None), ENULL),
+    (dict(bt=None), ENULL),
+    (dict(cl=None), ENULL),
+    (dict(kc=FAKE + 4), ESHAPE),
+    (dict(ws=None, wsb=0), EWS),           # two partitions of 512 need a workspace
+    (dict(ws=FAKE, wsb=1024), EWS),        # too small
+    (dict(ws=FAKE + 8, wsb=1 << 30), EWS),  # misaligned
+])
+def test_decode_validation(kw, status):
+    assert _dec(**kw) == status
+
+
+def test_decode_empty_batch_is_noop():
+    assert _dec(B=0, out=None, q=None, bt=None, cl=None) == OK
+
+
+def test_partition_policy_and_workspace_size():
+    L = pa.lib()
+    # one pass when the longest context fits one partition: no workspace
+    assert L.pa_decode_partition_size(4, 4, 4, 64, 16, 13, F32, 0) == 208
+    assert L.pa_decode_workspace_size(4, 4, 4, 64, 16, 13, 0, F32, 0) == 0
+    # MHA: 256-token partitions; GQA groups of 4: 512; of 8: 1024
+    assert L.pa_decode_partition_size(64, 32, 32, 128, 16, 128, F16, 0) == 256
+    assert L.pa_decode_partition_size(256, 32, 8, 128, 16, 512, BF16, 0) == 512
+    assert L.pa_decode_partition_size(64, 64, 8, 128, 32, 1025, BF16, 0) == 1024
+    # workspace = (m, l) and a head_dim vector per (seq, q head, partition), 256-B aligned
+    B, Hq, d, MB, bs, P = 256, 32, 128, 512, 16, 512
+    n_part = MB * bs // P
+    rows = B * Hq * n_part
+    expect = -(-rows * 8 // 256) * 256 + -(-rows * d * 4 // 256) * 256
+    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, 0) == expect
+    # forced partition sizes must be multiples of the block size; invalid -> 0
+    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 24, BF16, 0) == 0
+    assert L.pa_decode_partition_size(4, 3, 2, 128, 16, 8, BF16, 0) == ESHAPE

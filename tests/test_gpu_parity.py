@@ -1,0 +1,314 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bars: the cache write is bit-exact (whole NaN-poisoned pools compared); decode
+with fp32 KV is within 1e-5 rowwise normwise relative error, decode with
+fp16/bf16 KV within 2e-3 max absolute error, against the oracle in fp64 on the
+same rounded inputs.  Invariant checks (L = 1, one-hot probe, block
+permutation) are bit-exact.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pagedattention_kv_cache_amd as pa
+from pagedattention_kv_cache_amd.workloads import CONFIGS, Workload, custom_config, raw_bits
+from tests.gpu_harness import GpuState, max_abs_err, oracle_state_empty, rowwise_rel_err
+from tests.paged_host import OracleState
+
+pytestmark = pytest.mark.gpu
+
+TOL_ABS_HALF = 2e-3
+TOL_REL_F32 = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.lib()
+    oracle.build(force=False)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_decode(out: torch.Tensor, ref: np.ndarray, dtype: str, rows=None):
+    if dtype == "f32":
+        err = rowwise_rel_err(out, ref, rows)
+        assert err <= TOL_REL_F32, f"rowwise relative error {err:.3e}"
+    else:
+        err = max_abs_err(out, ref, rows)
+        assert err <= TOL_ABS_HALF, f"max abs error {err:.3e}"
+    return err
+
+
+def _pools_equal(gs: GpuState, st) -> None:
+    gk = raw_bits(gs.kc.cpu())
+    gv = raw_bits(gs.vc.cpu())
+    assert np.array_equal(gk, st.kc), "key pool differs from the oracle's"
+    assert np.array_equal(gv, st.vc), "value pool differs from the oracle's"
+
+
+def _run_small(cfg, flags=pa.AUTO, partition_size=None, out_dtype=torch.float32):
+    wl = Workload(cfg)
+    _say(f"case {cfg.name} lens={wl.lens0.tolist()} d={cfg.head_dim} bs={cfg.block_size} "
+         f"g={cfg.group} dtype={cfg.dtype} P={partition_size} flags={flags}")
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    results = []
+    for s in range(cfg.steps):
+        gs.write_step(s)
+        st.write_step(s)
+        out = gs.decode(s, out_dtype=out_dtype, partition_size=partition_size, flags=flags)
+        ref = st.decode(s)
+        results.append((out, ref))
+    torch.cuda.synchronize()
+    return wl, gs, st, results
+
+
+# ------------------------------------------------------------------ cache write
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
+def test_cache_write_bit_exact(dtype, d, bs):
+    cfg = custom_config(f"cw-{dtype}-{d}-{bs}", [1, bs - 1, bs, bs + 1, 3 * bs + 5], 2, 2, d,
+                        dtype, bs, seed=100 + d + bs, steps=2)
+    wl = Workload(cfg)
+    _say(f"cache write {dtype} d={d} bs={bs}")
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    for s in range(cfg.steps):
+        gs.write_step(s)
+        st.write_step(s)
+    torch.cuda.synchronize()
+    _pools_equal(gs, st)
+
+
+def test_cache_write_strided_tokens_and_negative_slots():
+    """k/v as column slices of a fused [T][3*H*d] projection output; slots < 0 skipped."""
+    T, H, d, bs, NB = 37, 4, 128, 16, 12
+    g = torch.Generator().manual_seed(5)
+    qkv = torch.randn(T, 3 * H * d, generator=g).to(torch.bfloat16)
+    k = qkv[:, H * d:2 * H * d].view(T, H, d)
+    v = qkv[:, 2 * H * d:].view(T, H, d)
+    slots = torch.randperm(NB * bs, generator=g)[:T].to(torch.int64)
+    slots[::5] = -1
+    kc_o = np.full((NB, H, bs, d), 0x7FC0, np.uint16)
+    vc_o = np.full((NB, H, d, bs), 0x7FC0, np.uint16)
+    oracle.cache_write(raw_bits(k.contiguous()), raw_bits(v.contiguous()), slots.numpy(), kc_o,
+                       vc_o, "bf16")
+    # start from the same poisoned pools as the oracle
+    kc = torch.full((NB, H, bs, d), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vc = torch.full((NB, H, d, bs), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    qkv_d = qkv.cuda()
+    pa.cache_write(qkv_d[:, H * d:2 * H * d].view(T, H, d), qkv_d[:, 2 * H * d:].view(T, H, d),
+                   slots.cuda(), kc, vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_bits(kc.cpu()), kc_o)
+    assert np.array_equal(raw_bits(vc.cpu()), vc_o)
+
+
+# ------------------------------------------------------------------ decode parity
+
+SMALL = [
+    # dtype, d, bs, Hq, Hkv, lens
+    ("f32", 64, 16, 4, 4, [1, 17, 64, 200]),
+    ("f32", 128, 8, 4, 2, [3, 40, 129]),
+    ("f16", 128, 16, 8, 8, [1, 15, 16, 17, 300, 513]),
+    ("f16", 64, 32, 6, 2, [2, 31, 33, 400]),
+    ("bf16", 128, 16, 8, 2, [5, 16, 100, 1000, 1500]),
+    ("bf16", 128, 32, 16, 2, [1, 64, 777, 2049]),
+    ("bf16", 64, 64, 12, 4, [63, 64, 65, 700]),
+    ("bf16", 128, 8, 7, 1, [9, 250, 600]),
+    ("f16", 128, 64, 16, 1, [1, 1000]),
+    ("bf16", 128, 16, 32, 8, [1, 2, 1024, 3000]),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1]}-bs{c[2]}-{c[3]}x{c[4]}")
+@pytest.mark.parametrize("partition", [0, "one-pass", "min"])
+def test_decode_parity_small(case, partition):
+    dtype, d, bs, hq, hkv, lens = case
+    max_ctx = -(-max(lens) // bs) * bs
+    p = {0: 0, "one-pass": max_ctx, "min": max(bs, 16) * 2}[partition]
+    cfg = custom_config(f"dp-{dtype}", lens, hq, hkv, d, dtype, bs, seed=sum(lens) + d + bs,
+                        partition_size=p)
+    wl, gs, st, res = _run_small(cfg)
+    for out, ref in res:
+        assert torch.isfinite(out).all()
+        _check_decode(out, ref, dtype)
+
+
+def test_decode_multistep_parity():
+    cfg = custom_config("ms", [1, 30, 31, 32, 500], 8, 2, 128, "bf16", 32, seed=9, steps=8)
+    wl, gs, st, res = _run_small(cfg)
+    for out, ref in res:
+        _check_decode(out, ref, "bf16")
+    _pools_equal(gs, st)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_f32_query_and_half_output(dtype):
+    cfg = custom_config("mix", [7, 200, 901], 8, 2, 128, dtype, 16, seed=77)
+    wl = Workload(cfg)
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    gs.write_step(0)
+    st.write_step(0)
+    # q in f32 (the same values as the half q, widened exactly)
+    qf = gs.q[0].float()
+    out_f = gs.decode(0, q=qf)
+    ref = st.decode(0)
+    _check_decode(out_f, ref, dtype)
+    # out in the kv dtype: within one ulp of that dtype plus the half tolerance
+    out_h = gs.decode(0, out_dtype=gs.kc.dtype)
+    ulp = 2.0 ** (-10 if dtype == "f16" else -7)
+    err = np.abs(out_h.double().cpu().numpy() - ref)
+    assert (err <= np.abs(ref) * ulp + TOL_ABS_HALF).all()
+
+
+# ------------------------------------------------------------------ invariants
+
+def _single_token_state(dtype, d, bs, hq, hkv, n_seqs, seed):
+    cfg = custom_config("l1", [1] * n_seqs, hq, hkv, d, dtype, bs, seed=seed, num_blocks=n_seqs + 3)
+    return cfg, Workload(cfg)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("partition", [0, 16])
+def test_context_length_one_returns_v_bit_exact(dtype, partition):
+    cfg, wl = _single_token_state(dtype, 128, 16, 8, 2, 6, seed=3)
+    gs = GpuState(wl)
+    gs.write_step(0)
+    out = gs.decode(0, partition_size=partition)
+    torch.cuda.synchronize()
+    v = gs.step_v[0].float()  # [B][Hkv][d]
+    expect = v.repeat_interleave(cfg.group, dim=1)
+    assert torch.equal(out, expect)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("partition", [0, 32, "one-pass"])
+def test_one_hot_probe_bit_exact(dtype, partition):
+    """K = 0 except one target token whose key is c*q (scale*c*|q|^2 >= 200):
+    every other weight underflows, so out == V[t*] exactly, for every t*."""
+    L, d, bs, H = 96, 64, 16, 1
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    gen = torch.Generator().manual_seed(17)
+    q = torch.randn(1, 1, d, generator=gen).to(dt)
+    V = torch.randn(L, H, d, generator=gen).to(dt)
+    qf = q.float()
+    scale = 1.0 / 8.0
+    c = 260.0 / (scale * float((qf ** 2).sum()))
+    NB = 12
+    perm = torch.randperm(NB, generator=gen)[: L // bs].to(torch.int32)
+    bt = perm.view(1, -1).cuda()
+    pos = torch.arange(L)
+    slots = (perm[pos // bs].to(torch.int64) * bs + pos % bs).cuda()
+    p = {0: 0, 32: 32, "one-pass": L}[partition]
+    for t in [0, 1, 15, 16, 17, 47, 63, 64, 95]:
+        K = torch.zeros(L, H, d, dtype=dt)
+        K[t, 0] = (qf[0, 0] * c).to(dt)
+        kc = torch.full((NB, H, bs, d), float("nan"), dtype=dt, device="cuda")
+        vc = torch.full((NB, H, d, bs), float("nan"), dtype=dt, device="cuda")
+        pa.cache_write(K.cuda(), V.cuda(), slots, kc, vc)
+        out = torch.empty(1, 1, d, device="cuda")
+        pa.decode(out, q.cuda(), kc, vc, bt, torch.tensor([L], dtype=torch.int32, device="cuda"),
+                  scale, bs, p)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0, 0].cpu(), V[t, 0].float()), f"t*={t}"
+
+
+def test_block_permutation_bit_identical():
+    """Moving physical blocks (and remapping the table) does not change a bit."""
+    cfg = custom_config("perm", [33, 300, 1000], 8, 2, 128, "bf16", 16, seed=44)
+    wl = Workload(cfg)
+    gs = GpuState(wl)
+    gs.write_step(0)
+    out1 = gs.decode(0)
+    NB = wl.num_blocks
+    perm = torch.randperm(NB, generator=torch.Generator().manual_seed(1)).cuda()
+    kc2 = torch.empty_like(gs.kc)
+    vc2 = torch.empty_like(gs.vc)
+    kc2[perm] = gs.kc
+    vc2[perm] = gs.vc
+    bt = gs.block_tables.long()
+    bt2 = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).to(torch.int32)
+    out2 = torch.empty_like(out1)
+    pa.decode(out2, gs.q[0], kc2, vc2, bt2.contiguous(), gs.ctx[0], cfg.attn_scale(),
+              cfg.block_size, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+
+
+def test_partition_sweep_within_tolerance():
+    cfg = custom_config("sweep", [1, 100, 1000, 4000], 8, 2, 128, "bf16", 16, seed=45)
+    wl = Workload(cfg)
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    gs.write_step(0)
+    st.write_step(0)
+    ref = st.decode(0)
+    for p in [16, 32, 48, 128, 256, 512, 1024, 4000, 4096]:
+        out = gs.decode(0, partition_size=p)
+        _check_decode(out, ref, "bf16")
+
+
+def test_zero_length_sequence_gives_zero_row_and_empty_batch_is_noop():
+    cfg = custom_config("z", [5, 40], 4, 4, 64, "f16", 16, seed=46)
+    wl = Workload(cfg)
+    gs = GpuState(wl)
+    gs.write_step(0)
+    ctx = gs.ctx[0].clone()
+    ctx[0] = 0
+    out = torch.full((2, 4, 64), 7.0, device="cuda")
+    pa.decode(out, gs.q[0], gs.kc, gs.vc, gs.block_tables, ctx, cfg.attn_scale(), 16, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], torch.zeros_like(out[0]))
+    assert torch.isfinite(out[1]).all()
+    empty = torch.empty(0, 4, 64, device="cuda")
+    pa.decode(empty, gs.q[0][:0], gs.kc, gs.vc, gs.block_tables[:0], ctx[:0],
+              cfg.attn_scale(), 16, 0)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sample_rows(wl: Workload, n_per_step: int, seed: int) -> np.ndarray:
+    c = wl.cfg
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(c.num_seqs * c.num_q_heads, size=min(n_per_step, c.num_seqs * c.num_q_heads),
+                      replace=False)
+    longest = int(np.argmax(wl.lens0))
+    rows = np.union1d(rows, longest * c.num_q_heads + np.arange(c.num_q_heads))
+    return rows.astype(np.int64)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_full_workload_parity(cid):
+    """Each of the five decode workloads at full size, in the launch
+    configuration the benchmark times (library-picked or the workload's
+    partition size, automatic kernel choice)."""
+    cfg = CONFIGS[cid]
+    wl = Workload(cfg)
+    _say(f"full workload {cid} {cfg.name}: {wl.describe()}")
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    full_rows = cid in (1, 2, 3, 4)
+    for s in range(cfg.steps):
+        gs.write_step(s)
+        st.write_step(s)
+        out = gs.decode(s)
+        rows = None if full_rows else _sample_rows(wl, 96, seed=s)
+        ref = st.decode(s, rows=rows, threads=16)
+        err = _check_decode(out, ref, cfg.dtype, rows)
+        _say(f"  step {s}: err {err:.3e} rows {'all' if rows is None else len(rows)}")
+    torch.cuda.synchronize()
+    _pools_equal(gs, st)
