@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path (KV slot write + paged attention) on
+one MI355X.
+
+A step is one pass of the whole path over one batch: write every sequence's
+new token into the paged KV cache through its slot (pa_cache_write), run
+attention over every partition (pa_decode_partitions) and merge the
+partitions (pa_decode_merge).  Inputs are seeded synthetic tensors already
+resident in HBM; the timed region holds exactly K steps bracketed by
+synchronisation.  Prints one JSON line:
+
+  value          KV bytes the step's attention must read (each context element
+                 once) / wall time per step, in GB/s
+  roofline       the partitioned attention kernel: algorithmic KV bytes per
+                 launch / its mean launch time (HIP events on the launch
+                 stream) against the 8 TB/s HBM3E peak; `traffic` is the HBM
+                 bytes per launch from the committed rocprofv3 counter summary
+                 when it was taken on the current kernel source, else null
+  cpu_baseline   the fp64 CPU oracle timed on this host on the same step
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload N]
+Only one GPU is used; --gpus N with N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published
+KERNEL_SOURCES = ["decode_valu.hip", "decode_mfma.hip", "pa_device.hpp", "pa_launch.hpp",
+                  "pa_api.cpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "pagedattention_kv_cache_amd", "csrc", name)
+        if os.path.exists(p):
+            h.update(name.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, help="decode workload 1..5 (default 4)")
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="-1: the workload's setting (0 = library picks)")
+    ap.add_argument("--flags", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, host cores)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
+                    help="first run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="post-process two rocprofv3 --pmc counter CSVs into profiles/ (no GPU)")
+    ap.add_argument("--pmc-copy-mib", type=int, default=1024)
+    return ap.parse_args(argv)
+
+
+# ----------------------------------------------------------------------------- counters
+
+def _read_counter_csv(path):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    out = {}
+    for r in rows:
+        name = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("KernelName") or ""
+        cname = r.get("Counter_Name") or r.get("Counter-Name") or ""
+        val = float(r.get("Counter_Value") or r.get("Counter-Value") or 0.0)
+        out.setdefault((name, cname), []).append(val)
+    return out
+
+
+def summarize_pmc(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode kernel, scaled
+    by what the same counters read for a plain device copy of known size."""
+    fetch = _read_counter_csv(args.summarize_pmc[0])
+    write = _read_counter_csv(args.summarize_pmc[1])
+    copy_bytes = args.pmc_copy_mib * 2**20
+
+    def pick(table, counter, pred):
+        vals = [v for (k, c), vs in table.items() if c == counter and pred(k) for v in vs]
+        return vals
+
+    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
+    is_dec = lambda k: "decode_valu_kernel" in k or "decode_mfma_kernel" in k  # noqa: E731
+    copy_f = max(pick(fetch, "FETCH_SIZE", is_copy))
+    copy_w = max(pick(write, "WRITE_SIZE", is_copy))
+    dec_f = statistics.median(pick(fetch, "FETCH_SIZE", is_dec))
+    dec_w = statistics.median(pick(write, "WRITE_SIZE", is_dec))
+    f_scale = copy_bytes / (copy_f * 1024.0)
+    w_scale = copy_bytes / (copy_w * 1024.0)
+    res = {
+        "kernel_source_hash": kernel_source_hash(),
+        "copy_probe_bytes": copy_bytes,
+        "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "decode_fetch_kib": dec_f, "decode_write_kib": dec_w,
+        "decode_fetch_bytes": dec_f * 1024.0 * f_scale,
+        "decode_write_bytes": dec_w * 1024.0 * w_scale,
+    }
+    res["traffic_bytes"] = res["decode_fetch_bytes"] + res["decode_write_bytes"]
+    from pagedattention_kv_cache_amd.workloads import CONFIGS
+    path = TRAFFIC_FILE.format(workload=CONFIGS[args.workload].name)
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
+    return res
+
+
+# ----------------------------------------------------------------------------- benchmark
+
+def fill_caches(wl, dev, kc, vc, oracle_caches=None):
+    import torch
+
+    import pagedattention_kv_cache_amd as pa
+    from pagedattention_kv_cache_amd.workloads import raw_bits
+    c = wl.cfg
+    for b in range(c.num_seqs):
+        k, v = wl.prior_kv(b)
+        if k.shape[0] == 0:
+            continue
+        slots = wl.prior_slots(b)
+        pa.cache_write(k.to(dev), v.to(dev), torch.from_numpy(slots).to(dev), kc, vc)
+        if oracle_caches is not None:
+            import oracle
+            oracle.cache_write(raw_bits(k), raw_bits(v), slots, oracle_caches[0], oracle_caches[1],
+                               c.dtype)
+
+
+def cpu_baseline(wl, okc, ovc, threads):
+    """The oracle on the same step: ORC-W of the step's new tokens, then ORC-D
+    of every (sequence, q head) row; median of repetitions."""
+    import numpy as np
+
+    import oracle
+    from pagedattention_kv_cache_amd.workloads import raw_bits
+    c = wl.cfg
+    sk, sv = wl.step_kv()
+    q = raw_bits(wl.queries()[0])
+    slots = wl.step_slots(0)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 2 or (time.perf_counter() - t_start < 10.0 and len(times) < 10):
+        t0 = time.perf_counter()
+        oracle.cache_write(raw_bits(sk[0]), raw_bits(sv[0]), slots, okc, ovc, c.dtype)
+        oracle.decode(q, c.dtype, okc, ovc, c.dtype, wl.block_tables, wl.context_lens(0),
+                      c.attn_scale(), threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    kv = wl.kv_bytes(0)
+    return {
+        "value": kv / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"one full step of {c.name} (write of {c.num_seqs} new tokens + all "
+                   f"{c.num_seqs * c.num_q_heads} attention rows), fp64, median of {len(times)} "
+                   f"repetitions"),
+        "seconds_per_step": t,
+        "tokens_per_s": c.num_seqs / t,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import pagedattention_kv_cache_amd as pa
+    from pagedattention_kv_cache_amd.workloads import CONFIGS, DTYPE_TORCH, Workload
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the paged decode "
+                          "path has no multi-GPU mode here (see DESIGN.md for how it would "
+                          "shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    pa.lib()
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.workload]
+    wl = Workload(cfg)
+    c = cfg
+    flags = {"auto": pa.AUTO, "valu": pa.FORCE_VALU, "mfma": pa.FORCE_MFMA}[args.flags]
+    part = cfg.partition_size if args.partition_size < 0 else args.partition_size
+
+    if args.copy_probe:
+        n = args.copy_probe * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    kdt = DTYPE_TORCH[c.dtype]
+    kc = torch.empty((wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim), dtype=kdt,
+                     device=dev)
+    vc = torch.empty((wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size), dtype=kdt,
+                     device=dev)
+    want_cpu = not args.no_cpu_baseline
+    okc = ovc = None
+    if want_cpu:
+        import oracle
+        from pagedattention_kv_cache_amd.workloads import POISON_BITS
+        oracle.build(force=False)
+        bits = np.uint32 if c.dtype == "f32" else np.uint16
+        okc = np.full(tuple(kc.shape), POISON_BITS[c.dtype], bits)
+        ovc = np.full(tuple(vc.shape), POISON_BITS[c.dtype], bits)
+    t_fill = time.perf_counter()
+    fill_caches(wl, dev, kc, vc, (okc, ovc) if want_cpu else None)
+    torch.cuda.synchronize()
+    t_fill = time.perf_counter() - t_fill
+
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    qs = wl.queries().to(dev)
+    sk, sv = wl.step_kv()
+    sk, sv = sk.to(dev), sv.to(dev)
+    slots = [torch.from_numpy(wl.step_slots(s)).to(dev) for s in range(c.steps)]
+    ctx = [torch.from_numpy(wl.context_lens(s)).to(dev) for s in range(c.steps)]
+    MB = wl.max_blocks_per_seq
+    p_eff = part if part else pa.decode_partition_size(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                                       c.head_dim, c.block_size, MB, kdt, flags)
+    ws_bytes = pa.decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                        c.block_size, MB, part, kdt, flags)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+    scale = c.attn_scale()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        s = i % c.steps
+        if ev is not None:
+            ev[0].record(stream)
+        pa.cache_write(sk[s], sv[s], slots[s], kc, vc)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.decode_partitions(out, qs[s], kc, vc, bt, ctx[s], scale, c.block_size, part, ws, flags)
+        if ev is not None:
+            ev[2].record(stream)
+        pa.decode_merge(out, qs[s], kc, vc, bt, ctx[s], scale, c.block_size, part, ws, flags)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    write_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    dec_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    merge_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
+
+    kv = statistics.mean(wl.kv_bytes(i % c.steps) for i in range(args.steps))
+    value = kv / (ms_step * 1e-3) / 1e9
+    achieved = kv / (dec_ms * 1e-3) / 1e9
+
+    traffic = None
+    tf = TRAFFIC_FILE.format(workload=c.name)
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec.get("traffic_bytes")
+
+    kname = "decode_valu_kernel" if flags != pa.FORCE_MFMA else "decode_mfma_kernel"
+    result = {
+        "metric": "paged decode attention: achieved KV HBM GB/s (% peak) + tokens/s, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block pool; no dataset)",
+        "config": {"workload": c.name, **{k: v for k, v in wl.describe().items() if k != "workload"},
+                   "partition_size": int(p_eff), "kernel_flags": args.flags},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": int(kv),
+        "write_ms": round(write_ms, 5),
+        "decode_partitions_ms": round(dec_ms, 5),
+        "decode_merge_ms": round(merge_ms, 5),
+        "roofline": {
+            "kernel": kname,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(kv),
+        },
+        "fill_seconds": round(t_fill, 2),
+    }
+    if want_cpu:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        result["cpu_baseline"] = cpu_baseline(wl, okc, ovc, threads)
+    print(json.dumps(result), flush=True)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -138,6 +138,37 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * pa_decode in its two phases, for callers that schedule them separately
+ * (e.g. to time them, or to merge partition results gathered from elsewhere).
+ * Both take exactly pa_decode's arguments and must be given the same ones.
+ *
+ * pa_decode_partitions: attention over each partition of partition_size
+ *   tokens; writes, per (sequence, q head, partition), the running max m
+ *   (log2 domain), the sum l and the unnormalised output vector to the
+ *   workspace, and writes `out` directly for sequences that fit one partition.
+ * pa_decode_merge: for sequences with more than one partition, merges the
+ *   workspace entries by log-sum-exp into `out` ("vLLM Project Update" talk,
+ *   second PagedAttention kernel, "similar to flash decoding").  Launches
+ *   nothing when every sequence fits one partition.
+ * pa_decode(...) == pa_decode_partitions(...) followed by pa_decode_merge(...)
+ * on the same stream.
+ */
+int pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         int32_t block_size, int32_t partition_size, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
+                         int32_t kv_dtype, int32_t out_dtype, void* workspace,
+                         size_t workspace_bytes, uint32_t flags, void* stream);
+int pa_decode_merge(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int32_t block_size, int32_t partition_size, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
+                    int32_t kv_dtype, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                    uint32_t flags, void* stream);
+
+/*
  * The partition size pa_decode uses when called with partition_size == 0 and
  * the same arguments (a pure function of them; no device query).  Returns a
  * negative pa_status for invalid arguments.

@@ -47,9 +47,11 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_size_t)
         L.pa_cache_write.restype = ctypes.c_int
         L.pa_cache_write.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i64, i32, i32, vp]
-        L.pa_decode.restype = ctypes.c_int
-        L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, i32,
-                                i32, i64, i32, i32, i32, i32, vp, sz, u32, vp]
+        dec_args = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, i32, i32, i64, i32,
+                    i32, i32, i32, vp, sz, u32, vp]
+        for name in ("pa_decode", "pa_decode_partitions", "pa_decode_merge"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = dec_args
         L.pa_decode_partition_size.restype = i32
         L.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, u32]
         L.pa_decode_workspace_size.restype = sz
@@ -123,11 +125,8 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, he
                                           _DTYPE[kv_dtype], flags)
 
 
-def decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-           block_size: int, partition_size: int = 0, workspace: torch.Tensor | None = None,
-           flags: int = AUTO) -> None:
-    """out[b][hq] = softmax(scale * q[b][hq] . K^T) V over the paged context of b."""
+def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                 partition_size, workspace, flags):
     _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
     B, Hq, d = q.shape
     _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
@@ -144,10 +143,37 @@ def decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     kvd = k_cache.dtype
     need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, kvd, flags)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        if fn_name != "pa_decode":
+            raise PAError(-5, "the phase entry points need the caller's workspace")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                           block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
-                           block_size, partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(k_cache),
-                           _dt(out), ws_ptr, ws_bytes, flags, _stream(q.device)))
+    _check(getattr(lib(), fn_name)(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), block_size,
+        partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(k_cache), _dt(out), ws_ptr, ws_bytes,
+        flags, _stream(q.device)))
+
+
+def decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+           block_size: int, partition_size: int = 0, workspace: torch.Tensor | None = None,
+           flags: int = AUTO) -> None:
+    """out[b][hq] = softmax(scale * q[b][hq] . K^T) V over the paged context of b.
+    Allocates the workspace with torch when none (or too small a one) is given."""
+    _decode_call("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 block_size, partition_size, workspace, flags)
+
+
+def decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                      partition_size=0, workspace=None, flags=AUTO) -> None:
+    """Phase 1 of decode (attention per partition); needs the caller's workspace."""
+    _decode_call("pa_decode_partitions", out, q, k_cache, v_cache, block_tables, context_lens,
+                 scale, block_size, partition_size, workspace, flags)
+
+
+def decode_merge(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                 partition_size=0, workspace=None, flags=AUTO) -> None:
+    """Phase 2 of decode (log-sum-exp merge of the partitions)."""
+    _decode_call("pa_decode_merge", out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 block_size, partition_size, workspace, flags)

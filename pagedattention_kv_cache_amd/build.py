@@ -17,7 +17,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pa_api.cpp", "cache_write.hip", "decode_valu.hip", "decode_reduce.hip"]
+SOURCES = ["pa_api.cpp", "cache_write.hip", "decode_valu.hip", "decode_mfma.hip",
+           "decode_reduce.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

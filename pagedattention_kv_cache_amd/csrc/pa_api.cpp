@@ -37,6 +37,25 @@ int32_t heads_per_item(int32_t g, int32_t cap) {
   return 1;
 }
 
+// Matrix-core tile width: the largest divisor of g that one 16-column tile
+// holds and that is instantiated.
+int32_t mfma_heads_per_item(int32_t g) {
+  for (int32_t h = g < 16 ? g : 16; h >= 1; --h)
+    if (g % h == 0 && pa::mfma_supports_heads(h)) return h;
+  return 1;
+}
+
+// Kernel family: the matrix-core kernel serves 16-bit caches queried in the
+// same dtype once a GQA group has at least two q heads per kv head (a
+// multi-column tile); plain multi-head attention and fp32 stay on the
+// vector-ALU kernel unless the caller forces the matrix cores.
+bool use_mfma(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t group) {
+  const bool eligible = kv_dtype != PA_DTYPE_F32 && q_dtype == kv_dtype;
+  if (flags == PA_DECODE_FORCE_MFMA) return eligible;
+  if (flags == PA_DECODE_FORCE_VALU) return false;
+  return eligible && group >= 2;
+}
+
 struct DecodeShape {
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   int32_t kv_dtype;
@@ -52,7 +71,7 @@ int check_shape(const DecodeShape& s) {
   if (!valid_block_size(s.block_size)) return PA_ERR_UNSUPPORTED;
   if ((int64_t)s.max_blocks_per_seq * s.block_size > (int64_t)1 << 30) return PA_ERR_SHAPE;
   if (s.flags > PA_DECODE_FORCE_MFMA) return PA_ERR_UNSUPPORTED;
-  if (s.flags == PA_DECODE_FORCE_MFMA) return PA_ERR_UNSUPPORTED;  // no matrix-core kernel built
+  if (s.flags == PA_DECODE_FORCE_MFMA && s.kv_dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -161,12 +180,18 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   return workspace_bytes_for(s, partition_size ? partition_size : pick_partition(s));
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, float scale,
-              int32_t block_size, int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
-              int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-              int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
-              void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+enum Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
+
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, float scale,
+                int32_t block_size, int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
+                void* workspace, size_t workspace_bytes, uint32_t flags, void* stream, int phase) {
   DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                 kv_dtype, flags};
   int st = check_shape(s);
@@ -177,6 +202,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   if (out_dtype != kv_dtype && out_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
     return PA_ERR_SHAPE;
+  if (flags == PA_DECODE_FORCE_MFMA && q_dtype != kv_dtype) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
@@ -208,7 +234,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = num_q_heads / num_kv_heads;
-  a.heads_per_item = heads_per_item(a.group, 8);
+  const bool mfma = use_mfma(flags, kv_dtype, q_dtype, a.group);
+  a.heads_per_item = mfma ? mfma_heads_per_item(a.group) : heads_per_item(a.group, 8);
   a.block_size = block_size;
   a.log2_block_size = log2_exact(block_size);
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -218,9 +245,34 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.out_dtype = out_dtype;
 
   hipStream_t hs = (hipStream_t)stream;
-  if (pa::launch_decode_valu(a, kv_dtype, head_dim, hs) != hipSuccess) return PA_ERR_HIP;
-  if (np > 1 && pa::launch_decode_reduce(a, head_dim, hs) != hipSuccess) return PA_ERR_HIP;
+  if (phase & kPartitions) {
+    const hipError_t e = mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, hs)
+                              : pa::launch_decode_valu(a, kv_dtype, head_dim, hs);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  if ((phase & kMerge) && np > 1 && pa::launch_decode_reduce(a, head_dim, hs) != hipSuccess)
+    return PA_ERR_HIP;
   return PA_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+#define PA_DECODE_PARAMS                                                                       \
+  void *out, const void *q, const void *k_cache, const void *v_cache,                          \
+      const int32_t *block_tables, const int32_t *context_lens, float scale, int32_t block_size, \
+      int32_t partition_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,     \
+      int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,       \
+      int32_t kv_dtype, int32_t out_dtype, void *workspace, size_t workspace_bytes,            \
+      uint32_t flags, void *stream
+#define PA_DECODE_ARGS                                                                       \
+  out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, partition_size,   \
+      num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, q_dtype, \
+      kv_dtype, out_dtype, workspace, workspace_bytes, flags, stream
+
+int pa_decode(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kBoth); }
+int pa_decode_partitions(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kPartitions); }
+int pa_decode_merge(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kMerge); }
 
 }  // extern "C"

@@ -56,6 +56,11 @@ struct DecodeArgs {
 // work item.  grid = (max_partitions, num_kv_heads * head_chunks, num_seqs).
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s);
 
+// Matrix-core decode kernel: f16/bf16 KV with q in the same dtype, head_dim
+// 64/128, up to 16 q heads per work item (see mfma_supports_heads).
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s);
+bool mfma_supports_heads(int heads_per_item);
+
 // Log-sum-exp merge of the partitions of every (sequence, q head) that has
 // more than one.
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t s);

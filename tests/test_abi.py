@@ -115,6 +115,8 @@ def _dec(**kw):
     (dict(P=-16), ESHAPE),
     (dict(P=24), ESHAPE),
     (dict(flags=7), EUNSUP),
+    (dict(flags=pa.FORCE_MFMA, kvd=F32, qd=F32), EUNSUP),  # matrix cores: 16-bit caches only
+    (dict(flags=pa.FORCE_MFMA, qd=F32), EUNSUP),           # ... queried in the same dtype
     (dict(out=None), ENULL),
     (dict(q=None), ENULL),
     (dict(bt=None), ENULL),

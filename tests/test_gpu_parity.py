@@ -133,15 +133,21 @@ SMALL = [
 ]
 
 
+KERNELS = {"auto": pa.AUTO, "valu": pa.FORCE_VALU, "mfma": pa.FORCE_MFMA}
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1]}-bs{c[2]}-{c[3]}x{c[4]}")
 @pytest.mark.parametrize("partition", [0, "one-pass", "min"])
-def test_decode_parity_small(case, partition):
+@pytest.mark.parametrize("kernel", ["auto", "valu", "mfma"])
+def test_decode_parity_small(case, partition, kernel):
     dtype, d, bs, hq, hkv, lens = case
+    if kernel == "mfma" and dtype == "f32":
+        pytest.skip("the matrix-core kernel serves 16-bit caches only")
     max_ctx = -(-max(lens) // bs) * bs
     p = {0: 0, "one-pass": max_ctx, "min": max(bs, 16) * 2}[partition]
     cfg = custom_config(f"dp-{dtype}", lens, hq, hkv, d, dtype, bs, seed=sum(lens) + d + bs,
                         partition_size=p)
-    wl, gs, st, res = _run_small(cfg)
+    wl, gs, st, res = _run_small(cfg, flags=KERNELS[kernel])
     for out, ref in res:
         assert torch.isfinite(out).all()
         _check_decode(out, ref, dtype)
@@ -184,11 +190,14 @@ def _single_token_state(dtype, d, bs, hq, hkv, n_seqs, seed):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("partition", [0, 16])
-def test_context_length_one_returns_v_bit_exact(dtype, partition):
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_context_length_one_returns_v_bit_exact(dtype, partition, kernel):
+    if kernel == "mfma" and dtype == "f32":
+        pytest.skip("the matrix-core kernel serves 16-bit caches only")
     cfg, wl = _single_token_state(dtype, 128, 16, 8, 2, 6, seed=3)
     gs = GpuState(wl)
     gs.write_step(0)
-    out = gs.decode(0, partition_size=partition)
+    out = gs.decode(0, partition_size=partition, flags=KERNELS[kernel])
     torch.cuda.synchronize()
     v = gs.step_v[0].float()  # [B][Hkv][d]
     expect = v.repeat_interleave(cfg.group, dim=1)
@@ -197,7 +206,10 @@ def test_context_length_one_returns_v_bit_exact(dtype, partition):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("partition", [0, 32, "one-pass"])
-def test_one_hot_probe_bit_exact(dtype, partition):
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_one_hot_probe_bit_exact(dtype, partition, kernel):
+    if kernel == "mfma" and dtype == "f32":
+        pytest.skip("the matrix-core kernel serves 16-bit caches only")
     """K = 0 except one target token whose key is c*q (scale*c*|q|^2 >= 200):
     every other weight underflows, so out == V[t*] exactly, for every t*."""
     L, d, bs, H = 96, 64, 16, 1
@@ -222,18 +234,19 @@ def test_one_hot_probe_bit_exact(dtype, partition):
         pa.cache_write(K.cuda(), V.cuda(), slots, kc, vc)
         out = torch.empty(1, 1, d, device="cuda")
         pa.decode(out, q.cuda(), kc, vc, bt, torch.tensor([L], dtype=torch.int32, device="cuda"),
-                  scale, bs, p)
+                  scale, bs, p, flags=KERNELS[kernel])
         torch.cuda.synchronize()
         assert torch.equal(out[0, 0].cpu(), V[t, 0].float()), f"t*={t}"
 
 
-def test_block_permutation_bit_identical():
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_block_permutation_bit_identical(kernel):
     """Moving physical blocks (and remapping the table) does not change a bit."""
     cfg = custom_config("perm", [33, 300, 1000], 8, 2, 128, "bf16", 16, seed=44)
     wl = Workload(cfg)
     gs = GpuState(wl)
     gs.write_step(0)
-    out1 = gs.decode(0)
+    out1 = gs.decode(0, flags=KERNELS[kernel])
     NB = wl.num_blocks
     perm = torch.randperm(NB, generator=torch.Generator().manual_seed(1)).cuda()
     kc2 = torch.empty_like(gs.kc)
@@ -244,12 +257,13 @@ def test_block_permutation_bit_identical():
     bt2 = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).to(torch.int32)
     out2 = torch.empty_like(out1)
     pa.decode(out2, gs.q[0], kc2, vc2, bt2.contiguous(), gs.ctx[0], cfg.attn_scale(),
-              cfg.block_size, 0)
+              cfg.block_size, 0, flags=KERNELS[kernel])
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
 
 
-def test_partition_sweep_within_tolerance():
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_partition_sweep_within_tolerance(kernel):
     cfg = custom_config("sweep", [1, 100, 1000, 4000], 8, 2, 128, "bf16", 16, seed=45)
     wl = Workload(cfg)
     st = oracle_state_empty(wl)
@@ -258,7 +272,7 @@ def test_partition_sweep_within_tolerance():
     st.write_step(0)
     ref = st.decode(0)
     for p in [16, 32, 48, 128, 256, 512, 1024, 4000, 4096]:
-        out = gs.decode(0, partition_size=p)
+        out = gs.decode(0, partition_size=p, flags=KERNELS[kernel])
         _check_decode(out, ref, "bf16")
 
 
