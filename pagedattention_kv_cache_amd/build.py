@@ -28,10 +28,17 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  The matrix-core kernel keeps its MFMA accumulators
+# in ordinary VGPRs: its online-softmax rescale multiplies them every few
+# chunks, and accumulator-register copies for that would raise the register
+# peak enough to cost a wave per SIMD.
+EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

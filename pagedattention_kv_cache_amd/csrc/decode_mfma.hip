@@ -41,47 +41,78 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 template <Elem E> struct Mma;
 template <> struct Mma<Elem::BF16> {
   using vec8 = bf16x8_t;
+  using vec4 = bf16x4_t;
   using scalar = __bf16;
-  static __device__ __forceinline__ f32x4_t mma(vec8 a, vec8 b, f32x4_t c) {
+  // S += K(16x32) . Q(32x16)
+  static __device__ __forceinline__ f32x4_t qk(vec8 a, vec8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // O^T += V^T(16x16) . P^T(16x16)
+  static __device__ __forceinline__ f32x4_t pv(vec4 a, vec4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
   }
 };
 template <> struct Mma<Elem::F16> {
   using vec8 = f16x8_t;
+  using vec4 = f16x4_t;
   using scalar = _Float16;
-  static __device__ __forceinline__ f32x4_t mma(vec8 a, vec8 b, f32x4_t c) {
+  static __device__ __forceinline__ f32x4_t qk(vec8 a, vec8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(vec4 a, vec4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
   }
 };
 
-constexpr int kChunk = 32;  // tokens per iteration
+constexpr int kChunk = 16;  // tokens per iteration: one 16-row QK^T tile
+
+// Raw buffer resource over [base, base + 2 GiB): 32-bit lane offsets, no
+// swizzle, dword data format (the gfx9 raw-buffer word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
 
 template <Elem KV, int D>
 struct Buffers {
-  using vec8 = typename Mma<KV>::vec8;
-  vec8 k[2][D / 32];  // [tile][dim chunk]
-  vec8 v[D / 16];     // [dim chunk]
+  typename Mma<KV>::vec8 k[D / 32];  // key row chunks of this lane's token
+  typename Mma<KV>::vec4 v[D / 16];  // 4-token value runs, one per 16-dim row chunk
 };
 
-template <Elem KV, int D, int G>
+// UB: every 16-token chunk lies in one cache block (block_size >= 16), so the
+// chunk's base address is wave-uniform (scalar registers) and each lane only
+// adds a fixed 32-bit offset; otherwise (block_size 8) lanes address their
+// own blocks.
+template <Elem KV, int D, int G, bool UB>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   using M = Mma<KV>;
   using vec8 = typename M::vec8;
+  using vec4 = typename M::vec4;
   using scalar = typename M::scalar;
   constexpr int KC = D / 32;  // QK^T k-chunks
   constexpr int VC = D / 16;  // P.V row chunks
   constexpr int RB = D * 2;   // bytes per key row
 
-  const int part = blockIdx.x;
-  const int b = blockIdx.z;
+  // grid.x walks (sequence, kv head, head chunk) fastest so that consecutive
+  // workgroups -- which the dispatcher deals round-robin to the XCDs -- carry
+  // the same partition index of different sequences and heads; grid.y walks
+  // partitions from the last to the first, so the short first partitions of
+  // short sequences are dispatched at the end.
   const int chunks = a.group / G;
-  const int h = blockIdx.y / chunks;
-  const int hq0 = h * a.group + (blockIdx.y % chunks) * G;
+  const int item = blockIdx.x;
+  const int per_seq = a.num_kv_heads * chunks;
+  const int b = item / per_seq;
+  const int hc = item - b * per_seq;
+  const int h = hc / chunks;
+  const int hq0 = h * a.group + (hc % chunks) * G;
+  const int part = (int)gridDim.y - 1 - (int)blockIdx.y;
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int j = lane >> 4;
@@ -108,6 +139,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
   const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
+  const int64_t vrow16 = (int64_t)16 * bs * 2;  // bytes between value rows 16 dims apart
 
   // queries: column n = head hq0 + n (zero beyond the group)
   vec8 qv[KC];
@@ -123,36 +155,45 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // block-id window: lane i holds the physical block of logical block wb + i
-  int wb = t_begin >> lbs;
-  int bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
+  // per-lane byte offsets inside a (block, head) tile
+  const uint32_t koff = (uint32_t)(n * RB + 16 * j);       // key row n, dims 8j.. of each 32
+  const uint32_t voff = (uint32_t)((n * bs + 4 * j) * 2);  // value row n, tokens 4j..4j+3
 
-  // token of this lane's key row in tiles A and B, and of its value run
-  const int tokA = 8 * (n >> 2) + (n & 3);
-  const int tokB = tokA + 4;
-  const int tokV = 8 * j;
+  int wb = 0;       // first logical block of the current block-id window
+  int bt_lane = 0;  // lane i: physical block of logical block wb + i
 
+  // Loads of one 16-token chunk.  Issued unconditionally (a chunk past the
+  // end re-reads the last one), so every path through the loop has the same
+  // loads in flight and the compiler's wait counts stay exact.
   auto issue = [&](Buffers<KV, D>& buf, int t0) {
-    const int need_last = min((t0 + kChunk - 1) >> lbs, last_blk);
-    if (need_last - wb >= 64) {  // slide the block-id window (uniform)
-      wb = t0 >> lbs;
-      bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
-    }
-    const int ta = t0 + tokA, tb = t0 + tokB, tv = t0 + tokV;
-    const int pa_ = __shfl(bt_lane, min(ta >> lbs, last_blk) - wb);
-    const int pb_ = __shfl(bt_lane, min(tb >> lbs, last_blk) - wb);
-    const int pv_ = __shfl(bt_lane, min(tv >> lbs, last_blk) - wb);
-    const char* ka = kc + (int64_t)pa_ * block_stride + (int64_t)(ta & (bs - 1)) * RB + 16 * j;
-    const char* kb = kc + (int64_t)pb_ * block_stride + (int64_t)(tb & (bs - 1)) * RB + 16 * j;
-    const char* vp = vc + (int64_t)pv_ * block_stride + ((int64_t)n * bs + (tv & (bs - 1))) * 2;
+    if constexpr (UB) {
+      // one block: a buffer resource based at the chunk's key / value tile,
+      // per-lane 32-bit offsets, the 16-dim row stride as the scalar offset
+      const int phys = __builtin_amdgcn_readlane(bt_lane, min(t0 >> lbs, last_blk) - wb);
+      const int64_t tile = (int64_t)phys * block_stride;
+      const int in_blk = t0 & (bs - 1);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + tile + (int64_t)in_blk * RB);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + tile + (int64_t)in_blk * 2);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      buf.k[0][c] = *reinterpret_cast<const vec8*>(ka + 64 * c);
-      buf.k[1][c] = *reinterpret_cast<const vec8*>(kb + 64 * c);
-    }
+      for (int c = 0; c < KC; ++c)
+        buf.k[c] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rk, (int)koff + 64 * c, 0, 0));
 #pragma unroll
-    for (int c = 0; c < VC; ++c)
-      buf.v[c] = *reinterpret_cast<const vec8*>(vp + (int64_t)c * 16 * bs * 2);
+      for (int c = 0; c < VC; ++c)
+        buf.v[c] = __builtin_bit_cast(vec4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                rv, (int)voff, c * (int)vrow16, 0));
+    } else {
+      const int tk = t0 + n;      // this lane's key row
+      const int tv = t0 + 4 * j;  // first token of this lane's value run
+      const int pk = __shfl(bt_lane, min(tk >> lbs, last_blk) - wb);
+      const int pv = __shfl(bt_lane, min(tv >> lbs, last_blk) - wb);
+      const char* kp = kc + (int64_t)pk * block_stride + (int64_t)(tk & (bs - 1)) * RB + 16 * j;
+      const char* vp = vc + (int64_t)pv * block_stride + ((int64_t)n * bs + (tv & (bs - 1))) * 2;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) buf.k[c] = *reinterpret_cast<const vec8*>(kp + 64 * c);
+#pragma unroll
+      for (int c = 0; c < VC; ++c) buf.v[c] = *reinterpret_cast<const vec4*>(vp + c * vrow16);
+    }
   };
 
   f32x4_t o[VC];
@@ -161,42 +202,33 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   float m = -INFINITY;  // running max of head n (log2 domain), uniform over j
   float lsum = 0.0f;    // this lane's share of head n's sum
 
-  auto compute = [&](Buffers<KV, D>& buf, int t0) {
-    f32x4_t sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](Buffers<KV, D>& buf, int t0, int t_stop) {
+    f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      sa = M::mma(buf.k[0][c], qv[c], sa);
-      sb = M::mma(buf.k[1][c], qv[c], sb);
-    }
-    float s[8];
+    for (int c = 0; c < KC; ++c) sacc = M::qk(buf.k[c], qv[c], sacc);
+    float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[r] = sa[r] * a.scale_log2;
-      s[4 + r] = sb[r] * a.scale_log2;
-    }
-    const bool tail = t0 + kChunk > t_end;
-    if (tail) {  // uniform: mask tokens past the partition / context
-      const int nv = t_end - t0 - 8 * j;  // valid tokens of this lane's run
+    for (int r = 0; r < 4; ++r) s[r] = sacc[r] * a.scale_log2;
+    if (t0 + kChunk > t_stop) {  // uniform: mask tokens past the partition / context
+      const int nv = t_stop - t0 - 4 * j;  // valid tokens of this lane's run
 #pragma unroll
-      for (int r = 0; r < 8; ++r) s[r] = r < nv ? s[r] : -INFINITY;
+      for (int r = 0; r < 4; ++r) s[r] = r < nv ? s[r] : -INFINITY;
 #pragma unroll
       for (int c = 0; c < VC; ++c)
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
+        for (int r = 0; r < 4; ++r)
           if (r >= nv) buf.v[c][r] = (scalar)0.0f;
     }
-    float mx = s[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m, mx);
     const float alpha = fast_exp2(m - m_new);
     m = m_new;
-    vec8 phi, plo;
+    vec4 phi, plo;
     float ps = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const float p = fast_exp2(s[r] - m_new);
       ps += p;
       const scalar hi = (scalar)p;
@@ -212,23 +244,30 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int c = 0; c < VC; ++c) {
-      o[c] = M::mma(buf.v[c], phi, o[c]);
-      o[c] = M::mma(buf.v[c], plo, o[c]);
+      o[c] = M::pv(buf.v[c], phi, o[c]);
+      o[c] = M::pv(buf.v[c], plo, o[c]);
     }
   };
 
+  // Walk the partition in windows of 64 blocks (one block id per lane); inside
+  // a window, chunk i+1 is loaded while chunk i is computed.
   Buffers<KV, D> b0, b1;
-  int t0 = t_begin;
-  issue(b0, t0);
-  for (;;) {
-    if (t0 + kChunk < t_end) issue(b1, t0 + kChunk);
-    compute(b0, t0);
-    t0 += kChunk;
-    if (t0 >= t_end) break;
-    if (t0 + kChunk < t_end) issue(b0, t0 + kChunk);
-    compute(b1, t0);
-    t0 += kChunk;
-    if (t0 >= t_end) break;
+  const int window = 64 * bs;
+  for (int w0 = t_begin; w0 < t_end; w0 += window) {
+    const int w1 = min(w0 + window, t_end);
+    wb = w0 >> lbs;
+    bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
+    const int nc = (w1 - w0 + kChunk - 1) / kChunk;
+    const int last_t0 = w0 + (nc - 1) * kChunk;
+    issue(b0, w0);
+    for (int i = 0; i < nc; i += 2) {
+      const int t0 = w0 + i * kChunk;
+      issue(b1, min(t0 + kChunk, last_t0));
+      compute(b0, t0, w1);
+      if (i + 1 >= nc) break;
+      issue(b0, min(t0 + 2 * kChunk, last_t0));
+      compute(b1, t0 + kChunk, w1);
+    }
   }
 
   // ---- finish the work item ------------------------------------------------
@@ -259,10 +298,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 
 template <Elem KV, int D>
 hipError_t dispatch_g(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  const bool ub = a.block_size >= 16;
   switch (a.heads_per_item) {
-#define PA_CASE(GG)                                                               \
-  case GG:                                                                        \
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, GG>), grid, dim3(64), 0, s, a); \
+#define PA_CASE(GG)                                                                        \
+  case GG:                                                                                 \
+    if (ub)                                                                                \
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, GG, true>), grid, dim3(64), 0, s, a);  \
+    else                                                                                   \
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, GG, false>), grid, dim3(64), 0, s, a); \
     break;
     PA_CASE(1) PA_CASE(2) PA_CASE(4) PA_CASE(8) PA_CASE(16)
     PA_CASE(3) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(10) PA_CASE(12)
@@ -286,7 +329,7 @@ bool mfma_supports_heads(int heads_per_item) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s) {
   const int chunks = a.group / a.heads_per_item;
-  dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * chunks), (unsigned)a.num_seqs);
+  dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * chunks), (unsigned)a.max_partitions);
   if (kv_dtype == 2) {
     if (head_dim == 128) return dispatch_g<Elem::BF16, 128>(a, grid, s);
     if (head_dim == 64) return dispatch_g<Elem::BF16, 64>(a, grid, s);

@@ -45,11 +45,19 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   static_assert(RL >= 8 && RL <= 64 && 64 % RL == 0, "row layout");
   static_assert(TPI <= SEG, "a key load instruction stays inside one block");
 
-  const int part = blockIdx.x;
-  const int b = blockIdx.z;
+  // grid.x walks (sequence, kv head, head chunk) fastest so that consecutive
+  // workgroups -- which the dispatcher deals round-robin to the XCDs -- carry
+  // the same partition index of different sequences and heads; grid.y walks
+  // partitions from the last to the first, so the short first partitions of
+  // short sequences are dispatched at the end.
   const int chunks = a.group / G;
-  const int h = blockIdx.y / chunks;
-  const int hq0 = h * a.group + (blockIdx.y % chunks) * G;
+  const int item = blockIdx.x;
+  const int per_seq = a.num_kv_heads * chunks;
+  const int b = item / per_seq;
+  const int hc = item - b * per_seq;
+  const int h = hc / chunks;
+  const int hq0 = h * a.group + (hc % chunks) * G;
+  const int part = (int)gridDim.y - 1 - (int)blockIdx.y;
   const int lane = threadIdx.x;
   const int c = lane % RL;    // 16-byte chunk of the key row
   const int row = lane / RL;  // token within a key load instruction
@@ -237,7 +245,7 @@ hipError_t dispatch_d(const DecodeArgs& a, int head_dim, dim3 grid, hipStream_t 
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s) {
   const int chunks = a.group / a.heads_per_item;
-  dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * chunks), (unsigned)a.num_seqs);
+  dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * chunks), (unsigned)a.max_partitions);
   switch (kv_dtype) {
     case 0: return dispatch_d<Elem::F32>(a, head_dim, grid, s);
     case 1: return dispatch_d<Elem::F16>(a, head_dim, grid, s);

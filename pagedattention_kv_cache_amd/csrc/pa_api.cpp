@@ -214,7 +214,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   const size_t need = workspace_bytes_for(s, p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
-  if (np > 65535 || (int64_t)num_seqs > 65535) return PA_ERR_SHAPE;
+  if (np > 65535 || (int64_t)num_seqs * num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
 
   pa::DecodeArgs a;
   a.out = out;
