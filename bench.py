@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published
 KERNEL_SOURCES = ["decode_valu.hip", "decode_mfma.hip", "pa_device.hpp", "pa_launch.hpp",
-                  "pa_api.cpp"]
+                  "pa_api.cpp", "../build.py"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
 
 
@@ -62,6 +62,10 @@ def parse_args(argv=None):
     ap.add_argument("--flags", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, host cores)")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="KV-cache copies the steps rotate over, so no step re-reads what the "
+                         "previous one left in the 256 MB Infinity Cache")
+    ap.add_argument("--no-stream-probe", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -174,6 +178,38 @@ def cpu_baseline(wl, okc, ovc, threads):
     }
 
 
+def stream_probe(dev, gib: int = 4, reps: int = 10) -> float:
+    """Attainable HBM read bandwidth: best of several grid sizes of a plain
+    non-temporal streaming read over `gib` GiB (libpa_probe.so)."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "pagedattention_kv_cache_amd", "libpa_probe.so"))
+    fn = lib.pa_probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_void_p]
+    nbytes = gib * 2**30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = 0.0
+    for blocks in (4096, 8192, 16384):
+        for _ in range(2):
+            assert fn(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream) == 0
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream)
+        e1.record(stream)
+        e1.synchronize()
+        best = max(best, nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -232,6 +268,11 @@ def run(args):
         ovc = np.full(tuple(vc.shape), POISON_BITS[c.dtype], bits)
     t_fill = time.perf_counter()
     fill_caches(wl, dev, kc, vc, (okc, ovc) if want_cpu else None)
+    # further layers: device copies of the first one (same values, own memory)
+    kcs, vcs = [kc], [vc]
+    for _ in range(1, max(1, args.layers)):
+        kcs.append(kc.clone())
+        vcs.append(vc.clone())
     torch.cuda.synchronize()
     t_fill = time.perf_counter() - t_fill
 
@@ -251,17 +292,22 @@ def run(args):
     scale = c.attn_scale()
     stream = torch.cuda.current_stream(dev)
 
+    n_layers = len(kcs)
+
     def step(i, ev=None):
-        s = i % c.steps
+        # step i: decode step (i // n_layers) % steps of layer i % n_layers
+        s = (i // n_layers) % c.steps
+        k_l, v_l = kcs[i % n_layers], vcs[i % n_layers]
         if ev is not None:
             ev[0].record(stream)
-        pa.cache_write(sk[s], sv[s], slots[s], kc, vc)
+        pa.cache_write(sk[s], sv[s], slots[s], k_l, v_l)
         if ev is not None:
             ev[1].record(stream)
-        pa.decode_partitions(out, qs[s], kc, vc, bt, ctx[s], scale, c.block_size, part, ws, flags)
+        pa.decode_partitions(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
+                             flags)
         if ev is not None:
             ev[2].record(stream)
-        pa.decode_merge(out, qs[s], kc, vc, bt, ctx[s], scale, c.block_size, part, ws, flags)
+        pa.decode_merge(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws, flags)
         if ev is not None:
             ev[3].record(stream)
 
@@ -280,10 +326,11 @@ def run(args):
     dec_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
     merge_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
 
-    kv = statistics.mean(wl.kv_bytes(i % c.steps) for i in range(args.steps))
+    kv = statistics.mean(wl.kv_bytes((i // n_layers) % c.steps) for i in range(args.steps))
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = kv / (dec_ms * 1e-3) / 1e9
 
+    attainable = None if args.no_stream_probe else stream_probe(dev)
     traffic = None
     tf = TRAFFIC_FILE.format(workload=c.name)
     if os.path.exists(tf):
@@ -291,7 +338,7 @@ def run(args):
         if rec.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("traffic_bytes")
 
-    kname = "decode_valu_kernel" if flags != pa.FORCE_MFMA else "decode_mfma_kernel"
+    kname = f"decode_{pa.decode_kernel(c.num_q_heads, c.num_kv_heads, kdt, kdt, flags)}_kernel"
     result = {
         "metric": "paged decode attention: achieved KV HBM GB/s (% peak) + tokens/s, 1 MI355X",
         "value": round(value, 2),
@@ -325,7 +372,11 @@ def run(args):
             "algorithmic_bytes_per_launch": int(kv),
         },
         "fill_seconds": round(t_fill, 2),
+        "kv_cache_layers": n_layers,
     }
+    if attainable:
+        result["attainable_read_gbps"] = round(attainable, 1)
+        result["roofline"]["frac_of_attainable"] = round(achieved / attainable, 4)
     if want_cpu:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(wl, okc, ovc, threads)

@@ -178,6 +178,14 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t max_blocks_per_seq, int32_t kv_dtype, uint32_t flags);
 
 /*
+ * The decode kernel family pa_decode runs for these arguments:
+ * PA_DECODE_FORCE_VALU (1) or PA_DECODE_FORCE_MFMA (2); a negative pa_status
+ * for an unsupported combination.
+ */
+int32_t pa_decode_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t q_dtype,
+                         int32_t kv_dtype, uint32_t flags);
+
+/*
  * Workspace bytes pa_decode needs for these arguments (partition_size as
  * passed to pa_decode, 0 allowed).  0 when a single pass suffices.  Returns 0
  * for invalid arguments as well; pa_decode reports those.

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, u32]
         L.pa_decode_workspace_size.restype = sz
         L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, u32]
+        L.pa_decode_kernel.restype = i32
+        L.pa_decode_kernel.argtypes = [i32, i32, i32, i32, u32]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_status_string.argtypes = [i32]
         L.pa_abi_version.restype = i32
@@ -115,6 +117,14 @@ def decode_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, he
                                        max_blocks_per_seq, _DTYPE[kv_dtype], flags)
     _check(min(p, 0))
     return p
+
+
+def decode_kernel(num_q_heads: int, num_kv_heads: int, q_dtype: torch.dtype,
+                  kv_dtype: torch.dtype, flags: int = AUTO) -> str:
+    """Which decode kernel family runs for these arguments: "valu" or "mfma"."""
+    k = lib().pa_decode_kernel(num_q_heads, num_kv_heads, _DTYPE[q_dtype], _DTYPE[kv_dtype], flags)
+    _check(min(k, 0))
+    return {FORCE_VALU: "valu", FORCE_MFMA: "mfma"}[k]
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -170,6 +170,18 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return pick_partition(s);
 }
 
+int32_t pa_decode_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t q_dtype,
+                         int32_t kv_dtype, uint32_t flags) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return PA_ERR_SHAPE;
+  if (!elem_bytes(q_dtype) || !elem_bytes(kv_dtype)) return PA_ERR_DTYPE;
+  if (q_dtype != kv_dtype && q_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
+  if (flags > PA_DECODE_FORCE_MFMA) return PA_ERR_UNSUPPORTED;
+  if (flags == PA_DECODE_FORCE_MFMA && (kv_dtype == PA_DTYPE_F32 || q_dtype != kv_dtype))
+    return PA_ERR_UNSUPPORTED;
+  return use_mfma(flags, kv_dtype, q_dtype, num_q_heads / num_kv_heads) ? PA_DECODE_FORCE_MFMA
+                                                                        : PA_DECODE_FORCE_VALU;
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t partition_size, int32_t kv_dtype, uint32_t flags) {

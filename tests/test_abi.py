@@ -28,8 +28,8 @@ pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
                                 reason="host-validation tests use fake pointers; CPU only")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
@@ -37,11 +37,27 @@ def _declared_functions():
 def test_library_loads_and_exports_header_symbols():
     L = pa.lib()
     names = _declared_functions()
-    assert {"pa_cache_write", "pa_decode", "pa_decode_workspace_size",
-            "pa_decode_partition_size", "pa_status_string", "pa_abi_version"} <= set(names)
+    assert {"pa_cache_write", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
+            "pa_decode_workspace_size", "pa_decode_partition_size", "pa_decode_kernel",
+            "pa_status_string", "pa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"libpa.so does not export {n}"
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_probe_library_exports_its_header():
+    probe = ctypes.CDLL(os.path.join(ROOT, "pagedattention_kv_cache_amd", "libpa_probe.so"))
+    names = _declared_functions(os.path.join(ROOT, "include", "pa_probe.h"))
+    assert names == ["pa_probe_stream_read"]
+    for n in names:
+        assert hasattr(probe, n)
+    fn = probe.pa_probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_void_p]
+    assert fn(None, 1024, FAKE, 64, None) == -1  # invalid arguments: nothing launched
+    assert fn(FAKE, 1000, FAKE, 64, None) == -1
+    assert fn(FAKE, 1024, FAKE, 0, None) == -1
 
 
 def test_status_strings_and_version():
@@ -132,6 +148,20 @@ def test_decode_validation(kw, status):
 
 def test_decode_empty_batch_is_noop():
     assert _dec(B=0, out=None, q=None, bt=None, cl=None) == OK
+
+
+def test_kernel_family_policy():
+    L = pa.lib()
+    assert L.pa_decode_kernel(32, 8, BF16, BF16, 0) == pa.FORCE_MFMA   # GQA group of 4
+    assert L.pa_decode_kernel(64, 8, BF16, BF16, 0) == pa.FORCE_MFMA
+    assert L.pa_decode_kernel(32, 32, F16, F16, 0) == pa.FORCE_VALU    # plain MHA
+    assert L.pa_decode_kernel(4, 4, F32, F32, 0) == pa.FORCE_VALU      # fp32 cache
+    assert L.pa_decode_kernel(32, 8, F32, BF16, 0) == pa.FORCE_VALU    # fp32 queries
+    assert L.pa_decode_kernel(32, 32, F16, F16, pa.FORCE_MFMA) == pa.FORCE_MFMA
+    assert L.pa_decode_kernel(32, 8, BF16, BF16, pa.FORCE_VALU) == pa.FORCE_VALU
+    assert L.pa_decode_kernel(32, 8, F32, F32, pa.FORCE_MFMA) == EUNSUP
+    assert L.pa_decode_kernel(30, 8, BF16, BF16, 0) == ESHAPE
+    assert L.pa_decode_kernel(32, 8, F16, BF16, 0) == EDTYPE
 
 
 def test_partition_policy_and_workspace_size():
