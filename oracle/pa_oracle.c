@@ -21,8 +21,11 @@
  *    mapping, per-sequence block tables, sequence lengths and a block size.
  *
  * Storage convention shared with the GPU library (a format both sides must
- * agree on, not arithmetic):
- *   key cache   [num_blocks][num_kv_heads][block_size][head_dim]
+ * agree on, not arithmetic), with X = 16 / element bytes (8 for the 16-bit
+ * types, 4 for fp32):
+ *   key cache   [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *               (key element e of the token at offset o of a block is at
+ *               chunk e / X, row o, lane e % X)
  *   value cache [num_blocks][num_kv_heads][head_dim][block_size]
  *   slot s -> block s / block_size, offset s % block_size.
  *
@@ -156,9 +159,9 @@ int orc_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                     int32_t block_size, int32_t dtype) {
   int eb = orc_elem_bytes(dtype);
   if (!eb || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      num_blocks <= 0 || num_tokens < 0)
+      num_blocks <= 0 || num_tokens < 0 || head_dim % (16 / eb) != 0)
     return ORC_ERR_ARG;
-  const int64_t H = num_kv_heads, D = head_dim, BS = block_size;
+  const int64_t H = num_kv_heads, D = head_dim, BS = block_size, X = 16 / eb;
   for (int64_t i = 0; i < num_tokens; ++i) {
     int64_t slot = slot_mapping[i];
     if (slot < 0) continue;
@@ -169,7 +172,7 @@ int orc_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
       for (int64_t e = 0; e < D; ++e) {
         int64_t src_k = i * k_token_stride + h * D + e;
         int64_t src_v = i * v_token_stride + h * D + e;
-        int64_t dst_k = ((blk * H + h) * BS + off) * D + e;
+        int64_t dst_k = (((blk * H + h) * (D / X) + e / X) * BS + off) * X + e % X;
         int64_t dst_v = ((blk * H + h) * D + e) * BS + off;
         memcpy((char*)k_cache + dst_k * eb, (const char*)k + src_k * eb, eb);
         memcpy((char*)v_cache + dst_v * eb, (const char*)v + src_v * eb, eb);
@@ -210,6 +213,7 @@ typedef struct {
  */
 static int orc_decode_row(const orc_decode_job* J, int64_t row) {
   const int64_t Hq = J->num_q_heads, Hkv = J->num_kv_heads, D = J->head_dim;
+  const int64_t X = 16 / orc_elem_bytes(J->kv_dtype);
   const int64_t BS = J->block_size, MB = J->max_blocks_per_seq;
   const int64_t b = row / Hq, hq = row % Hq;
   const int64_t group = Hq / Hkv;
@@ -233,11 +237,11 @@ static int orc_decode_row(const orc_decode_job* J, int64_t row) {
       free(acc);
       return ORC_ERR_BLOCK;
     }
-    int64_t krow = ((phys * Hkv + hk) * BS + t % BS) * D;
+    const int64_t ktile = (phys * Hkv + hk) * D * BS;  // this block's key tile
     double dot = 0.0;
     for (int64_t e = 0; e < D; ++e)
       dot += orc_load(J->q, J->q_dtype, (b * Hq + hq) * D + e) *
-             orc_load(J->k_cache, J->kv_dtype, krow + e);
+             orc_load(J->k_cache, J->kv_dtype, ktile + ((e / X) * BS + t % BS) * X + e % X);
     s[t] = J->scale * dot;
   }
 
@@ -297,7 +301,8 @@ int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
   if (!orc_elem_bytes(q_dtype) || !orc_elem_bytes(kv_dtype)) return ORC_ERR_ARG;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0)
+      max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      head_dim % (16 / orc_elem_bytes(kv_dtype)) != 0)
     return ORC_ERR_ARG;
   if (rows) {
     for (int64_t i = 0; i < n_rows; ++i)

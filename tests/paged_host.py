@@ -15,11 +15,24 @@ from pagedattention_kv_cache_amd.workloads import POISON_BITS, Workload, raw_bit
 _BITS_NP = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
 
 
+def key_chunk(dtype: str) -> int:
+    """X: elements per 16-byte chunk of the key layout."""
+    return 4 if dtype == "f32" else 8
+
+
 def poisoned_pool(wl: Workload, transposed: bool) -> np.ndarray:
+    """Value pool [NB][Hkv][d][bs] (transposed=True) or key pool
+    [NB][Hkv][d/X][bs][X], filled with the dtype's quiet NaN."""
     c = wl.cfg
+    X = key_chunk(c.dtype)
     shape = ((wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size) if transposed else
-             (wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim))
+             (wl.num_blocks, c.num_kv_heads, c.head_dim // X, c.block_size, X))
     return np.full(shape, POISON_BITS[c.dtype], dtype=_BITS_NP[c.dtype])
+
+
+def key_rows(kc: np.ndarray, blk: int, off: int) -> np.ndarray:
+    """The [Hkv][d] key rows of the token at (block, offset) of a key pool."""
+    return kc[blk, :, :, off, :].reshape(kc.shape[1], -1)
 
 
 class OracleState:

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from pagedattention_kv_cache_amd.workloads import CONFIGS, Workload, custom_config, raw_bits
-from tests.paged_host import OracleState, logical_kv, poisoned_pool
+from tests.paged_host import OracleState, key_chunk, key_rows, logical_kv, poisoned_pool
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -71,37 +71,54 @@ def test_f32_decoder_patterns():
 # ---------------------------------------------------------------- cache write
 
 def _read_layout_fixture():
-    K, V = [], []
+    cases, cur = [], None
     with open(os.path.join(GOLDEN, "cache_write_layout.txt")) as f:
         for line in f:
             line = line.split("#")[0].strip()
             if not line:
                 continue
             kind, *vals = line.split()
-            (K if kind == "K" else V).append(tuple(int(x) for x in vals))
-    return K, V
+            if kind == "CASE":
+                name, dtype, nb, h, bs, d, *slots = vals
+                cur = dict(dtype=dtype, NB=int(nb), H=int(h), bs=int(bs), d=int(d),
+                           slots=[int(x) for x in slots], K=[], V=[])
+                cases.append(cur)
+            else:
+                cur[kind].append(tuple(int(x) for x in vals))
+    return cases
 
 
 def test_cache_write_hand_worked_layout():
-    NB, H, bs, d = 3, 2, 2, 3
-    i = np.arange(4)[:, None, None]
-    h = np.arange(H)[None, :, None]
-    e = np.arange(d)[None, None, :]
-    k = (100 * i + 10 * h + e + 1).astype(np.float32)
-    v = -k
-    kc = np.zeros((NB, H, bs, d), np.float32)
-    vc = np.zeros((NB, H, d, bs), np.float32)
-    oracle.cache_write(k.view(np.uint32), v.view(np.uint32), np.array([5, 0, -1, 2]),
-                       kc.view(np.uint32), vc.view(np.uint32), "f32")
-    K, V = _read_layout_fixture()
-    ek = np.zeros_like(kc)
-    ev = np.zeros_like(vc)
-    for blk, hh, off, ee, val in K:
-        ek[blk, hh, off, ee] = val
-    for blk, hh, ee, off, val in V:
-        ev[blk, hh, ee, off] = val
-    assert np.array_equal(kc, ek)
-    assert np.array_equal(vc, ev)
+    cases = _read_layout_fixture()
+    assert [c["dtype"] for c in cases] == ["f32", "bf16"]
+    for cs in cases:
+        NB, H, bs, d, T = cs["NB"], cs["H"], cs["bs"], cs["d"], len(cs["slots"])
+        X = 4 if cs["dtype"] == "f32" else 8
+        i = np.arange(T)[:, None, None]
+        h = np.arange(H)[None, :, None]
+        e = np.arange(d)[None, None, :]
+        k = (100 * i + 10 * h + e + 1).astype(np.float32)
+        ek = np.zeros((NB, H, d // X, bs, X), np.float32)
+        ev = np.zeros((NB, H, d, bs), np.float32)
+        for blk, hh, ch, off, lane, val in cs["K"]:
+            ek[blk, hh, ch, off, lane] = val
+        for blk, hh, ee, off, val in cs["V"]:
+            ev[blk, hh, ee, off] = val
+        if cs["dtype"] == "f32":
+            kb, vb = k.view(np.uint32), (-k).view(np.uint32)
+            kc = np.zeros(ek.shape, np.uint32)
+            vc = np.zeros(ev.shape, np.uint32)
+            exp_k, exp_v = ek.view(np.uint32), ev.view(np.uint32)
+        else:
+            kb = raw_bits(torch.from_numpy(k).to(torch.bfloat16))
+            vb = raw_bits(torch.from_numpy(-k).to(torch.bfloat16))
+            kc = np.zeros(ek.shape, np.uint16)
+            vc = np.zeros(ev.shape, np.uint16)
+            exp_k = raw_bits(torch.from_numpy(ek).to(torch.bfloat16))
+            exp_v = raw_bits(torch.from_numpy(ev).to(torch.bfloat16))
+        oracle.cache_write(kb, vb, np.array(cs["slots"]), kc, vc, cs["dtype"])
+        assert np.array_equal(kc, exp_k), cs["dtype"]
+        assert np.array_equal(vc, exp_v), cs["dtype"]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -122,11 +139,15 @@ def test_cache_write_roundtrip_and_poison(dtype):
         for pos in range(wl.lens0[b]):
             blk = wl.block_tables[b, pos // cfg.block_size]
             off = pos % cfg.block_size
-            assert np.array_equal(st.kc[blk, :, off, :], kb[pos])
+            assert np.array_equal(key_rows(st.kc, blk, off), kb[pos])
             assert np.array_equal(st.vc[blk, :, :, off], vb[pos])
             written[blk, off] = True
     pois = poisoned_pool(wl, False)
-    assert np.array_equal(st.kc.transpose(0, 2, 1, 3)[~written], pois.transpose(0, 2, 1, 3)[~written])
+    # key pool as [block][offset][...]: slots never written keep their poison
+    kt = st.kc.transpose(0, 3, 1, 2, 4)
+    assert np.array_equal(kt[~written], pois.transpose(0, 3, 1, 2, 4)[~written])
+    vt = st.vc.transpose(0, 3, 1, 2)
+    assert np.array_equal(vt[~written], poisoned_pool(wl, True).transpose(0, 3, 1, 2)[~written])
     # skip semantics: all-negative slots leave the pools untouched
     kc0, vc0 = st.kc.copy(), st.vc.copy()
     oracle.cache_write(raw_bits(st.step_k[0]), raw_bits(st.step_v[0]),
@@ -135,7 +156,7 @@ def test_cache_write_roundtrip_and_poison(dtype):
 
 
 def test_cache_write_rejects_out_of_range_slot():
-    kc = np.zeros((2, 1, 4, 4), np.float32)
+    kc = np.zeros((2, 1, 1, 4, 4), np.float32)
     vc = np.zeros((2, 1, 4, 4), np.float32)
     k = np.ones((1, 1, 4), np.float32)
     with pytest.raises(oracle.OracleError):
@@ -200,7 +221,8 @@ def _paged_from_logical(Ks, Vs, bs, perm_seed, nb_extra=3, dtype="f32"):
     perm = rng.permutation(NB)
     bits = np.uint32 if dtype == "f32" else np.uint16
     from pagedattention_kv_cache_amd.workloads import POISON_BITS
-    kc = np.full((NB, H, bs, d), POISON_BITS[dtype], bits)
+    X = key_chunk(dtype)
+    kc = np.full((NB, H, d // X, bs, X), POISON_BITS[dtype], bits)
     vc = np.full((NB, H, d, bs), POISON_BITS[dtype], bits)
     MB = max(nblk)
     bt = np.full((len(Ks), MB), -1, np.int32)
