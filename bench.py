@@ -253,10 +253,10 @@ def run(args):
         del src, dst
 
     kdt = DTYPE_TORCH[c.dtype]
-    kc = torch.empty((wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim), dtype=kdt,
-                     device=dev)
-    vc = torch.empty((wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size), dtype=kdt,
-                     device=dev)
+    kc = torch.empty(pa.key_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size,
+                                        kdt), dtype=kdt, device=dev)
+    vc = torch.empty(pa.value_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim,
+                                          c.block_size), dtype=kdt, device=dev)
     want_cpu = not args.no_cpu_baseline
     okc = ovc = None
     if want_cpu:

@@ -19,7 +19,7 @@
  *                   not what is computed).  Long or uneven contexts are split
  *                   into partitions whose partial results are merged with a
  *                   log-sum-exp reduction (same talk, passage on the second
- *                   PagedAttention kernel, "similar to flash decoding").
+ *                   PagedAttention kernel, likened there to flash decoding).
  *
  * Conventions
  *   - All tensor arguments are DEVICE pointers to densely packed row-major
@@ -33,11 +33,13 @@
  *   - Errors are reported by the return value: a negative pa_status, detected
  *     on the host before anything is launched (or PA_ERR_HIP if a launch
  *     fails).  No C++ exception crosses this interface.
- *   - Cache layout (chosen for gfx950, see each kernel):
- *       key cache   [num_blocks][num_kv_heads][block_size][head_dim]
+ *   - Cache layout (chosen for gfx950, see each kernel), with X = 16 bytes /
+ *     element size (8 for f16/bf16, 4 for f32):
+ *       key cache   [num_blocks][num_kv_heads][head_dim / X][block_size][X]
  *       value cache [num_blocks][num_kv_heads][head_dim][block_size]
- *     so a token's key row is one contiguous head_dim run and, for one
- *     dimension, a block's values for consecutive tokens are contiguous.
+ *     Key element e of the token at offset o lives in 16-byte chunk e / X at
+ *     row o, so one chunk of consecutive tokens is a contiguous run; for one
+ *     value dimension, a block's consecutive tokens are contiguous too.
  *   - Slot s addresses block s / block_size, offset s % block_size.
  *   - Block-table entries and slots are preconditions: entries
  *     block_tables[b][0 .. ceil(L_b/block_size)-1] must lie in
@@ -77,10 +79,10 @@ typedef enum pa_status {
 
 /*
  * pa_cache_write -- for every token i in [0, num_tokens) whose
- * slot_mapping[i] >= 0, copy k[i][h][:] into
- * k_cache[slot / block_size][h][slot % block_size][:] and v[i][h][:] into
- * v_cache[slot / block_size][h][:][slot % block_size], for all kv heads h, as
- * raw bits.  Tokens with a negative slot are skipped (padding).  All other
+ * slot_mapping[i] >= 0, copy k[i][h][e] into
+ * k_cache[slot / block_size][h][e / X][slot % block_size][e % X] and
+ * v[i][h][e] into v_cache[slot / block_size][h][e][slot % block_size], for all
+ * kv heads h and dims e, as raw bits.  Tokens with a negative slot are skipped (padding).  All other
  * cache bytes are left unchanged.
  *
  *   k, v            device, dtype, token i / head h / dim e at
@@ -148,7 +150,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *   workspace, and writes `out` directly for sequences that fit one partition.
  * pa_decode_merge: for sequences with more than one partition, merges the
  *   workspace entries by log-sum-exp into `out` ("vLLM Project Update" talk,
- *   second PagedAttention kernel, "similar to flash decoding").  Launches
+ *   second PagedAttention kernel, likened there to flash decoding).  Launches
  *   nothing when every sequence fits one partition.
  * pa_decode(...) == pa_decode_partitions(...) followed by pa_decode_merge(...)
  * on the same stream.

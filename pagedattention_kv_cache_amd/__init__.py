@@ -10,8 +10,9 @@ fallback.  If libpa.so is missing, :func:`lib` raises -- build it with
     decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
            block_size, partition_size=0, workspace=None, flags=AUTO)
 
-Cache tensors: ``k_cache`` [num_blocks][num_kv_heads][block_size][head_dim],
-``v_cache`` [num_blocks][num_kv_heads][head_dim][block_size].
+Cache tensors: ``k_cache`` [num_blocks][num_kv_heads][head_dim/X][block_size][X]
+with X = 16 bytes / element size (see :func:`key_cache_shape`), ``v_cache``
+[num_blocks][num_kv_heads][head_dim][block_size].
 """
 from __future__ import annotations
 
@@ -34,6 +35,33 @@ class PAError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"pa status {status}: {message}")
         self.status = status
+
+
+def key_chunk(dtype: torch.dtype) -> int:
+    """X: elements per 16-byte chunk of the key cache layout."""
+    return 16 // torch.tensor([], dtype=dtype).element_size()
+
+
+def key_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                    dtype: torch.dtype) -> tuple:
+    X = key_chunk(dtype)
+    return (num_blocks, num_kv_heads, head_dim // X, block_size, X)
+
+
+def value_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int,
+                      block_size: int) -> tuple:
+    return (num_blocks, num_kv_heads, head_dim, block_size)
+
+
+def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """(num_blocks, num_kv_heads, block_size, head_dim) from validated caches."""
+    _require(k_cache.dim() == 5 and v_cache.dim() == 4, "k_cache must be 5-D, v_cache 4-D")
+    NB, H, dx, bs, X = k_cache.shape
+    _require(X == key_chunk(k_cache.dtype), "k_cache last dim must be 16 bytes of elements")
+    d = dx * X
+    _require(tuple(v_cache.shape) == (NB, H, d, bs), "v_cache shape does not match k_cache")
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    return NB, H, bs, d
 
 
 def lib() -> ctypes.CDLL:
@@ -95,11 +123,8 @@ def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     """Scatter k/v [T][Hkv][d] (token dim may be strided) into the caches."""
     _require(k.dim() == 3 and v.dim() == 3 and k.shape == v.shape, "k, v must be [T][Hkv][d]")
     T, H, d = k.shape
-    _require(k_cache.dim() == 4 and v_cache.dim() == 4, "caches must be 4-D")
-    NB, H2, bs, d2 = k_cache.shape
-    _require((H2, d2) == (H, d) and tuple(v_cache.shape) == (NB, H, d, bs),
-             "cache shapes do not match k/v")
-    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    NB, H2, bs, d2 = _cache_dims(k_cache, v_cache)
+    _require((H2, d2) == (H, d), "cache shapes do not match k/v")
     for t in (k, v):
         _require(t.stride(2) == 1 and t.stride(1) == d, "heads of a token must be packed")
     _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,)
@@ -140,10 +165,8 @@ def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, 
     _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
     B, Hq, d = q.shape
     _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
-    NB, Hkv, bs, d2 = k_cache.shape
-    _require(bs == block_size and d2 == d, "k_cache shape does not match block_size / head_dim")
-    _require(tuple(v_cache.shape) == (NB, Hkv, d, bs), "v_cache shape does not match")
-    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    NB, Hkv, bs, d2 = _cache_dims(k_cache, v_cache)
+    _require(bs == block_size and d2 == d, "cache shapes do not match block_size / head_dim")
     _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
              and block_tables.shape[0] == B and block_tables.is_contiguous(),
              "block_tables must be contiguous int32 [B][max_blocks]")

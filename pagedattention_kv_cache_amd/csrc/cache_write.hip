@@ -6,9 +6,10 @@
 // arithmetic on values.
 //
 // Thread mapping: one thread moves one 16-byte chunk of one (token, kv head)
-// row.  Keys: the chunk lands contiguously in the token's key row, so the
-// head_dim*elem/16 threads of a row write one contiguous run (256 B for a
-// 128-wide bf16 head) -- full cache lines.  Values: the value cache is
+// row.  Keys: the key cache is [block][head][chunk][block_size][16 bytes], so
+// chunk c of the token at offset o lands at (c * block_size + o) * 16 bytes
+// into the (block, head) tile; tokens of consecutive offsets fill consecutive
+// 16-byte slots of one chunk row.  Values: the value cache is
 // [block][head][dim][block_size], so the chunk's elements go to consecutive
 // dims of one offset, block_size elements apart.
 #include "pa_device.hpp"
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int 
   const uint4 vraw = ld16(vsrc);
 
   const int64_t head_base = blk * a.num_kv_heads + h;
-  char* kdst = reinterpret_cast<char*>(a.k_cache) + ((head_base * a.block_size + off) * D + e0) * EB;
+  char* kdst = reinterpret_cast<char*>(a.k_cache) +
+               ((head_base * chunks_per_row + c) * a.block_size + off) * 16;
   *reinterpret_cast<uint4*>(kdst) = kraw;
 
   char* vrow = reinterpret_cast<char*>(a.v_cache) + ((head_base * D + e0) * a.block_size + off) * EB;

@@ -2,27 +2,29 @@
 // cores (v_mfma_f32_16x16x32_{bf16,f16}), for 16-bit KV caches.
 //
 // A grouped-query head group is a real dense tile: the g query heads that
-// share a kv head multiply the same keys and values, so per 32-token chunk
-//   S[token][head]   = K[token][:] . Q[head][:]        (2 tiles of 16 tokens)
+// share a kv head multiply the same keys and values, so per 16-token chunk
+//   S[token][head]   = K[token][:] . Q[head][:]
 //   O^T[dim][head]  += V^T[dim][token] . P^T[token][head]
 // are small GEMMs with N = g (up to 16) columns.  Keys and values are still
 // read from HBM once per kv head; the matrix cores take the multiply-adds off
 // the vector ALUs, which then only run the online softmax ("vLLM Project
 // Update" talk: PagedAttention over KV blocks; second kernel: sequences split
-// into partitions merged "similar to flash decoding").
+// into partitions merged the way flash decoding merges them).
 //
 // Lane layout (one wave = one (sequence, kv head, partition) work item):
 //   lane = 16*j + n, n in [0,16), j in [0,4).
-//   QK^T: A = keys, row n = token tau(n) of the tile, k-slots = 8 dims at
-//         32c + 8j; B = queries, column n = head n, same k-slots.
-//         Result: lane (n, j) holds head n's scores of 4 tokens.  Tile A
-//         rows are tokens 8*(i/4) + i%4, tile B rows the same + 4, so lane
-//         (n, j) ends up with head n's scores for tokens 8j .. 8j+7.
-//   P.V:  A = values from the [dim][block_size] value layout, row n = dim
-//         16c + n, k-slots = tokens 8j .. 8j+7 (one contiguous 16-byte run);
-//         B = probabilities, column n = head n, k-slots = the same tokens --
-//         exactly the registers the QK^T result left in the lane, so no
-//         shuffle is needed.  Result: lane (n, j) holds O^T[16c + 4j + r][n].
+//   Chunks of 16 tokens.
+//   QK^T (16x16x32): A = keys, row n = token n of the chunk, k-slots = the 8
+//         dims of key chunk 4c + j (the key cache keeps each 16-byte chunk of
+//         consecutive tokens contiguous, so the 16 lanes of a group read one
+//         256-byte run); B = queries, column n = head n, same k-slots.
+//         Result: lane (n, j) holds head n's scores of tokens 4j .. 4j+3.
+//   P.V (16x16x16): A = values from the [dim][block_size] value layout,
+//         row n = dim 16c + n, k-slots = tokens 4j .. 4j+3 (one contiguous
+//         8-byte run); B = probabilities, column n = head n, k-slots = the
+//         same tokens -- exactly the registers the QK^T result left in the
+//         lane, so no shuffle is needed.  Result: lane (n, j) holds
+//         O^T[16c + 4j + r][n].
 //   Every per-head quantity (running max, sum, rescale factor) therefore
 //   lives in the lanes of column n.
 //
@@ -31,8 +33,8 @@
 // bits; all accumulation is fp32.  p = 1 and p = 0 stay exact.
 //
 // Memory: the block ids of the current 64-block window are held one per lane
-// and fetched with a lane shuffle; the keys and values of chunk i+1 are
-// loaded while chunk i is computed (two register buffers).
+// and fetched with a lane read; the keys and values of chunk i+1 are loaded
+// while chunk i is computed (two register buffers).
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
 
@@ -73,6 +75,13 @@ template <> struct Mma<Elem::F16> {
 
 constexpr int kChunk = 16;  // tokens per iteration: one 16-row QK^T tile
 
+// Cache-policy bits of buffer loads: non-temporal.  Used for keys only: a
+// chunk's key loads consume whole cache lines (16 tokens x 16 bytes per key
+// chunk), while a value row of a block larger than 16 tokens is split across
+// consecutive chunks, and streaming hints on it were measured to cost a
+// re-fetch of the second half.
+constexpr int kNonTemporal = 2;
+
 // Raw buffer resource over [base, base + 2 GiB): 32-bit lane offsets, no
 // swizzle, dword data format (the gfx9 raw-buffer word 3).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
@@ -98,7 +107,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   using scalar = typename M::scalar;
   constexpr int KC = D / 32;  // QK^T k-chunks
   constexpr int VC = D / 16;  // P.V row chunks
-  constexpr int RB = D * 2;   // bytes per key row
 
   // grid.x walks (sequence, kv head, head chunk) fastest so that consecutive
   // workgroups -- which the dispatcher deals round-robin to the XCDs -- carry
@@ -156,8 +164,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 
   // per-lane byte offsets inside a (block, head) tile
-  const uint32_t koff = (uint32_t)(n * RB + 16 * j);       // key row n, dims 8j.. of each 32
+  const uint32_t koff = (uint32_t)((j * bs + n) * 16);     // key chunk j, token n
   const uint32_t voff = (uint32_t)((n * bs + 4 * j) * 2);  // value row n, tokens 4j..4j+3
+  const int kstep = 64 * bs;                               // bytes between key chunks 4 apart
 
   int wb = 0;       // first logical block of the current block-id window
   int bt_lane = 0;  // lane i: physical block of logical block wb + i
@@ -172,25 +181,27 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       const int phys = __builtin_amdgcn_readlane(bt_lane, min(t0 >> lbs, last_blk) - wb);
       const int64_t tile = (int64_t)phys * block_stride;
       const int in_blk = t0 & (bs - 1);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + tile + (int64_t)in_blk * RB);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + tile + (int64_t)in_blk * 16);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + tile + (int64_t)in_blk * 2);
 #pragma unroll
       for (int c = 0; c < KC; ++c)
         buf.k[c] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rk, (int)koff + 64 * c, 0, 0));
+                                                rk, (int)koff, c * kstep, kNonTemporal));
 #pragma unroll
       for (int c = 0; c < VC; ++c)
         buf.v[c] = __builtin_bit_cast(vec4, __builtin_amdgcn_raw_buffer_load_b64(
                                                 rv, (int)voff, c * (int)vrow16, 0));
     } else {
-      const int tk = t0 + n;      // this lane's key row
+      const int tk = t0 + n;      // this lane's key token
       const int tv = t0 + 4 * j;  // first token of this lane's value run
       const int pk = __shfl(bt_lane, min(tk >> lbs, last_blk) - wb);
       const int pv = __shfl(bt_lane, min(tv >> lbs, last_blk) - wb);
-      const char* kp = kc + (int64_t)pk * block_stride + (int64_t)(tk & (bs - 1)) * RB + 16 * j;
+      const char* kp =
+          kc + (int64_t)pk * block_stride + ((int64_t)j * bs + (tk & (bs - 1))) * 16;
       const char* vp = vc + (int64_t)pv * block_stride + ((int64_t)n * bs + (tv & (bs - 1))) * 2;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) buf.k[c] = *reinterpret_cast<const vec8*>(kp + 64 * c);
+      for (int c = 0; c < KC; ++c)
+        buf.k[c] = __builtin_bit_cast(vec8, ld16_nt(kp + (int64_t)c * kstep));
 #pragma unroll
       for (int c = 0; c < VC; ++c) buf.v[c] = *reinterpret_cast<const vec4*>(vp + c * vrow16);
     }

@@ -1,8 +1,8 @@
 // decode_reduce.hip -- log-sum-exp merge of a sequence's partition results.
 //
 // The second PagedAttention kernel of the "vLLM Project Update" talk splits
-// each sequence into pieces spread across the GPU and combines them "similar
-// to flash decoding"; the talk gives no formula.  With per-partition running
+// each sequence into pieces spread across the GPU and combines them the way
+// flash decoding does; the talk gives no formula.  With per-partition running
 // max m_p (log2 domain), sum l_p = sum_t 2^(s_t - m_p) and unnormalised
 // output a_p = sum_t 2^(s_t - m_p) v_t, the exact merge is
 //     M = max_p m_p,  w_p = 2^(m_p - M),

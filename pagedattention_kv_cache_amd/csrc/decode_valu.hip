@@ -7,13 +7,14 @@
 // talk, PagedAttention recap: attention over fixed-size blocks of the KV
 // cache); a partition covers partition_size tokens and long or uneven contexts
 // are split into several partitions merged later by log-sum-exp (same talk,
-// second PagedAttention kernel, "similar to flash decoding").
+// second PagedAttention kernel, which the talk likens to flash decoding).
 //
 // Per tile:
 //  * scores: a key row (head_dim * elem bytes) is spread over RL = row/16
 //    lanes holding one 16-byte chunk each, TPI = 64/RL tokens per load
-//    instruction; each lane forms partial dots for every head of the group
-//    and a DPP butterfly within the row completes them;
+//    instruction (with the chunked key layout, chunk c of TPI consecutive
+//    tokens is one contiguous run); each lane forms partial dots for every
+//    head of the group and a DPP butterfly within the row completes them;
 //  * online softmax in the exp2 domain (scale * log2 e folded into the
 //    scores): the tile max is made wave-uniform, so the running max m, the
 //    rescale factor and the accumulator rescale are uniform per head;
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
       const int tok0 = t0 + i * TPI;
       const int64_t phys = clamp_block(bt[min(tok0 >> lbs, last_blk)], a.num_blocks);
       const int off = (tok0 & (bs - 1)) + row;
-      kraw[i] = ld16(kc + (((phys * Hkv + h) * bs + off) * D + c * EPL) * EB);
+      kraw[i] = ld16(kc + (((phys * Hkv + h) * RL + c) * bs + off) * 16);
     }
     uint4 vraw[DPL][NSEG][VL];
 #pragma unroll

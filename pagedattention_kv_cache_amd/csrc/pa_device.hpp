@@ -74,6 +74,15 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal hint: cache data that is streamed once
+// (keys and values) without displacing reused lines.
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---- cross-lane reductions -----------------------------------------------
 // DPP row (16-lane) butterflies: after the four steps every lane of a row
 // holds the row's total.  Control codes are the GFX9 DPP encodings:

@@ -30,8 +30,9 @@ class GpuState:
         self.wl = wl
         c = wl.cfg
         self.device = device
-        shape_k = (wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
-        shape_v = (wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size)
+        shape_k = pa.key_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size,
+                                     DTYPE_TORCH[c.dtype])
+        shape_v = pa.value_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size)
         if poison:
             self.kc = _poison(shape_k, c.dtype, device)
             self.vc = _poison(shape_v, c.dtype, device)

@@ -101,12 +101,13 @@ def test_cache_write_strided_tokens_and_negative_slots():
     v = qkv[:, 2 * H * d:].view(T, H, d)
     slots = torch.randperm(NB * bs, generator=g)[:T].to(torch.int64)
     slots[::5] = -1
-    kc_o = np.full((NB, H, bs, d), 0x7FC0, np.uint16)
+    kc_o = np.full(pa.key_cache_shape(NB, H, d, bs, torch.bfloat16), 0x7FC0, np.uint16)
     vc_o = np.full((NB, H, d, bs), 0x7FC0, np.uint16)
     oracle.cache_write(raw_bits(k.contiguous()), raw_bits(v.contiguous()), slots.numpy(), kc_o,
                        vc_o, "bf16")
     # start from the same poisoned pools as the oracle
-    kc = torch.full((NB, H, bs, d), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    kc = torch.full(pa.key_cache_shape(NB, H, d, bs, torch.bfloat16), 0x7FC0, dtype=torch.int16,
+                    device="cuda").view(torch.bfloat16)
     vc = torch.full((NB, H, d, bs), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
     qkv_d = qkv.cuda()
     pa.cache_write(qkv_d[:, H * d:2 * H * d].view(T, H, d), qkv_d[:, 2 * H * d:].view(T, H, d),
@@ -229,7 +230,7 @@ def test_one_hot_probe_bit_exact(dtype, partition, kernel):
     for t in [0, 1, 15, 16, 17, 47, 63, 64, 95]:
         K = torch.zeros(L, H, d, dtype=dt)
         K[t, 0] = (qf[0, 0] * c).to(dt)
-        kc = torch.full((NB, H, bs, d), float("nan"), dtype=dt, device="cuda")
+        kc = torch.full(pa.key_cache_shape(NB, H, d, bs, dt), float("nan"), dtype=dt, device="cuda")
         vc = torch.full((NB, H, d, bs), float("nan"), dtype=dt, device="cuda")
         pa.cache_write(K.cuda(), V.cuda(), slots, kc, vc)
         out = torch.empty(1, 1, d, device="cuda")
