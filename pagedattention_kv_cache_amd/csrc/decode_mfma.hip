@@ -82,12 +82,6 @@ constexpr int kChunk = 16;  // tokens per iteration: one 16-row QK^T tile
 // re-fetch of the second half.
 constexpr int kNonTemporal = 2;
 
-// Raw buffer resource over [base, base + 2 GiB): 32-bit lane offsets, no
-// swizzle, dword data format (the gfx9 raw-buffer word 3).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
-                                           0x00020000);
-}
 
 template <Elem KV, int D>
 struct Buffers {
@@ -125,29 +119,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const int n = lane & 15;
   const int j = lane >> 4;
 
-  const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
-  const int P = a.partition_size;
-  if (L <= 0) {
-    if (part == 0) {
-      for (int g = 0; g < G; ++g)
-        for (int e = lane; e < D; e += 64)
-          store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
-    }
-    return;
-  }
-  const int n_parts = (L + P - 1) / P;
-  if (part >= n_parts) return;
-  const int t_begin = part * P;
-  const int t_end = min(t_begin + P, L);
+  // Start-up loads that do not depend on the context length go out together
+  // with it: the first block-id window (clamped to the table width; entries
+  // past the sequence are never used) and the queries.
   const int lbs = a.log2_block_size;
   const int bs = a.block_size;
-  const int last_blk = (L - 1) >> lbs;
+  const int P = a.partition_size;
+  const int t_begin = part * P;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const int64_t head_tile = (int64_t)bs * D * 2;  // bytes of one (block, head) tile
-  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
-  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
-  const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
-  const int64_t vrow16 = (int64_t)16 * bs * 2;  // bytes between value rows 16 dims apart
+  const int L_in = a.context_lens[b];
+  const int bt_first = bt[min((t_begin >> lbs) + lane, a.max_blocks_per_seq - 1)];
 
   // queries: column n = head hq0 + n (zero beyond the group)
   vec8 qv[KC];
@@ -163,26 +144,48 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
+  const int L = clamp_len(L_in, a.max_blocks_per_seq, a.block_size);
+  if (L <= 0) {
+    if (part == 0) {
+      for (int g = 0; g < G; ++g)
+        for (int e = lane; e < D; e += 64)
+          store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
+    }
+    return;
+  }
+  const int n_parts = (L + P - 1) / P;
+  if (part >= n_parts) return;
+  const int t_end = min(t_begin + P, L);
+  const int last_blk = (L - 1) >> lbs;
+  const int64_t head_tile = (int64_t)bs * D * 2;  // bytes of one (block, head) tile
+  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
+  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
+  const int64_t vrow16 = (int64_t)16 * bs * 2;  // bytes between value rows 16 dims apart
+
   // per-lane byte offsets inside a (block, head) tile
   const uint32_t koff = (uint32_t)((j * bs + n) * 16);     // key chunk j, token n
   const uint32_t voff = (uint32_t)((n * bs + 4 * j) * 2);  // value row n, tokens 4j..4j+3
   const int kstep = 64 * bs;                               // bytes between key chunks 4 apart
 
-  int wb = 0;       // first logical block of the current block-id window
-  int bt_lane = 0;  // lane i: physical block of logical block wb + i
+  int wb = t_begin >> lbs;  // first logical block of the current block-id window
+  int bt_lane = (int)clamp_block(bt_first, a.num_blocks);  // lane i: block of wb + i
 
-  // Loads of one 16-token chunk.  Issued unconditionally (a chunk past the
-  // end re-reads the last one), so every path through the loop has the same
-  // loads in flight and the compiler's wait counts stay exact.
-  auto issue = [&](Buffers<KV, D>& buf, int t0) {
+  // Loads of one 16-token chunk.  Issued unconditionally, so every path
+  // through the loop has the same loads in flight and the compiler's wait
+  // counts stay exact; the prefetch past the last chunk (`none`) reads
+  // through an empty buffer range, which returns zeros without touching
+  // memory (or re-reads the last chunk where plain global loads are used).
+  auto issue = [&](Buffers<KV, D>& buf, int t0, bool none) {
     if constexpr (UB) {
       // one block: a buffer resource based at the chunk's key / value tile,
       // per-lane 32-bit offsets, the 16-dim row stride as the scalar offset
       const int phys = __builtin_amdgcn_readlane(bt_lane, min(t0 >> lbs, last_blk) - wb);
       const int64_t tile = (int64_t)phys * block_stride;
       const int in_blk = t0 & (bs - 1);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + tile + (int64_t)in_blk * 16);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + tile + (int64_t)in_blk * 2);
+      const int range = none ? 0 : 0x7fffffff;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + tile + (int64_t)in_blk * 16, range);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + tile + (int64_t)in_blk * 2, range);
 #pragma unroll
       for (int c = 0; c < KC; ++c)
         buf.k[c] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -266,17 +269,19 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const int window = 64 * bs;
   for (int w0 = t_begin; w0 < t_end; w0 += window) {
     const int w1 = min(w0 + window, t_end);
-    wb = w0 >> lbs;
-    bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
+    if (w0 != t_begin) {  // later windows (one-pass over long contexts)
+      wb = w0 >> lbs;
+      bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
+    }
     const int nc = (w1 - w0 + kChunk - 1) / kChunk;
     const int last_t0 = w0 + (nc - 1) * kChunk;
-    issue(b0, w0);
+    issue(b0, w0, false);
     for (int i = 0; i < nc; i += 2) {
       const int t0 = w0 + i * kChunk;
-      issue(b1, min(t0 + kChunk, last_t0));
+      issue(b1, min(t0 + kChunk, last_t0), t0 + kChunk > last_t0);
       compute(b0, t0, w1);
       if (i + 1 >= nc) break;
-      issue(b0, min(t0 + 2 * kChunk, last_t0));
+      issue(b0, min(t0 + 2 * kChunk, last_t0), t0 + 2 * kChunk > last_t0);
       compute(b1, t0 + kChunk, w1);
     }
   }

@@ -20,8 +20,12 @@
 //    rescale factor and the accumulator rescale are uniform per head;
 //  * the tile's probabilities go through LDS (broadcast reads) and each lane
 //    accumulates p * v for head_dim/64 output dims from the value cache's
-//    [dim][block_size] rows: 16 consecutive tokens of one dim are one
+//    [dim][block_size] rows: 8 consecutive tokens of one dim are one
 //    contiguous run.
+// Memory: the block ids of a 64-block window sit one per lane and are read
+// with readlane; each 8-token segment of a tile gets a buffer resource at its
+// block, so lanes only add fixed 32-bit offsets; tile i+1 is loaded while
+// tile i is computed.
 // Masking is by selection (score -inf, value term skipped), never by
 // multiplying by zero, so unused cache slots may hold anything (even NaN).
 #include "pa_device.hpp"
@@ -32,17 +36,29 @@ namespace {
 
 constexpr int kTile = 16;
 
+template <Elem KV, int D>
+struct Tile {
+  static constexpr int EB = ElemTraits<KV>::bytes;
+  static constexpr int RL = D * EB / 16;         // lanes per key row
+  static constexpr int NI = kTile / (64 / RL);   // key load instructions per tile
+  static constexpr int DPL = D / 64;             // value dims per lane
+  static constexpr int VL = 8 * EB / 16;         // 16-byte loads per 8-token segment and dim
+  uint4 k[NI];
+  uint4 v[2][DPL][VL];
+};
+
 template <Elem KV, int D, int G>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
-  constexpr int EB = ElemTraits<KV>::bytes;
+  using T = Tile<KV, D>;
+  constexpr int EB = T::EB;
   constexpr int EPL = 16 / EB;     // elements per 16-byte chunk
-  constexpr int RL = D * EB / 16;  // lanes per key row
+  constexpr int RL = T::RL;        // lanes per key row
   constexpr int TPI = 64 / RL;     // tokens per key load instruction
-  constexpr int NI = kTile / TPI;  // key load instructions per tile
-  constexpr int DPL = D / 64;      // value dims per lane
-  constexpr int SEG = 8;           // tokens per value load segment
+  constexpr int NI = T::NI;
+  constexpr int DPL = T::DPL;
+  constexpr int SEG = 8;           // tokens per value load segment (one block)
   constexpr int NSEG = kTile / SEG;
-  constexpr int VL = SEG * EB / 16;  // 16-byte loads per segment and dim
+  constexpr int VL = T::VL;
   static_assert(RL >= 8 && RL <= 64 && 64 % RL == 0, "row layout");
   static_assert(TPI <= SEG, "a key load instruction stays inside one block");
 
@@ -63,8 +79,25 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   const int c = lane % RL;    // 16-byte chunk of the key row
   const int row = lane / RL;  // token within a key load instruction
 
-  const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
+  // start-up loads that do not depend on the context length go out with it
+  const int lbs = a.log2_block_size;
+  const int bs = a.block_size;
   const int P = a.partition_size;
+  const int t_begin = part * P;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+  const int L_in = a.context_lens[b];
+  const int bt_first = bt[min((t_begin >> lbs) + lane, a.max_blocks_per_seq - 1)];
+
+  // query chunk for every head of the group, widened to fp32
+  float qf[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t qb = ((int64_t)b * a.num_q_heads + hq0 + g) * D + c * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[g][e] = load_elem_f32(a.q, qb + e, a.q_dtype);
+  }
+
+  const int L = clamp_len(L_in, a.max_blocks_per_seq, a.block_size);
   if (L <= 0) {
     if (part == 0) {
       for (int g = 0; g < G; ++g)
@@ -75,22 +108,50 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   }
   const int n_parts = (L + P - 1) / P;
   if (part >= n_parts) return;
-  const int t_begin = part * P;
   const int t_end = min(t_begin + P, L);
-  const int lbs = a.log2_block_size;
-  const int bs = a.block_size;
   const int last_blk = (L - 1) >> lbs;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const int64_t Hkv = a.num_kv_heads;
+  const int64_t head_tile = (int64_t)bs * D * EB;  // bytes of one (block, head) tile
+  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
+  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
 
-  // query chunk for every head of the group, widened to fp32
-  float qf[G][EPL];
+  // per-lane byte offsets inside a (block, head) tile, relative to the segment
+  const int koff = (c * bs + row) * 16;  // key chunk c of token `row`
+  int voff[DPL];                         // value row of each owned dim
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int64_t qb = ((int64_t)b * a.num_q_heads + hq0 + g) * D + c * EPL;
+  for (int dd = 0; dd < DPL; ++dd) voff[dd] = (lane * DPL + dd) * bs * EB;
+
+  int wb = t_begin >> lbs;  // block-id window: lane i holds the block of wb + i
+  int bt_lane = (int)clamp_block(bt_first, a.num_blocks);
+
+  // Loads of one 16-token tile (two 8-token segments, each inside one block),
+  // through buffer resources based at each segment.  Always issued; the
+  // prefetch past the last tile reads through an empty range (zeros, no
+  // memory access), so the wait counts are the same on every path.
+  auto issue = [&](T& buf, int t0, bool none) {
+    const int range = none ? 0 : 0x7fffffff;
+    __amdgpu_buffer_rsrc_t rk[NSEG], rv[NSEG];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[g][e] = load_elem_f32(a.q, qb + e, a.q_dtype);
-  }
+    for (int sgm = 0; sgm < NSEG; ++sgm) {
+      const int tok = t0 + sgm * SEG;
+      const int phys = __builtin_amdgcn_readlane(bt_lane, min(tok >> lbs, last_blk) - wb);
+      const int64_t tile = (int64_t)phys * block_stride;
+      const int in_blk = tok & (bs - 1);
+      rk[sgm] = make_rsrc(kc + tile + (int64_t)in_blk * 16, range);
+      rv[sgm] = make_rsrc(vc + tile + (int64_t)in_blk * EB, range);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int sgm = (i * TPI) / SEG;
+      buf.k[i] = buf_ld16(rk[sgm], koff, ((i * TPI) % SEG) * 16);
+    }
+#pragma unroll
+    for (int sgm = 0; sgm < NSEG; ++sgm)
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd)
+#pragma unroll
+        for (int jj = 0; jj < VL; ++jj) buf.v[sgm][dd][jj] = buf_ld16(rv[sgm], voff[dd], 16 * jj);
+  };
 
   __shared__ float p_lds[G][kTile];
 
@@ -103,41 +164,14 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     for (int dd = 0; dd < DPL; ++dd) acc[g][dd] = 0.0f;
   }
 
-  const char* kc = reinterpret_cast<const char*>(a.k_cache);
-  const char* vc = reinterpret_cast<const char*>(a.v_cache);
-
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    // ---- issue the tile's key and value loads --------------------------
-    uint4 kraw[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int tok0 = t0 + i * TPI;
-      const int64_t phys = clamp_block(bt[min(tok0 >> lbs, last_blk)], a.num_blocks);
-      const int off = (tok0 & (bs - 1)) + row;
-      kraw[i] = ld16(kc + (((phys * Hkv + h) * RL + c) * bs + off) * 16);
-    }
-    uint4 vraw[DPL][NSEG][VL];
-#pragma unroll
-    for (int sgm = 0; sgm < NSEG; ++sgm) {
-      const int tok0 = t0 + sgm * SEG;
-      const int64_t phys = clamp_block(bt[min(tok0 >> lbs, last_blk)], a.num_blocks);
-      const int off = tok0 & (bs - 1);
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) {
-        const int e = lane * DPL + dd;
-        const char* p = vc + (((phys * Hkv + h) * D + e) * bs + off) * EB;
-#pragma unroll
-        for (int j = 0; j < VL; ++j) vraw[dd][sgm][j] = ld16(p + 16 * j);
-      }
-    }
-
+  auto compute = [&](T& buf, int t0, int t_stop) {
     // ---- scores ----------------------------------------------------------
     float s[G][NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float kf[EPL];
-      widen16<KV>(kraw[i], kf);
-      const bool valid = (t0 + i * TPI + row) < t_end;
+      widen16<KV>(buf.k[i], kf);
+      const bool valid = (t0 + i * TPI + row) < t_stop;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float part_dot = 0.0f;
@@ -168,6 +202,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
       for (int dd = 0; dd < DPL; ++dd) acc[g][dd] *= alpha;
     }
+    __syncthreads();  // the previous tile's probabilities have been read
     if (c == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -177,25 +212,47 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     __syncthreads();
 
     // ---- p . V -------------------------------------------------------------
-    const int nv = min(kTile, t_end - t0);  // valid tokens in this tile
+    const int nv = min(kTile, t_stop - t0);  // valid tokens in this tile
 #pragma unroll
     for (int sgm = 0; sgm < NSEG; ++sgm) {
 #pragma unroll
       for (int dd = 0; dd < DPL; ++dd) {
         float vf[SEG];
 #pragma unroll
-        for (int j = 0; j < VL; ++j) widen16<KV>(vraw[dd][sgm][j], vf + j * (16 / EB));
+        for (int jj = 0; jj < VL; ++jj) widen16<KV>(buf.v[sgm][dd][jj], vf + jj * EPL);
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) {
-          const int t = sgm * SEG + j;
+        for (int r = 0; r < SEG; ++r) {
+          const int t = sgm * SEG + r;
           if (t < nv) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(p_lds[g][t], vf[j], acc[g][dd]);
+            for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(p_lds[g][t], vf[r], acc[g][dd]);
           }
         }
       }
     }
-    __syncthreads();
+  };
+
+  // Walk the partition in windows of 64 blocks; inside a window, tile i+1 is
+  // loaded while tile i is computed.
+  T b0, b1;
+  const int window = 64 * bs;
+  for (int w0 = t_begin; w0 < t_end; w0 += window) {
+    const int w1 = min(w0 + window, t_end);
+    if (w0 != t_begin) {
+      wb = w0 >> lbs;
+      bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
+    }
+    const int nt = (w1 - w0 + kTile - 1) / kTile;
+    const int last_t0 = w0 + (nt - 1) * kTile;
+    issue(b0, w0, false);
+    for (int i = 0; i < nt; i += 2) {
+      const int t0 = w0 + i * kTile;
+      issue(b1, min(t0 + kTile, last_t0), t0 + kTile > last_t0);
+      compute(b0, t0, w1);
+      if (i + 1 >= nt) break;
+      issue(b0, min(t0 + 2 * kTile, last_t0), t0 + 2 * kTile > last_t0);
+      compute(b1, t0 + kTile, w1);
+    }
   }
 
   // ---- finish the work item ------------------------------------------------

@@ -83,6 +83,17 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Raw buffer resource over [base, base + range) bytes: 32-bit lane offsets,
+// no swizzle, dword data format (the gfx9 raw-buffer word 3).  Loads past the
+// range return zero without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int range) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, range, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // ---- cross-lane reductions -----------------------------------------------
 // DPP row (16-lane) butterflies: after the four steps every lane of a row
 // holds the row's total.  Control codes are the GFX9 DPP encodings:
