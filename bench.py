@@ -66,6 +66,9 @@ def parse_args(argv=None):
                     help="KV-cache copies the steps rotate over, so no step re-reads what the "
                          "previous one left in the 256 MB Infinity Cache")
     ap.add_argument("--no-stream-probe", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="multi-step workloads: also time the steps captured in HIP graphs, "
+                         "state advanced on the device by pa_advance_step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -176,6 +179,61 @@ def cpu_baseline(wl, okc, ovc, threads):
         "tokens_per_s": c.num_seqs / t,
         "cpu_model": _cpu_model(),
     }
+
+
+def graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags) -> dict:
+    """The workload's consecutive decode steps (write -> partitions -> merge ->
+    device advance step) captured once per KV-cache layer in a HIP graph;
+    each timed replay restores the initial per-sequence state first (four
+    small device copies, as a scheduler would upload it) and runs all steps."""
+    import torch
+
+    import pagedattention_kv_cache_amd as pa
+    c = wl.cfg
+    dev = out.device
+    init = {k: torch.from_numpy(v.copy()).to(dev) for k, v in wl.initial_state().items()}
+    state = {k: v.clone() for k, v in init.items()}
+    sampled = torch.from_numpy(wl.sampled_tokens()).to(dev)
+    scale = c.attn_scale()
+
+    def steps(k_l, v_l):
+        for s in range(c.steps):
+            pa.cache_write(sk[s], sv[s], state["slot_mapping"], k_l, v_l)
+            pa.decode_partitions(out, qs[s], k_l, v_l, bt, state["seq_lens"], scale, c.block_size,
+                                 part, ws, flags)
+            pa.decode_merge(out, qs[s], k_l, v_l, bt, state["seq_lens"], scale, c.block_size,
+                            part, ws, flags)
+            pa.advance_step(c.num_seqs, c.block_size, state["input_tokens"], sampled[s],
+                            state["input_positions"], state["seq_lens"], state["slot_mapping"], bt)
+
+    def reset():
+        for k in state:
+            state[k].copy_(init[k])
+
+    graphs = []
+    for k_l, v_l in zip(kcs, vcs):
+        reset()
+        steps(k_l, v_l)  # eager pass before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            steps(k_l, v_l)
+        graphs.append(g)
+    for g in graphs:
+        reset()
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // c.steps) * len(graphs)
+    t0 = time.perf_counter()
+    for i in range(reps):
+        reset()
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / (reps * c.steps)
+    kv = statistics.mean(wl.kv_bytes(s) for s in range(c.steps))
+    return {"steps_per_graph": c.steps, "replays": reps, "ms_per_step": round(ms_step, 5),
+            "value": round(kv / (ms_step * 1e-3) / 1e9, 2),
+            "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1)}
 
 
 def stream_probe(dev, gib: int = 4, reps: int = 10) -> float:
@@ -330,6 +388,9 @@ def run(args):
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = kv / (dec_ms * 1e-3) / 1e9
 
+    graph = None
+    if args.graph and c.steps > 1:
+        graph = graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags)
     attainable = None if args.no_stream_probe else stream_probe(dev)
     traffic = None
     tf = TRAFFIC_FILE.format(workload=c.name)
@@ -374,6 +435,8 @@ def run(args):
         "fill_seconds": round(t_fill, 2),
         "kv_cache_layers": n_layers,
     }
+    if graph:
+        result["graph"] = graph
     if attainable:
         result["attainable_read_gbps"] = round(attainable, 1)
         result["roofline"]["frac_of_attainable"] = round(achieved / attainable, 4)

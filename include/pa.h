@@ -102,6 +102,32 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
                    int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream);
 
 /*
+ * pa_advance_step -- advance each sequence's decode state by one step on the
+ * device, in place ("[core] Multi Step Scheduling" pull request, review
+ * thread on ops.advance_step: between steps of a multi-step run the GPU
+ * updates next input tokens, positions, sequence lengths and slots from the
+ * sampled ids, block tables and block size).  For i < num_queries:
+ *     input_tokens[i]    = sampled_token_ids[i]
+ *     input_positions[i] = input_positions[i] + 1            (call it p)
+ *     seq_lens[i]        = p + 1
+ *     slot_mapping[i]    = block_tables[i][p / block_size] * block_size
+ *                          + p % block_size
+ *                          (-1 when p / block_size >= max_blocks_per_seq or the
+ *                          table entry is negative: the block was not allocated
+ *                          ahead, and pa_cache_write skips the token)
+ * and for num_queries <= i < num_seqs (padding rows) slot_mapping[i] = -1,
+ * everything else untouched.  All pointers are device pointers:
+ * input_tokens, input_positions, slot_mapping int64 [num_seqs];
+ * sampled_token_ids int64 [num_queries]; seq_lens int32 [num_seqs];
+ * block_tables int32 [num_seqs][max_blocks_per_seq] (read only).
+ * Callers allocate the blocks of the coming steps before launching them.
+ */
+int pa_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
+                    int64_t* input_tokens, const int64_t* sampled_token_ids,
+                    int64_t* input_positions, int32_t* seq_lens, int64_t* slot_mapping,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, void* stream);
+
+/*
  * pa_decode -- out[b][hq][:] = sum_t softmax_t(scale * q[b][hq] . K_t) V_t
  * over the logical positions t in [0, context_lens[b]) of sequence b, where
  * position t is found in physical block block_tables[b][t / block_size] at

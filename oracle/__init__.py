@@ -66,6 +66,9 @@ def lib():
         L.orc_decode.argtypes = [c_void_p, c_void_p, i32, c_void_p, c_void_p, i32, c_void_p,
                                  c_void_p, i32, i32, i32, i32, i64, i32, i32, ctypes.c_float,
                                  c_void_p, i64, i32]
+        L.orc_advance_step.restype = ctypes.c_int
+        L.orc_advance_step.argtypes = [i32, i32, i32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, i32]
         L.orc_decode_bits.restype = None
         L.orc_decode_bits.argtypes = [c_void_p, i32, i64, c_void_p]
         _lib = L
@@ -145,3 +148,22 @@ def decode(q: np.ndarray, q_dtype: str, k_cache: np.ndarray, v_cache: np.ndarray
                             d, NB, bs, MB, float(scale), None if r is None else _ptr(r),
                             0 if r is None else r.size, int(threads)))
     return out
+
+
+def advance_step(num_queries: int, block_size: int, input_tokens: np.ndarray,
+                 sampled_token_ids: np.ndarray, input_positions: np.ndarray,
+                 seq_lens: np.ndarray, slot_mapping: np.ndarray,
+                 block_tables: np.ndarray) -> None:
+    """In-place advance of host state arrays (int64 tokens/positions/slots,
+    int32 lengths, int32 [B][MB] tables)."""
+    arrs = [(input_tokens, np.int64), (input_positions, np.int64), (seq_lens, np.int32),
+            (slot_mapping, np.int64)]
+    for a, dt in arrs:
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise OracleError("state arrays must be contiguous int64 (int32 for seq_lens)")
+    B = input_tokens.shape[0]
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sampled = np.ascontiguousarray(sampled_token_ids, dtype=np.int64)
+    _check(lib().orc_advance_step(B, num_queries, block_size, _ptr(input_tokens), _ptr(sampled),
+                                  _ptr(input_positions), _ptr(seq_lens), _ptr(slot_mapping),
+                                  _ptr(bt), bt.shape[1]))

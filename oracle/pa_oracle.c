@@ -39,7 +39,9 @@
  * half/bfloat16 decoders against numpy/torch over all 65536 patterns, a
  * hand-worked cache-write layout fixture, block-permutation and block-size
  * invariance, L=1 -> V, identical keys -> mean(V), one-hot probe -> V[t*],
- * scale 0 -> mean(V), GQA == replicated MHA.  No function here is unpinned.
+ * scale 0 -> mean(V), GQA == replicated MHA; the advance step against a
+ * hand-worked table and against the seeded generator's own slot arithmetic.
+ * No function here is unpinned.
  */
 #include <math.h>
 #include <pthread.h>
@@ -353,6 +355,43 @@ int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
   for (int i = 0; i < started; ++i) pthread_join(tids[i], NULL);
   for (int i = 0; i < n_threads; ++i)
     if (jobs[i].status != ORC_OK) return jobs[i].status;
+  return ORC_OK;
+}
+
+/* ---- advance step ------------------------------------------------------- */
+
+/*
+ * One decode step forward for every live sequence ("[core] Multi Step
+ * Scheduling" pull request, review thread on ops.advance_step): the sampled
+ * id becomes the next input token, the position moves one forward, the
+ * sequence length becomes position + 1, and the slot is the position's offset
+ * inside the block the table names (-1 when the table has no block there).
+ * Rows num_queries..num_seqs-1 are padding: their slot becomes -1.
+ */
+int orc_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
+                     int64_t* input_tokens, const int64_t* sampled_token_ids,
+                     int64_t* input_positions, int32_t* seq_lens, int64_t* slot_mapping,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq) {
+  if (num_seqs < 0 || num_queries < 0 || num_queries > num_seqs || block_size <= 0 ||
+      max_blocks_per_seq <= 0)
+    return ORC_ERR_ARG;
+  for (int64_t i = 0; i < num_seqs; ++i) {
+    if (i >= num_queries) {
+      slot_mapping[i] = -1;
+      continue;
+    }
+    input_tokens[i] = sampled_token_ids[i];
+    int64_t position = input_positions[i] + 1;
+    input_positions[i] = position;
+    seq_lens[i] = (int32_t)(position + 1);
+    int64_t logical_block = position / block_size;
+    int64_t slot = -1;
+    if (logical_block < max_blocks_per_seq) {
+      int64_t physical = block_tables[i * max_blocks_per_seq + logical_block];
+      if (physical >= 0) slot = physical * block_size + position % block_size;
+    }
+    slot_mapping[i] = slot;
+  }
   return ORC_OK;
 }
 

@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, u32]
         L.pa_decode_workspace_size.restype = sz
         L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, u32]
+        L.pa_advance_step.restype = ctypes.c_int
+        L.pa_advance_step.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]
         L.pa_decode_kernel.restype = i32
         L.pa_decode_kernel.argtypes = [i32, i32, i32, i32, u32]
         L.pa_status_string.restype = ctypes.c_char_p
@@ -133,6 +135,28 @@ def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     _check(lib().pa_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
                                 k_cache.data_ptr(), v_cache.data_ptr(), T, k.stride(0),
                                 v.stride(0), H, d, NB, bs, _dt(k), _stream(k_cache.device)))
+
+
+def advance_step(num_queries: int, block_size: int, input_tokens: torch.Tensor,
+                 sampled_token_ids: torch.Tensor, input_positions: torch.Tensor,
+                 seq_lens: torch.Tensor, slot_mapping: torch.Tensor,
+                 block_tables: torch.Tensor) -> None:
+    """Advance every sequence's decode state one step on the device (in place)."""
+    B = input_tokens.shape[0]
+    for t, dt in ((input_tokens, torch.int64), (input_positions, torch.int64),
+                  (slot_mapping, torch.int64), (seq_lens, torch.int32)):
+        _require(t.dtype == dt and t.shape == (B,) and t.is_contiguous(),
+                 "state tensors: int64/int32 [num_seqs], contiguous")
+    _require(sampled_token_ids.dtype == torch.int64 and sampled_token_ids.is_contiguous()
+             and sampled_token_ids.numel() >= num_queries, "sampled_token_ids: int64 [num_queries]")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(),
+             "block_tables must be contiguous int32 [num_seqs][max_blocks]")
+    _check(lib().pa_advance_step(B, num_queries, block_size, input_tokens.data_ptr(),
+                                 sampled_token_ids.data_ptr(), input_positions.data_ptr(),
+                                 seq_lens.data_ptr(), slot_mapping.data_ptr(),
+                                 block_tables.data_ptr(), block_tables.shape[1],
+                                 _stream(input_tokens.device)))
 
 
 def decode_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

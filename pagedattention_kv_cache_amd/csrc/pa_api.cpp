@@ -160,6 +160,31 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
   return pa::launch_cache_write(a, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int pa_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
+                    int64_t* input_tokens, const int64_t* sampled_token_ids,
+                    int64_t* input_positions, int32_t* seq_lens, int64_t* slot_mapping,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, void* stream) {
+  if (num_seqs < 0 || num_queries < 0 || num_queries > num_seqs || max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (block_size <= 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!input_tokens || !input_positions || !seq_lens || !slot_mapping || !block_tables ||
+      (num_queries > 0 && !sampled_token_ids))
+    return PA_ERR_NULL;
+  pa::AdvanceArgs a;
+  a.input_tokens = input_tokens;
+  a.sampled_token_ids = sampled_token_ids;
+  a.input_positions = input_positions;
+  a.seq_lens = seq_lens;
+  a.slot_mapping = slot_mapping;
+  a.block_tables = block_tables;
+  a.num_seqs = num_seqs;
+  a.num_queries = num_queries;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  return pa::launch_advance_step(a, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size,
                                  int32_t max_blocks_per_seq, int32_t kv_dtype, uint32_t flags) {

@@ -65,4 +65,20 @@ bool mfma_supports_heads(int heads_per_item);
 // more than one.
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t s);
 
+struct AdvanceArgs {
+  int64_t* input_tokens;
+  const int64_t* sampled_token_ids;
+  int64_t* input_positions;
+  int32_t* seq_lens;
+  int64_t* slot_mapping;
+  const int32_t* block_tables;
+  int32_t num_seqs;
+  int32_t num_queries;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+};
+
+// One thread per sequence: next token, position, length and slot.
+hipError_t launch_advance_step(const AdvanceArgs& a, hipStream_t s);
+
 }  // namespace pa

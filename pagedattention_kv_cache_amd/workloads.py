@@ -34,7 +34,8 @@ DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 POISON_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
 
 # stream indices under SeedSequence(seed).spawn(...)
-_S_LENGTHS, _S_POOL, _S_Q, _S_STEP, _S_SEQ = range(5)
+_S_LENGTHS, _S_POOL, _S_Q, _S_STEP, _S_SEQ, _S_SAMPLED = range(6)
+VOCAB = 128256  # token ids drawn for the "sampled" next tokens (a Llama-3-sized vocabulary)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -137,7 +138,7 @@ class Workload:
     def __init__(self, cfg: DecodeConfig):
         self.cfg = cfg
         root = np.random.SeedSequence(cfg.seed)
-        self._ss = root.spawn(5)
+        self._ss = root.spawn(6)
         n = cfg.num_seqs
         self._seq_ss = self._ss[_S_SEQ].spawn(n)
         rng_len = np.random.Generator(np.random.PCG64(self._ss[_S_LENGTHS]))
@@ -222,6 +223,23 @@ class Workload:
         if c.k_scale != 1.0:
             k *= np.float32(c.k_scale)
         return round_to(k, c.dtype), round_to(v, c.dtype)
+
+    def sampled_tokens(self) -> np.ndarray:
+        """Token ids standing in for the sampler's output after each step:
+        int64 [steps][B], uniform over the vocabulary."""
+        c = self.cfg
+        rng = np.random.Generator(np.random.PCG64(self._ss[_S_SAMPLED]))
+        return rng.integers(0, VOCAB, size=(c.steps, c.num_seqs), dtype=np.int64)
+
+    def initial_state(self) -> dict:
+        """Per-sequence decode state before the first step: the input position
+        of the first new token, the context length it is attended with and its
+        slot."""
+        pos = (self.lens0 - 1).astype(np.int64)
+        return {"input_tokens": np.zeros(self.cfg.num_seqs, np.int64),
+                "input_positions": pos,
+                "seq_lens": self.lens0.astype(np.int32),
+                "slot_mapping": self.step_slots(0)}
 
     def describe(self) -> dict:
         L = self.context_lens(self.cfg.steps - 1).astype(np.int64)

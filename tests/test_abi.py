@@ -39,7 +39,7 @@ def test_library_loads_and_exports_header_symbols():
     names = _declared_functions()
     assert {"pa_cache_write", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
             "pa_decode_workspace_size", "pa_decode_partition_size", "pa_decode_kernel",
-            "pa_status_string", "pa_abi_version"} <= set(names)
+            "pa_advance_step", "pa_status_string", "pa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"libpa.so does not export {n}"
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
@@ -182,3 +182,29 @@ def test_partition_policy_and_workspace_size():
     # forced partition sizes must be multiples of the block size; invalid -> 0
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 24, BF16, 0) == 0
     assert L.pa_decode_partition_size(4, 3, 2, 128, 16, 8, BF16, 0) == ESHAPE
+
+
+def _adv(**kw):
+    a = dict(B=8, nq=6, bs=16, tok=FAKE, samp=FAKE, pos=FAKE, lens=FAKE, slots=FAKE, bt=FAKE, MB=4)
+    a.update(kw)
+    return pa.lib().pa_advance_step(a["B"], a["nq"], a["bs"], a["tok"], a["samp"], a["pos"],
+                                    a["lens"], a["slots"], a["bt"], a["MB"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ESHAPE),
+    (dict(nq=-1), ESHAPE),
+    (dict(nq=9), ESHAPE),
+    (dict(MB=0), ESHAPE),
+    (dict(bs=0), ESHAPE),
+    (dict(tok=None), ENULL),
+    (dict(samp=None), ENULL),
+    (dict(slots=None), ENULL),
+    (dict(bt=None), ENULL),
+])
+def test_advance_step_validation(kw, status):
+    assert _adv(**kw) == status
+
+
+def test_advance_step_empty_is_noop():
+    assert _adv(B=0, nq=0, tok=None, samp=None, pos=None, lens=None, slots=None, bt=None) == OK

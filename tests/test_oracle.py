@@ -415,3 +415,40 @@ def test_config1_end_to_end_against_brute_force():
     # poisoned tail slots of the last blocks and unused blocks never leak
     assert np.isfinite(got).all()
     assert math.isclose(wl.cfg.attn_scale(), 0.125)
+
+
+# ---------------------------------------------------------------- advance step
+
+def test_advance_step_hand_worked():
+    """block_size 16; tables: seq0 -> [7, 3], seq1 -> [5, -1], seq2 (padding)."""
+    bt = np.array([[7, 3], [5, -1], [9, 9]], np.int32)
+    tokens = np.array([11, 12, 13], np.int64)
+    pos = np.array([14, 15, 2], np.int64)
+    lens = np.array([15, 16, 3], np.int32)
+    slots = np.array([0, 0, 0], np.int64)
+    oracle.advance_step(2, 16, tokens, np.array([101, 102], np.int64), pos, lens, slots, bt)
+    # seq0: position 15 -> block 7, offset 15 -> slot 127; seq1: position 16 ->
+    # logical block 1 -> entry -1 -> slot -1; seq2 is padding
+    assert tokens.tolist() == [101, 102, 13]
+    assert pos.tolist() == [15, 16, 2]
+    assert lens.tolist() == [16, 17, 3]
+    assert slots.tolist() == [127, -1, -1]
+    oracle.advance_step(2, 16, tokens, np.array([7, 8], np.int64), pos, lens, slots, bt)
+    # seq0: position 16 -> logical block 1 -> block 3, offset 0 -> slot 48
+    assert slots.tolist() == [48, -1, -1] and pos.tolist() == [16, 17, 2]
+
+
+def test_advance_step_matches_generator_slots():
+    """Stepping the oracle's state reproduces the generator's per-step slots and
+    context lengths (two independent derivations of the same positions)."""
+    wl = Workload(custom_config("adv", [1, 15, 16, 17, 31, 32, 200], 4, 2, 8, "bf16", 16,
+                                seed=3, steps=8))
+    st = wl.initial_state()
+    sampled = wl.sampled_tokens()
+    assert sampled.shape == (8, 7) and sampled.min() >= 0
+    for s in range(8):
+        assert np.array_equal(st["slot_mapping"], wl.step_slots(s))
+        assert np.array_equal(st["seq_lens"], wl.context_lens(s))
+        oracle.advance_step(7, 16, st["input_tokens"], sampled[s], st["input_positions"],
+                            st["seq_lens"], st["slot_mapping"], wl.block_tables)
+        assert np.array_equal(st["input_tokens"], sampled[s])
