@@ -75,20 +75,22 @@ int check_shape(const DecodeShape& s) {
   return PA_OK;
 }
 
-// Partition policy for partition_size == 0.  Each partition adds
-// (head_dim*4 + 8) bytes of fp32 partial results per q head, written once and
-// read once by the merge; its key/value bytes per kv head are
-// 2 * partition * head_dim * elem.  Partitions of 256 tokens per two q heads
-// of the group keep the merge traffic near 1-3% of the KV stream while
-// leaving thousands of work items for long contexts.
+// Partition policy for partition_size == 0: about an eighth of the longest
+// context the block table can hold, as a power of two in [256, 4096] tokens.
+// The longest sequence then spreads over at least ~8 work items (waves),
+// while items stay long enough to amortise their start-up (context length,
+// block-id window and first chunk are three dependent loads before a wave
+// streams) and the merge traffic stays near 1% of the KV bytes.  Measured on
+// the MHA, skewed, GQA and long-context 16-bit workloads, this lands on the
+// best of the power-of-two sizes for each.  One pass when the longest context
+// fits a partition.
 int32_t pick_partition(const DecodeShape& s) {
-  const int32_t g = s.num_q_heads / s.num_kv_heads;
-  int32_t p = 256;
-  while (p < 2048 && p * 2 <= 256 * ((g + 1) / 2)) p *= 2;
-  if (p % s.block_size) p = ((p + s.block_size - 1) / s.block_size) * s.block_size;
   const int64_t max_ctx = (int64_t)s.max_blocks_per_seq * s.block_size;
+  int64_t p = 256;
+  while (p < 4096 && p * 8 < max_ctx) p *= 2;
+  if (p % s.block_size) p = ((p + s.block_size - 1) / s.block_size) * s.block_size;
   if (max_ctx <= p) return (int32_t)max_ctx;  // one pass
-  return p;
+  return (int32_t)p;
 }
 
 int64_t n_partitions(const DecodeShape& s, int32_t p) {

@@ -138,7 +138,7 @@ def _dec(**kw):
     (dict(bt=None), ENULL),
     (dict(cl=None), ENULL),
     (dict(kc=FAKE + 4), ESHAPE),
-    (dict(ws=None, wsb=0), EWS),           # two partitions of 512 need a workspace
+    (dict(ws=None, wsb=0), EWS),           # four partitions of 256 need a workspace
     (dict(ws=FAKE, wsb=1024), EWS),        # too small
     (dict(ws=FAKE + 8, wsb=1 << 30), EWS),  # misaligned
 ])
@@ -169,10 +169,12 @@ def test_partition_policy_and_workspace_size():
     # one pass when the longest context fits one partition: no workspace
     assert L.pa_decode_partition_size(4, 4, 4, 64, 16, 13, F32, 0) == 208
     assert L.pa_decode_workspace_size(4, 4, 4, 64, 16, 13, 0, F32, 0) == 0
-    # MHA: 256-token partitions; GQA groups of 4: 512; of 8: 1024
-    assert L.pa_decode_partition_size(64, 32, 32, 128, 16, 128, F16, 0) == 256
-    assert L.pa_decode_partition_size(256, 32, 8, 128, 16, 512, BF16, 0) == 512
-    assert L.pa_decode_partition_size(64, 64, 8, 128, 32, 1025, BF16, 0) == 1024
+    # about an eighth of the longest context, a power of two in [256, 4096]
+    assert L.pa_decode_partition_size(64, 32, 32, 128, 16, 128, F16, 0) == 256     # 2048 max
+    assert L.pa_decode_partition_size(32, 40, 40, 128, 16, 256, F16, 0) == 512     # 4096 max
+    assert L.pa_decode_partition_size(256, 32, 8, 128, 16, 512, BF16, 0) == 1024   # 8192 max
+    assert L.pa_decode_partition_size(64, 64, 8, 128, 32, 1025, BF16, 0) == 4096   # 32800 max
+    assert L.pa_decode_partition_size(1, 8, 8, 128, 16, 100000, BF16, 0) == 4096   # capped
     # workspace = (m, l) and a head_dim vector per (seq, q head, partition), 256-B aligned
     B, Hq, d, MB, bs, P = 256, 32, 128, 512, 16, 512
     n_part = MB * bs // P
