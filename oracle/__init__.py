@@ -106,19 +106,19 @@ def cache_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, k_cache:
                 v_cache: np.ndarray, dtype: str) -> None:
     """In-place ORC-W on host arrays of raw bits.
 
-    k, v: [T][Hkv][d] (or [T][Hkv*d]); k_cache: [NB][Hkv][d/X][bs][X] with
-    X = 16 / element bytes; v_cache: [NB][Hkv][d][bs]; slot_mapping: int64 [T]."""
+    k, v: [T][Hkv][d] (or [T][Hkv*d]); k_cache: [NB][Hkv][bs/4][d/X][4][X] with
+    X = 16 / element bytes; v_cache: [NB][Hkv][bs/4][d][4]; slot_mapping: int64 [T]."""
     k = _raw(k, dtype)
     v = _raw(v, dtype)
     slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
     if not (k_cache.flags.c_contiguous and v_cache.flags.c_contiguous):
         raise OracleError("caches must be C-contiguous")
-    NB, Hkv, dx, bs, X = k_cache.shape
-    d = dx * X
-    if X != 16 // (4 if dtype == "f32" else 2):
-        raise OracleError(f"k_cache last dim {X} is not 16 bytes of {dtype}")
-    if v_cache.shape != (NB, Hkv, d, bs):
-        raise OracleError(f"v_cache shape {v_cache.shape} != {(NB, Hkv, d, bs)}")
+    NB, Hkv, nq, dx, four, X = k_cache.shape
+    d, bs = dx * X, nq * 4
+    if X != 16 // (4 if dtype == "f32" else 2) or four != 4:
+        raise OracleError(f"k_cache shape {k_cache.shape} is not the quad layout of {dtype}")
+    if v_cache.shape != (NB, Hkv, nq, d, 4):
+        raise OracleError(f"v_cache shape {v_cache.shape} != {(NB, Hkv, nq, d, 4)}")
     T = slots.shape[0]
     if k.size != T * Hkv * d or v.size != T * Hkv * d:
         raise OracleError("k/v size does not match slot_mapping")
@@ -133,8 +133,9 @@ def decode(q: np.ndarray, q_dtype: str, k_cache: np.ndarray, v_cache: np.ndarray
     """ORC-D: float64 [B][Hq][d] attention output (rows not requested stay NaN)."""
     q = _raw(q, q_dtype)
     B, Hq, d = q.shape
-    NB, Hkv, dx, bs, X = k_cache.shape
-    if dx * X != d or v_cache.shape != (NB, Hkv, d, bs):
+    NB, Hkv, nq, dx, four, X = k_cache.shape
+    bs = nq * 4
+    if dx * X != d or four != 4 or v_cache.shape != (NB, Hkv, nq, d, 4):
         raise OracleError("cache shapes do not match q")
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     cl = np.ascontiguousarray(context_lens, dtype=np.int32)

@@ -21,12 +21,14 @@
  *    mapping, per-sequence block tables, sequence lengths and a block size.
  *
  * Storage convention shared with the GPU library (a format both sides must
- * agree on, not arithmetic), with X = 16 / element bytes (8 for the 16-bit
- * types, 4 for fp32):
- *   key cache   [num_blocks][num_kv_heads][head_dim / X][block_size][X]
- *               (key element e of the token at offset o of a block is at
- *               chunk e / X, row o, lane e % X)
- *   value cache [num_blocks][num_kv_heads][head_dim][block_size]
+ * agree on, not arithmetic).  Tokens of a block are kept in quads of four
+ * consecutive offsets; X = 16 / element bytes (8 for the 16-bit types, 4 for
+ * fp32):
+ *   key cache   [num_blocks][num_kv_heads][block_size/4][head_dim/X][4][X]
+ *               (key element e of the token at offset o: quad o/4, chunk e/X,
+ *               row o%4, lane e%X)
+ *   value cache [num_blocks][num_kv_heads][block_size/4][head_dim][4]
+ *               (value element e of offset o: quad o/4, dim e, row o%4)
  *   slot s -> block s / block_size, offset s % block_size.
  *
  * Every floating-point step is done in double precision.  Half and bfloat16
@@ -161,7 +163,7 @@ int orc_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                     int32_t block_size, int32_t dtype) {
   int eb = orc_elem_bytes(dtype);
   if (!eb || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      num_blocks <= 0 || num_tokens < 0 || head_dim % (16 / eb) != 0)
+      num_blocks <= 0 || num_tokens < 0 || head_dim % (16 / eb) != 0 || block_size % 4 != 0)
     return ORC_ERR_ARG;
   const int64_t H = num_kv_heads, D = head_dim, BS = block_size, X = 16 / eb;
   for (int64_t i = 0; i < num_tokens; ++i) {
@@ -174,8 +176,9 @@ int orc_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
       for (int64_t e = 0; e < D; ++e) {
         int64_t src_k = i * k_token_stride + h * D + e;
         int64_t src_v = i * v_token_stride + h * D + e;
-        int64_t dst_k = (((blk * H + h) * (D / X) + e / X) * BS + off) * X + e % X;
-        int64_t dst_v = ((blk * H + h) * D + e) * BS + off;
+        int64_t quad = (blk * H + h) * (BS / 4) + off / 4;
+        int64_t dst_k = ((quad * (D / X) + e / X) * 4 + off % 4) * X + e % X;
+        int64_t dst_v = (quad * D + e) * 4 + off % 4;
         memcpy((char*)k_cache + dst_k * eb, (const char*)k + src_k * eb, eb);
         memcpy((char*)v_cache + dst_v * eb, (const char*)v + src_v * eb, eb);
       }
@@ -239,11 +242,12 @@ static int orc_decode_row(const orc_decode_job* J, int64_t row) {
       free(acc);
       return ORC_ERR_BLOCK;
     }
-    const int64_t ktile = (phys * Hkv + hk) * D * BS;  // this block's key tile
+    const int64_t o = t % BS;
+    const int64_t quad = (phys * Hkv + hk) * (BS / 4) + o / 4;  // this token's quad
     double dot = 0.0;
     for (int64_t e = 0; e < D; ++e)
       dot += orc_load(J->q, J->q_dtype, (b * Hq + hq) * D + e) *
-             orc_load(J->k_cache, J->kv_dtype, ktile + ((e / X) * BS + t % BS) * X + e % X);
+             orc_load(J->k_cache, J->kv_dtype, ((quad * (D / X) + e / X) * 4 + o % 4) * X + e % X);
     s[t] = J->scale * dot;
   }
 
@@ -261,8 +265,10 @@ static int orc_decode_row(const orc_decode_job* J, int64_t row) {
   for (int64_t e = 0; e < D; ++e) acc[e] = 0.0;
   for (int64_t t = 0; t < L; ++t) {
     int64_t phys = J->block_tables[b * MB + t / BS];
+    int64_t o = t % BS;
+    int64_t quad = (phys * Hkv + hk) * (BS / 4) + o / 4;
     for (int64_t e = 0; e < D; ++e) {
-      int64_t vidx = ((phys * Hkv + hk) * D + e) * BS + t % BS;
+      int64_t vidx = (quad * D + e) * 4 + o % 4;
       acc[e] += s[t] * orc_load(J->v_cache, J->kv_dtype, vidx);
     }
   }
@@ -303,7 +309,7 @@ int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
   if (!orc_elem_bytes(q_dtype) || !orc_elem_bytes(kv_dtype)) return ORC_ERR_ARG;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size % 4 != 0 ||
       head_dim % (16 / orc_elem_bytes(kv_dtype)) != 0)
     return ORC_ERR_ARG;
   if (rows) {

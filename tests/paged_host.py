@@ -20,19 +20,42 @@ def key_chunk(dtype: str) -> int:
     return 4 if dtype == "f32" else 8
 
 
+def key_pool_shape(NB: int, H: int, d: int, bs: int, dtype: str) -> tuple:
+    X = key_chunk(dtype)
+    return (NB, H, bs // 4, d // X, 4, X)
+
+
+def value_pool_shape(NB: int, H: int, d: int, bs: int) -> tuple:
+    return (NB, H, bs // 4, d, 4)
+
+
 def poisoned_pool(wl: Workload, transposed: bool) -> np.ndarray:
-    """Value pool [NB][Hkv][d][bs] (transposed=True) or key pool
-    [NB][Hkv][d/X][bs][X], filled with the dtype's quiet NaN."""
+    """Value pool [NB][Hkv][bs/4][d][4] (transposed=True) or key pool
+    [NB][Hkv][bs/4][d/X][4][X], filled with the dtype's quiet NaN."""
     c = wl.cfg
-    X = key_chunk(c.dtype)
-    shape = ((wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size) if transposed else
-             (wl.num_blocks, c.num_kv_heads, c.head_dim // X, c.block_size, X))
+    shape = (value_pool_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size)
+             if transposed else
+             key_pool_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.dtype))
     return np.full(shape, POISON_BITS[c.dtype], dtype=_BITS_NP[c.dtype])
 
 
 def key_rows(kc: np.ndarray, blk: int, off: int) -> np.ndarray:
     """The [Hkv][d] key rows of the token at (block, offset) of a key pool."""
-    return kc[blk, :, :, off, :].reshape(kc.shape[1], -1)
+    return kc[blk, :, off // 4, :, off % 4, :].reshape(kc.shape[1], -1)
+
+
+def value_rows(vc: np.ndarray, blk: int, off: int) -> np.ndarray:
+    """The [Hkv][d] value rows of the token at (block, offset) of a value pool."""
+    return vc[blk, :, off // 4, :, off % 4]
+
+
+def offset_major(pool: np.ndarray, key: bool) -> np.ndarray:
+    """A pool viewed as [block][offset][...] (for per-slot comparisons)."""
+    if key:  # [NB][H][bs/4][d/X][4][X] -> [NB][bs/4][4][H][d/X][X] -> [NB][bs][...]
+        t = pool.transpose(0, 2, 4, 1, 3, 5)
+    else:    # [NB][H][bs/4][d][4] -> [NB][bs/4][4][H][d]
+        t = pool.transpose(0, 2, 4, 1, 3)
+    return t.reshape(pool.shape[0], pool.shape[2] * 4, -1)
 
 
 class OracleState:

@@ -19,7 +19,8 @@ import torch
 
 import oracle
 from pagedattention_kv_cache_amd.workloads import CONFIGS, Workload, custom_config, raw_bits
-from tests.paged_host import OracleState, key_chunk, key_rows, logical_kv, poisoned_pool
+from tests.paged_host import (OracleState, key_pool_shape, key_rows, logical_kv, offset_major,
+                               poisoned_pool, value_pool_shape, value_rows)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -98,12 +99,12 @@ def test_cache_write_hand_worked_layout():
         h = np.arange(H)[None, :, None]
         e = np.arange(d)[None, None, :]
         k = (100 * i + 10 * h + e + 1).astype(np.float32)
-        ek = np.zeros((NB, H, d // X, bs, X), np.float32)
-        ev = np.zeros((NB, H, d, bs), np.float32)
-        for blk, hh, ch, off, lane, val in cs["K"]:
-            ek[blk, hh, ch, off, lane] = val
-        for blk, hh, ee, off, val in cs["V"]:
-            ev[blk, hh, ee, off] = val
+        ek = np.zeros((NB, H, bs // 4, d // X, 4, X), np.float32)
+        ev = np.zeros((NB, H, bs // 4, d, 4), np.float32)
+        for blk, hh, quad, ch, row, lane, val in cs["K"]:
+            ek[blk, hh, quad, ch, row, lane] = val
+        for blk, hh, quad, ee, row, val in cs["V"]:
+            ev[blk, hh, quad, ee, row] = val
         if cs["dtype"] == "f32":
             kb, vb = k.view(np.uint32), (-k).view(np.uint32)
             kc = np.zeros(ek.shape, np.uint32)
@@ -140,14 +141,12 @@ def test_cache_write_roundtrip_and_poison(dtype):
             blk = wl.block_tables[b, pos // cfg.block_size]
             off = pos % cfg.block_size
             assert np.array_equal(key_rows(st.kc, blk, off), kb[pos])
-            assert np.array_equal(st.vc[blk, :, :, off], vb[pos])
+            assert np.array_equal(value_rows(st.vc, blk, off), vb[pos])
             written[blk, off] = True
-    pois = poisoned_pool(wl, False)
-    # key pool as [block][offset][...]: slots never written keep their poison
-    kt = st.kc.transpose(0, 3, 1, 2, 4)
-    assert np.array_equal(kt[~written], pois.transpose(0, 3, 1, 2, 4)[~written])
-    vt = st.vc.transpose(0, 3, 1, 2)
-    assert np.array_equal(vt[~written], poisoned_pool(wl, True).transpose(0, 3, 1, 2)[~written])
+    # pools as [block][offset][...]: slots never written keep their poison
+    kt, vt = offset_major(st.kc, True), offset_major(st.vc, False)
+    assert np.array_equal(kt[~written], offset_major(poisoned_pool(wl, False), True)[~written])
+    assert np.array_equal(vt[~written], offset_major(poisoned_pool(wl, True), False)[~written])
     # skip semantics: all-negative slots leave the pools untouched
     kc0, vc0 = st.kc.copy(), st.vc.copy()
     oracle.cache_write(raw_bits(st.step_k[0]), raw_bits(st.step_v[0]),
@@ -156,8 +155,8 @@ def test_cache_write_roundtrip_and_poison(dtype):
 
 
 def test_cache_write_rejects_out_of_range_slot():
-    kc = np.zeros((2, 1, 1, 4, 4), np.float32)
-    vc = np.zeros((2, 1, 4, 4), np.float32)
+    kc = np.zeros(key_pool_shape(2, 1, 4, 4, "f32"), np.float32)
+    vc = np.zeros(value_pool_shape(2, 1, 4, 4), np.float32)
     k = np.ones((1, 1, 4), np.float32)
     with pytest.raises(oracle.OracleError):
         oracle.cache_write(k.view(np.uint32), k.view(np.uint32), np.array([8]),
@@ -182,9 +181,9 @@ def _brute(wl: Workload, step: int) -> np.ndarray:
 
 
 @pytest.mark.parametrize("dtype,d,bs,hq,hkv,lens,seed", [
-    ("f32", 8, 1, 2, 2, [1, 5, 9], 21),
+    ("f32", 8, 4, 2, 2, [1, 5, 9], 21),
     ("f32", 64, 16, 4, 4, [1, 17, 64, 70], 22),
-    ("f16", 8, 2, 4, 2, [3, 33, 70], 23),
+    ("f16", 8, 8, 4, 2, [3, 33, 70], 23),
     ("bf16", 64, 4, 4, 1, [2, 40, 64], 24),
     ("bf16", 8, 16, 8, 2, [16, 17, 48], 25),
     ("f16", 64, 4, 3, 3, [69], 26),
@@ -221,9 +220,8 @@ def _paged_from_logical(Ks, Vs, bs, perm_seed, nb_extra=3, dtype="f32"):
     perm = rng.permutation(NB)
     bits = np.uint32 if dtype == "f32" else np.uint16
     from pagedattention_kv_cache_amd.workloads import POISON_BITS
-    X = key_chunk(dtype)
-    kc = np.full((NB, H, d // X, bs, X), POISON_BITS[dtype], bits)
-    vc = np.full((NB, H, d, bs), POISON_BITS[dtype], bits)
+    kc = np.full(key_pool_shape(NB, H, d, bs, dtype), POISON_BITS[dtype], bits)
+    vc = np.full(value_pool_shape(NB, H, d, bs), POISON_BITS[dtype], bits)
     MB = max(nblk)
     bt = np.full((len(Ks), MB), -1, np.int32)
     off = 0
@@ -250,7 +248,7 @@ def test_block_permutation_and_block_size_invariance():
     q = _rand_f32(rng, (len(lens), Hq, d)).view(np.uint32)
     cl = np.array(lens, np.int32)
     outs = []
-    for bs, ps in [(1, 0), (2, 1), (4, 2), (8, 3), (16, 4), (16, 5), (32, 6), (64, 7)]:
+    for bs, ps in [(4, 0), (4, 1), (8, 2), (8, 3), (16, 4), (16, 5), (32, 6), (64, 7)]:
         kc, vc, bt = _paged_from_logical(Ks, Vs, bs, ps)
         outs.append(oracle.decode(q, "f32", kc, vc, "f32", bt, cl, 0.25))
     for o in outs[1:]:
@@ -340,7 +338,7 @@ def test_two_token_closed_form():
     K = _rand_f32(rng, (2, 1, d))
     V = _rand_f32(rng, (2, 1, d))
     q = _rand_f32(rng, (1, 1, d))
-    kc, vc, bt = _paged_from_logical([K.view(np.uint32)], [V.view(np.uint32)], 2, 0)
+    kc, vc, bt = _paged_from_logical([K.view(np.uint32)], [V.view(np.uint32)], 4, 0)
     out = oracle.decode(q.view(np.uint32), "f32", kc, vc, "f32", bt, np.array([2], np.int32), 0.9)
     # the library and the oracle take scale as fp32
     s = float(np.float32(0.9)) * (K[:, 0, :].astype(np.float64) @ q[0, 0].astype(np.float64))
