@@ -33,13 +33,15 @@
  *   - Errors are reported by the return value: a negative pa_status, detected
  *     on the host before anything is launched (or PA_ERR_HIP if a launch
  *     fails).  No C++ exception crosses this interface.
- *   - Cache layout (chosen for gfx950, see each kernel), with X = 16 bytes /
- *     element size (8 for f16/bf16, 4 for f32):
- *       key cache   [num_blocks][num_kv_heads][head_dim / X][block_size][X]
- *       value cache [num_blocks][num_kv_heads][head_dim][block_size]
- *     Key element e of the token at offset o lives in 16-byte chunk e / X at
- *     row o, so one chunk of consecutive tokens is a contiguous run; for one
- *     value dimension, a block's consecutive tokens are contiguous too.
+ *   - Cache layout (chosen for gfx950, see each kernel): the tokens of a block
+ *     are kept in quads of four consecutive offsets; X = 16 bytes / element
+ *     size (8 for f16/bf16, 4 for f32):
+ *       key cache   [num_blocks][num_kv_heads][block_size/4][head_dim/X][4][X]
+ *       value cache [num_blocks][num_kv_heads][block_size/4][head_dim][4]
+ *     Key element e of the token at offset o: quad o/4, chunk e/X, row o%4,
+ *     lane e%X.  Value element e of offset o: quad o/4, dim e, row o%4.  So a
+ *     quad's 16-byte key chunks and a quad's four values of one dim are
+ *     contiguous, and one token's write fills 32 of each 128 bytes it touches.
  *   - Slot s addresses block s / block_size, offset s % block_size.
  *   - Block-table entries and slots are preconditions: entries
  *     block_tables[b][0 .. ceil(L_b/block_size)-1] must lie in
@@ -79,10 +81,10 @@ typedef enum pa_status {
 
 /*
  * pa_cache_write -- for every token i in [0, num_tokens) whose
- * slot_mapping[i] >= 0, copy k[i][h][e] into
- * k_cache[slot / block_size][h][e / X][slot % block_size][e % X] and
- * v[i][h][e] into v_cache[slot / block_size][h][e][slot % block_size], for all
- * kv heads h and dims e, as raw bits.  Tokens with a negative slot are skipped (padding).  All other
+ * slot_mapping[i] >= 0, with block = slot / block_size and o = slot %
+ * block_size, copy k[i][h][e] into k_cache[block][h][o/4][e/X][o%4][e%X] and
+ * v[i][h][e] into v_cache[block][h][o/4][e][o%4], for all kv heads h and dims
+ * e, as raw bits.  Tokens with a negative slot are skipped (padding).  All other
  * cache bytes are left unchanged.
  *
  *   k, v            device, dtype, token i / head h / dim e at

@@ -10,9 +10,10 @@ fallback.  If libpa.so is missing, :func:`lib` raises -- build it with
     decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
            block_size, partition_size=0, workspace=None, flags=AUTO)
 
-Cache tensors: ``k_cache`` [num_blocks][num_kv_heads][head_dim/X][block_size][X]
-with X = 16 bytes / element size (see :func:`key_cache_shape`), ``v_cache``
-[num_blocks][num_kv_heads][head_dim][block_size].
+Cache tensors (tokens of a block in quads of four consecutive offsets):
+``k_cache`` [num_blocks][num_kv_heads][block_size/4][head_dim/X][4][X] with
+X = 16 bytes / element size (see :func:`key_cache_shape`), ``v_cache``
+[num_blocks][num_kv_heads][block_size/4][head_dim][4].
 """
 from __future__ import annotations
 
@@ -44,22 +45,25 @@ def key_chunk(dtype: torch.dtype) -> int:
 
 def key_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
                     dtype: torch.dtype) -> tuple:
+    """[blocks][kv heads][block_size/4][head_dim/X][4][X]: tokens in quads of four."""
     X = key_chunk(dtype)
-    return (num_blocks, num_kv_heads, head_dim // X, block_size, X)
+    return (num_blocks, num_kv_heads, block_size // 4, head_dim // X, 4, X)
 
 
 def value_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int,
                       block_size: int) -> tuple:
-    return (num_blocks, num_kv_heads, head_dim, block_size)
+    """[blocks][kv heads][block_size/4][head_dim][4]."""
+    return (num_blocks, num_kv_heads, block_size // 4, head_dim, 4)
 
 
 def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
     """(num_blocks, num_kv_heads, block_size, head_dim) from validated caches."""
-    _require(k_cache.dim() == 5 and v_cache.dim() == 4, "k_cache must be 5-D, v_cache 4-D")
-    NB, H, dx, bs, X = k_cache.shape
-    _require(X == key_chunk(k_cache.dtype), "k_cache last dim must be 16 bytes of elements")
-    d = dx * X
-    _require(tuple(v_cache.shape) == (NB, H, d, bs), "v_cache shape does not match k_cache")
+    _require(k_cache.dim() == 6 and v_cache.dim() == 5, "k_cache must be 6-D, v_cache 5-D")
+    NB, H, nq, dx, four, X = k_cache.shape
+    _require(X == key_chunk(k_cache.dtype) and four == 4,
+             "k_cache must be [blocks][heads][block_size/4][head_dim/X][4][X]")
+    d, bs = dx * X, nq * 4
+    _require(tuple(v_cache.shape) == (NB, H, nq, d, 4), "v_cache shape does not match k_cache")
     _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
     return NB, H, bs, d
 

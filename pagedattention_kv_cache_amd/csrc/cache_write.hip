@@ -6,12 +6,13 @@
 // arithmetic on values.
 //
 // Thread mapping: one thread moves one 16-byte chunk of one (token, kv head)
-// row.  Keys: the key cache is [block][head][chunk][block_size][16 bytes], so
-// chunk c of the token at offset o lands at (c * block_size + o) * 16 bytes
-// into the (block, head) tile; tokens of consecutive offsets fill consecutive
-// 16-byte slots of one chunk row.  Values: the value cache is
-// [block][head][dim][block_size], so the chunk's elements go to consecutive
-// dims of one offset, block_size elements apart.
+// row.  Both caches keep the tokens of a block in quads of four consecutive
+// offsets.  Keys: [block][head][quad][chunk][4][16 bytes], so chunk c of the
+// token at offset o lands at ((o/4 * chunks + c) * 4 + o%4) * 16 bytes into
+// the (block, head) tile.  Values: [block][head][quad][dim][4], so the
+// chunk's elements go to consecutive dims of row o%4, four elements apart.
+// A single token therefore fills 32 of every 128 bytes it touches, not a
+// single 16- or 2-byte slot of each line.
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
 
@@ -43,13 +44,13 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int 
   const uint4 kraw = ld16(ksrc);
   const uint4 vraw = ld16(vsrc);
 
-  const int64_t head_base = blk * a.num_kv_heads + h;
-  char* kdst = reinterpret_cast<char*>(a.k_cache) +
-               ((head_base * chunks_per_row + c) * a.block_size + off) * 16;
+  const int64_t quad = (blk * a.num_kv_heads + h) * (a.block_size / 4) + off / 4;
+  const int row = off % 4;
+  char* kdst = reinterpret_cast<char*>(a.k_cache) + ((quad * chunks_per_row + c) * 4 + row) * 16;
   *reinterpret_cast<uint4*>(kdst) = kraw;
 
-  char* vrow = reinterpret_cast<char*>(a.v_cache) + ((head_base * D + e0) * a.block_size + off) * EB;
-  const int64_t vstep = (int64_t)a.block_size * EB;
+  char* vrow = reinterpret_cast<char*>(a.v_cache) + ((quad * D + e0) * 4 + row) * EB;
+  const int64_t vstep = 4 * EB;  // next dim of the same row
   if constexpr (EB == 4) {
     const uint32_t w[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
 #pragma unroll

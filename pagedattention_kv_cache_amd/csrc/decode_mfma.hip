@@ -15,13 +15,15 @@
 //   lane = 16*j + n, n in [0,16), j in [0,4).
 //   Chunks of 16 tokens.
 //   QK^T (16x16x32): A = keys, row n = token n of the chunk, k-slots = the 8
-//         dims of key chunk 4c + j (the key cache keeps each 16-byte chunk of
-//         consecutive tokens contiguous, so the 16 lanes of a group read one
-//         256-byte run); B = queries, column n = head n, same k-slots.
-//         Result: lane (n, j) holds head n's scores of tokens 4j .. 4j+3.
-//   P.V (16x16x16): A = values from the [dim][block_size] value layout,
-//         row n = dim 16c + n, k-slots = tokens 4j .. 4j+3 (one contiguous
-//         8-byte run); B = probabilities, column n = head n, k-slots = the
+//         dims of key chunk 4c + j (the key cache keeps a 16-byte chunk of
+//         four consecutive tokens contiguous and the chunks of a token quad
+//         side by side, so the four lanes n of a quad and the four groups j
+//         read one 256-byte run per quad); B = queries, column n = head n,
+//         same k-slots.  Result: lane (n, j) holds head n's scores of tokens
+//         4j .. 4j+3.
+//   P.V (16x16x16): A = values from the [quad][dim][4] value layout, row
+//         n = dim 16c + n, k-slots = tokens 4j .. 4j+3 (quad j of the chunk:
+//         one 8-byte run); B = probabilities, column n = head n, k-slots = the
 //         same tokens -- exactly the registers the QK^T result left in the
 //         lane, so no shuffle is needed.  Result: lane (n, j) holds
 //         O^T[16c + 4j + r][n].
@@ -75,11 +77,10 @@ template <> struct Mma<Elem::F16> {
 
 constexpr int kChunk = 16;  // tokens per iteration: one 16-row QK^T tile
 
-// Cache-policy bits of buffer loads: non-temporal.  Used for keys only: a
-// chunk's key loads consume whole cache lines (16 tokens x 16 bytes per key
-// chunk), while a value row of a block larger than 16 tokens is split across
-// consecutive chunks, and streaming hints on it were measured to cost a
-// re-fetch of the second half.
+// Cache-policy bits of buffer loads: non-temporal.  Used for keys, whose
+// 256-byte quad runs a chunk consumes whole; values stay on the default
+// policy (measured: streaming hints on values cost re-fetches when a value
+// line is shared by consecutive chunks).
 constexpr int kNonTemporal = 2;
 
 
@@ -161,12 +162,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
   const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
-  const int64_t vrow16 = (int64_t)16 * bs * 2;  // bytes between value rows 16 dims apart
 
-  // per-lane byte offsets inside a (block, head) tile
-  const uint32_t koff = (uint32_t)((j * bs + n) * 16);     // key chunk j, token n
-  const uint32_t voff = (uint32_t)((n * bs + 4 * j) * 2);  // value row n, tokens 4j..4j+3
-  const int kstep = 64 * bs;                               // bytes between key chunks 4 apart
+  // per-lane byte offsets from the chunk's first token quad: key token n
+  // (quad n/4, row n%4) chunk j; value quad j, dim n.  Key chunk 4c + j and
+  // value dim 16c + n add 256*c and 128*c bytes.
+  constexpr int CPR = D / 8;  // 16-byte key chunks per row
+  const int koff = ((n >> 2) * CPR + j) * 64 + (n & 3) * 16;
+  const int voff = (j * D + n) * 8;
 
   int wb = t_begin >> lbs;  // first logical block of the current block-id window
   int bt_lane = (int)clamp_block(bt_first, a.num_blocks);  // lane i: block of wb + i
@@ -181,32 +183,31 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       // one block: a buffer resource based at the chunk's key / value tile,
       // per-lane 32-bit offsets, the 16-dim row stride as the scalar offset
       const int phys = __builtin_amdgcn_readlane(bt_lane, min(t0 >> lbs, last_blk) - wb);
-      const int64_t tile = (int64_t)phys * block_stride;
-      const int in_blk = t0 & (bs - 1);
+      const int64_t first_quad = (int64_t)phys * block_stride + (int64_t)(t0 & (bs - 1)) * D * 2;
       const int range = none ? 0 : 0x7fffffff;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + tile + (int64_t)in_blk * 16, range);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + tile + (int64_t)in_blk * 2, range);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + first_quad, range);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + first_quad, range);
 #pragma unroll
       for (int c = 0; c < KC; ++c)
         buf.k[c] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rk, (int)koff, c * kstep, kNonTemporal));
+                                                rk, koff + 256 * c, 0, kNonTemporal));
 #pragma unroll
       for (int c = 0; c < VC; ++c)
         buf.v[c] = __builtin_bit_cast(vec4, __builtin_amdgcn_raw_buffer_load_b64(
-                                                rv, (int)voff, c * (int)vrow16, 0));
+                                                rv, voff + 128 * c, 0, 0));
     } else {
       const int tk = t0 + n;      // this lane's key token
-      const int tv = t0 + 4 * j;  // first token of this lane's value run
+      const int tv = t0 + 4 * j;  // first token of this lane's value quad
       const int pk = __shfl(bt_lane, min(tk >> lbs, last_blk) - wb);
       const int pv = __shfl(bt_lane, min(tv >> lbs, last_blk) - wb);
-      const char* kp =
-          kc + (int64_t)pk * block_stride + ((int64_t)j * bs + (tk & (bs - 1))) * 16;
-      const char* vp = vc + (int64_t)pv * block_stride + ((int64_t)n * bs + (tv & (bs - 1))) * 2;
+      const int ik = tk & (bs - 1), iv = tv & (bs - 1);
+      const char* kp = kc + (int64_t)pk * block_stride +
+                       (((ik >> 2) * CPR + j) * 64 + (ik & 3) * 16);
+      const char* vp = vc + (int64_t)pv * block_stride + (((iv >> 2) * D + n) * 8);
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        buf.k[c] = __builtin_bit_cast(vec8, ld16_nt(kp + (int64_t)c * kstep));
+      for (int c = 0; c < KC; ++c) buf.k[c] = __builtin_bit_cast(vec8, ld16_nt(kp + 256 * c));
 #pragma unroll
-      for (int c = 0; c < VC; ++c) buf.v[c] = *reinterpret_cast<const vec4*>(vp + c * vrow16);
+      for (int c = 0; c < VC; ++c) buf.v[c] = *reinterpret_cast<const vec4*>(vp + 128 * c);
     }
   };
 

@@ -12,16 +12,17 @@
 // Per tile:
 //  * scores: a key row (head_dim * elem bytes) is spread over RL = row/16
 //    lanes holding one 16-byte chunk each, TPI = 64/RL tokens per load
-//    instruction (with the chunked key layout, chunk c of TPI consecutive
-//    tokens is one contiguous run); each lane forms partial dots for every
-//    head of the group and a DPP butterfly within the row completes them;
+//    instruction (with the token-quad key layout the lanes of one
+//    instruction read one contiguous run); each lane forms partial dots for
+//    every head of the group and a DPP butterfly within the row completes
+//    them;
 //  * online softmax in the exp2 domain (scale * log2 e folded into the
 //    scores): the tile max is made wave-uniform, so the running max m, the
 //    rescale factor and the accumulator rescale are uniform per head;
 //  * the tile's probabilities go through LDS (broadcast reads) and each lane
 //    accumulates p * v for head_dim/64 output dims from the value cache's
-//    [dim][block_size] rows: 8 consecutive tokens of one dim are one
-//    contiguous run.
+//    [quad][dim][4] layout: the four tokens of a quad of one dim are one
+//    contiguous run, and consecutive lanes read consecutive dims.
 // Memory: the block ids of a 64-block window sit one per lane and are read
 // with readlane; each 8-token segment of a tile gets a buffer resource at its
 // block, so lanes only add fixed 32-bit offsets; tile i+1 is loaded while
@@ -36,16 +37,48 @@ namespace {
 
 constexpr int kTile = 16;
 
+// Four tokens of one value dim: 8 bytes for the 16-bit types, 16 for fp32.
+template <int EB> struct QuadRaw;
+template <> struct QuadRaw<2> { using type = uint2; };
+template <> struct QuadRaw<4> { using type = uint4; };
+
 template <Elem KV, int D>
 struct Tile {
   static constexpr int EB = ElemTraits<KV>::bytes;
   static constexpr int RL = D * EB / 16;         // lanes per key row
   static constexpr int NI = kTile / (64 / RL);   // key load instructions per tile
   static constexpr int DPL = D / 64;             // value dims per lane
-  static constexpr int VL = 8 * EB / 16;         // 16-byte loads per 8-token segment and dim
+  using VQ = typename QuadRaw<EB>::type;
   uint4 k[NI];
-  uint4 v[2][DPL][VL];
+  VQ v[4][DPL];  // [token quad of the tile][owned dim]
 };
+
+template <Elem KV>
+__device__ __forceinline__ void widen_quad(const uint2& r, float* out) {
+  out[0] = lo_to_f32<KV>(r.x);
+  out[1] = hi_to_f32<KV>(r.x);
+  out[2] = lo_to_f32<KV>(r.y);
+  out[3] = hi_to_f32<KV>(r.y);
+}
+template <Elem KV>
+__device__ __forceinline__ void widen_quad(const uint4& r, float* out) {
+  out[0] = __uint_as_float(r.x);
+  out[1] = __uint_as_float(r.y);
+  out[2] = __uint_as_float(r.z);
+  out[3] = __uint_as_float(r.w);
+}
+
+template <int EB>
+__device__ __forceinline__ typename QuadRaw<EB>::type buf_ld_quad(__amdgpu_buffer_rsrc_t r,
+                                                                  int voff, int soff);
+template <>
+__device__ __forceinline__ uint2 buf_ld_quad<2>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+template <>
+__device__ __forceinline__ uint4 buf_ld_quad<4>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return buf_ld16(r, voff, soff);
+}
 
 template <Elem KV, int D, int G>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
@@ -56,9 +89,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   constexpr int TPI = 64 / RL;     // tokens per key load instruction
   constexpr int NI = T::NI;
   constexpr int DPL = T::DPL;
-  constexpr int SEG = 8;           // tokens per value load segment (one block)
+  constexpr int SEG = 8;           // tokens per load segment (one block)
   constexpr int NSEG = kTile / SEG;
-  constexpr int VL = T::VL;
   static_assert(RL >= 8 && RL <= 64 && 64 % RL == 0, "row layout");
   static_assert(TPI <= SEG, "a key load instruction stays inside one block");
 
@@ -115,11 +147,12 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
 
-  // per-lane byte offsets inside a (block, head) tile, relative to the segment
-  const int koff = (c * bs + row) * 16;  // key chunk c of token `row`
-  int voff[DPL];                         // value row of each owned dim
+  // per-lane byte offsets from a segment's first token quad: key chunk c of
+  // token `row` (quad row/4, row row%4); the value quad of each owned dim
+  const int koff = ((row >> 2) * RL + c) * 64 + (row & 3) * 16;
+  int voff[DPL];
 #pragma unroll
-  for (int dd = 0; dd < DPL; ++dd) voff[dd] = (lane * DPL + dd) * bs * EB;
+  for (int dd = 0; dd < DPL; ++dd) voff[dd] = (dd * 64 + lane) * 4 * EB;
 
   int wb = t_begin >> lbs;  // block-id window: lane i holds the block of wb + i
   int bt_lane = (int)clamp_block(bt_first, a.num_blocks);
@@ -135,22 +168,21 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     for (int sgm = 0; sgm < NSEG; ++sgm) {
       const int tok = t0 + sgm * SEG;
       const int phys = __builtin_amdgcn_readlane(bt_lane, min(tok >> lbs, last_blk) - wb);
-      const int64_t tile = (int64_t)phys * block_stride;
-      const int in_blk = tok & (bs - 1);
-      rk[sgm] = make_rsrc(kc + tile + (int64_t)in_blk * 16, range);
-      rv[sgm] = make_rsrc(vc + tile + (int64_t)in_blk * EB, range);
+      const int64_t first_quad = (int64_t)phys * block_stride + (int64_t)(tok & (bs - 1)) * D * EB;
+      rk[sgm] = make_rsrc(kc + first_quad, range);
+      rv[sgm] = make_rsrc(vc + first_quad, range);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int sgm = (i * TPI) / SEG;
-      buf.k[i] = buf_ld16(rk[sgm], koff, ((i * TPI) % SEG) * 16);
+      const int l0 = (i * TPI) % SEG;  // first token of the instruction inside the segment
+      buf.k[i] = buf_ld16(rk[sgm], koff, (l0 >> 2) * RL * 64 + (l0 & 3) * 16);
     }
 #pragma unroll
-    for (int sgm = 0; sgm < NSEG; ++sgm)
+    for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
       for (int dd = 0; dd < DPL; ++dd)
-#pragma unroll
-        for (int jj = 0; jj < VL; ++jj) buf.v[sgm][dd][jj] = buf_ld16(rv[sgm], voff[dd], 16 * jj);
+        buf.v[qd][dd] = buf_ld_quad<EB>(rv[qd >> 1], voff[dd], (qd & 1) * D * 4 * EB);
   };
 
   __shared__ float p_lds[G][kTile];
@@ -214,15 +246,14 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     // ---- p . V -------------------------------------------------------------
     const int nv = min(kTile, t_stop - t0);  // valid tokens in this tile
 #pragma unroll
-    for (int sgm = 0; sgm < NSEG; ++sgm) {
+    for (int qd = 0; qd < 4; ++qd) {
 #pragma unroll
       for (int dd = 0; dd < DPL; ++dd) {
-        float vf[SEG];
+        float vf[4];
+        widen_quad<KV>(buf.v[qd][dd], vf);
 #pragma unroll
-        for (int jj = 0; jj < VL; ++jj) widen16<KV>(buf.v[sgm][dd][jj], vf + jj * EPL);
-#pragma unroll
-        for (int r = 0; r < SEG; ++r) {
-          const int t = sgm * SEG + r;
+        for (int r = 0; r < 4; ++r) {
+          const int t = qd * 4 + r;
           if (t < nv) {
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(p_lds[g][t], vf[r], acc[g][dd]);
@@ -264,11 +295,11 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
       const float inv = 1.0f / l;
 #pragma unroll
       for (int dd = 0; dd < DPL; ++dd)
-        store_elem(a.out, row_id * D + lane * DPL + dd, acc[g][dd] * inv, a.out_dtype);
+        store_elem(a.out, row_id * D + dd * 64 + lane, acc[g][dd] * inv, a.out_dtype);
     } else {
       const int64_t slot = row_id * a.max_partitions + part;
 #pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) a.ws_acc[slot * D + lane * DPL + dd] = acc[g][dd];
+      for (int dd = 0; dd < DPL; ++dd) a.ws_acc[slot * D + dd * 64 + lane] = acc[g][dd];
       if (lane == 0) {
         a.ws_ml[slot * 2] = m[g];
         a.ws_ml[slot * 2 + 1] = l;

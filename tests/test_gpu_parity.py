@@ -102,13 +102,14 @@ def test_cache_write_strided_tokens_and_negative_slots():
     slots = torch.randperm(NB * bs, generator=g)[:T].to(torch.int64)
     slots[::5] = -1
     kc_o = np.full(pa.key_cache_shape(NB, H, d, bs, torch.bfloat16), 0x7FC0, np.uint16)
-    vc_o = np.full((NB, H, d, bs), 0x7FC0, np.uint16)
+    vc_o = np.full(pa.value_cache_shape(NB, H, d, bs), 0x7FC0, np.uint16)
     oracle.cache_write(raw_bits(k.contiguous()), raw_bits(v.contiguous()), slots.numpy(), kc_o,
                        vc_o, "bf16")
     # start from the same poisoned pools as the oracle
     kc = torch.full(pa.key_cache_shape(NB, H, d, bs, torch.bfloat16), 0x7FC0, dtype=torch.int16,
                     device="cuda").view(torch.bfloat16)
-    vc = torch.full((NB, H, d, bs), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vc = torch.full(pa.value_cache_shape(NB, H, d, bs), 0x7FC0, dtype=torch.int16,
+                    device="cuda").view(torch.bfloat16)
     qkv_d = qkv.cuda()
     pa.cache_write(qkv_d[:, H * d:2 * H * d].view(T, H, d), qkv_d[:, 2 * H * d:].view(T, H, d),
                    slots.cuda(), kc, vc)
@@ -231,7 +232,7 @@ def test_one_hot_probe_bit_exact(dtype, partition, kernel):
         K = torch.zeros(L, H, d, dtype=dt)
         K[t, 0] = (qf[0, 0] * c).to(dt)
         kc = torch.full(pa.key_cache_shape(NB, H, d, bs, dt), float("nan"), dtype=dt, device="cuda")
-        vc = torch.full((NB, H, d, bs), float("nan"), dtype=dt, device="cuda")
+        vc = torch.full(pa.value_cache_shape(NB, H, d, bs), float("nan"), dtype=dt, device="cuda")
         pa.cache_write(K.cuda(), V.cuda(), slots, kc, vc)
         out = torch.empty(1, 1, d, device="cuda")
         pa.decode(out, q.cuda(), kc, vc, bt, torch.tensor([L], dtype=torch.int32, device="cuda"),
