@@ -60,6 +60,10 @@ def parse_args(argv=None):
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1: the workload's setting (0 = library picks)")
     ap.add_argument("--flags", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--waves", type=int, choices=[0, 1, 2, 4], default=0,
+                    help="waves per decode work item (0: library picks)")
+    ap.add_argument("--no-work-list", action="store_true",
+                    help="one workgroup per possible decode item instead of the persistent grid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, host cores)")
     ap.add_argument("--layers", type=int, default=4,
@@ -300,6 +304,10 @@ def run(args):
     wl = Workload(cfg)
     c = cfg
     flags = {"auto": pa.AUTO, "valu": pa.FORCE_VALU, "mfma": pa.FORCE_MFMA}[args.flags]
+    if args.waves:
+        flags |= pa.WAVES_FLAG[args.waves]
+    if args.no_work_list:
+        flags |= pa.NO_WORK_LIST
     part = cfg.partition_size if args.partition_size < 0 else args.partition_size
 
     if args.copy_probe:
@@ -345,7 +353,7 @@ def run(args):
                                                        c.head_dim, c.block_size, MB, kdt, flags)
     ws_bytes = pa.decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
                                         c.block_size, MB, part, kdt, flags)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # zeroed once
     out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=torch.float32, device=dev)
     scale = c.attn_scale()
     stream = torch.cuda.current_stream(dev)
@@ -415,7 +423,15 @@ def run(args):
         "accumulate": "f32",
         "data": "synthetic (seeded N(0,1) q/K/V, shuffled block pool; no dataset)",
         "config": {"workload": c.name, **{k: v for k, v in wl.describe().items() if k != "workload"},
-                   "partition_size": int(p_eff), "kernel_flags": args.flags},
+                   "partition_size": int(p_eff), "kernel_flags": args.flags,
+                   "work_list": pa.decode_work_list(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                                    c.head_dim, c.block_size,
+                                                    wl.max_blocks_per_seq, int(p_eff), kdt, kdt,
+                                                    flags),
+                   "waves_per_item": pa.decode_waves(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                                     c.head_dim, c.block_size,
+                                                     wl.max_blocks_per_seq, int(p_eff), kdt, kdt,
+                                                     flags)},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(kv),

@@ -74,10 +74,21 @@ typedef enum pa_status {
   PA_ERR_HIP = -6          /* a HIP launch failed */
 } pa_status;
 
-/* pa_decode flags: which decode kernel family to use. */
-#define PA_DECODE_AUTO 0u      /* library picks */
+/* pa_decode flags.  Bits 0-1: which decode kernel family to use. */
+#define PA_DECODE_AUTO 0u       /* library picks kernel family and waves */
 #define PA_DECODE_FORCE_VALU 1u /* vector-ALU kernel (all dtypes) */
 #define PA_DECODE_FORCE_MFMA 2u /* matrix-core kernel (f16/bf16 KV only) */
+#define PA_DECODE_KERNEL_MASK 3u
+/* Bits 2-3: waves per (sequence, kv head, partition) work item; the waves
+ * split the item's tokens and merge their partial results on chip.  0 lets
+ * the library pick. */
+#define PA_DECODE_WAVES_1 4u
+#define PA_DECODE_WAVES_2 8u
+#define PA_DECODE_WAVES_4 12u
+#define PA_DECODE_WAVES_MASK 12u
+/* Bit 4: one workgroup per possible (sequence, head, partition) item instead
+ * of a persistent grid walking the list of items that hold tokens. */
+#define PA_DECODE_NO_WORK_LIST 16u
 
 /*
  * pa_cache_write -- for every token i in [0, num_tokens) whose
@@ -154,11 +165,18 @@ int pa_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
  *                  reduction and no workspace
  *   head_dim       64 or 128;  num_q_heads % num_kv_heads == 0
  *   workspace      device scratch of at least pa_decode_workspace_size(...)
- *                  bytes for the same arguments (may be NULL when that is 0);
- *                  its contents on entry do not matter
- *   flags          PA_DECODE_AUTO or a PA_DECODE_FORCE_* kernel choice
- * The result does not depend on partition_size or on the kernel family beyond
- * floating-point rounding (fp32 accumulation throughout).
+ *                  bytes for the same arguments (may be NULL when that is 0),
+ *                  16-byte aligned; its contents on entry do not matter.
+ *                  Calls that may run at the same time need distinct
+ *                  workspaces.
+ *   flags          PA_DECODE_AUTO, or a PA_DECODE_FORCE_* kernel choice OR-ed
+ *                  with a PA_DECODE_WAVES_* split (either part may be 0 =
+ *                  library picks) and optionally PA_DECODE_NO_WORK_LIST;
+ *                  other bits set, or both kernel bits, give
+ *                  PA_ERR_UNSUPPORTED
+ * The result does not depend on partition_size, the kernel family or the
+ * waves per item beyond floating-point rounding (fp32 accumulation
+ * throughout).
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -210,15 +228,38 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
 /*
  * The decode kernel family pa_decode runs for these arguments:
  * PA_DECODE_FORCE_VALU (1) or PA_DECODE_FORCE_MFMA (2); a negative pa_status
- * for an unsupported combination.
+ * for an unsupported combination.  The waves bits of flags are validated but
+ * do not affect the family.
  */
 int32_t pa_decode_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t q_dtype,
                          int32_t kv_dtype, uint32_t flags);
 
 /*
+ * The waves per work item (1, 2 or 4) pa_decode uses for these arguments
+ * (partition_size as passed to pa_decode, 0 allowed); a negative pa_status
+ * for invalid arguments.  A pure function of the arguments.
+ */
+int32_t pa_decode_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        int32_t partition_size, int32_t q_dtype, int32_t kv_dtype,
+                        uint32_t flags);
+
+/*
+ * 1 when pa_decode runs these arguments on a persistent grid over the list of
+ * (sequence, partition) items that hold tokens, 0 when it launches one
+ * workgroup per possible item; a negative pa_status for invalid arguments.
+ */
+int32_t pa_decode_work_list(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                            int32_t partition_size, int32_t q_dtype, int32_t kv_dtype,
+                            uint32_t flags);
+
+/*
  * Workspace bytes pa_decode needs for these arguments (partition_size as
- * passed to pa_decode, 0 allowed).  0 when a single pass suffices.  Returns 0
- * for invalid arguments as well; pa_decode reports those.
+ * passed to pa_decode, 0 allowed): per (sequence, q head, partition) the
+ * running max and sum, then the partial output vector, each region 256-byte
+ * aligned.  0 when a single pass
+ * suffices.  Returns 0 for invalid arguments as well; pa_decode reports those.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,

@@ -27,6 +27,12 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_OK = 0
 AUTO, FORCE_VALU, FORCE_MFMA = 0, 1, 2
+# waves per work item, OR-ed into flags (0 = library picks)
+WAVES_1, WAVES_2, WAVES_4 = 4, 8, 12
+WAVES_FLAG = {1: WAVES_1, 2: WAVES_2, 4: WAVES_4}
+# one workgroup per possible (sequence, head, partition) item instead of the
+# persistent grid over the items that hold tokens
+NO_WORK_LIST = 16
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _lib = None
@@ -92,6 +98,10 @@ def lib() -> ctypes.CDLL:
         L.pa_advance_step.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]
         L.pa_decode_kernel.restype = i32
         L.pa_decode_kernel.argtypes = [i32, i32, i32, i32, u32]
+        L.pa_decode_waves.restype = i32
+        L.pa_decode_waves.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, u32]
+        L.pa_decode_work_list.restype = i32
+        L.pa_decode_work_list.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, u32]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_status_string.argtypes = [i32]
         L.pa_abi_version.restype = i32
@@ -178,6 +188,28 @@ def decode_kernel(num_q_heads: int, num_kv_heads: int, q_dtype: torch.dtype,
     k = lib().pa_decode_kernel(num_q_heads, num_kv_heads, _DTYPE[q_dtype], _DTYPE[kv_dtype], flags)
     _check(min(k, 0))
     return {FORCE_VALU: "valu", FORCE_MFMA: "mfma"}[k]
+
+
+def decode_waves(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 block_size: int, max_blocks_per_seq: int, partition_size: int,
+                 q_dtype: torch.dtype, kv_dtype: torch.dtype, flags: int = AUTO) -> int:
+    """Waves per (sequence, kv head, partition) work item that decode uses."""
+    w = lib().pa_decode_waves(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                              max_blocks_per_seq, partition_size, _DTYPE[q_dtype],
+                              _DTYPE[kv_dtype], flags)
+    _check(min(w, 0))
+    return w
+
+
+def decode_work_list(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     block_size: int, max_blocks_per_seq: int, partition_size: int,
+                     q_dtype: torch.dtype, kv_dtype: torch.dtype, flags: int = AUTO) -> bool:
+    """Whether decode runs a persistent grid over the items that hold tokens."""
+    r = lib().pa_decode_work_list(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_blocks_per_seq, partition_size, _DTYPE[q_dtype],
+                                  _DTYPE[kv_dtype], flags)
+    _check(min(r, 0))
+    return bool(r)
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

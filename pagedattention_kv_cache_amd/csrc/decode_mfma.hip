@@ -11,7 +11,7 @@
 // Update" talk: PagedAttention over KV blocks; second kernel: sequences split
 // into partitions merged the way flash decoding merges them).
 //
-// Lane layout (one wave = one (sequence, kv head, partition) work item):
+// Lane layout (per wave of a (sequence, kv head, partition) work item):
 //   lane = 16*j + n, n in [0,16), j in [0,4).
 //   Chunks of 16 tokens.
 //   QK^T (16x16x32): A = keys, row n = token n of the chunk, k-slots = the 8
@@ -35,10 +35,18 @@
 // bits; all accumulation is fp32.  p = 1 and p = 0 stay exact.
 //
 // Memory: the block ids of the current 64-block window are held one per lane
-// and fetched with a lane read; the keys and values of chunk i+1 are loaded
-// while chunk i is computed (two register buffers).
+// and fetched with a lane read; the keys and values of a wave's next chunk are
+// loaded while its current chunk is computed (two register buffers).
+//
+// A work item may run on 1, 2 or 4 waves (one workgroup).  Wave w takes the
+// chunks w, w + W, w + 2W, ... of the partition with its own running max, sum
+// and accumulators, and at the end the waves' partial results are merged
+// through LDS with the same log-sum-exp rule that merges partitions.  More
+// waves per item shorten the longest items (one long sequence among short
+// ones) at the price of a few more start-up loads.
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
+#include "work_list.hpp"
 
 namespace pa {
 namespace {
@@ -95,7 +103,7 @@ struct Buffers {
 // adds a fixed 32-bit offset; otherwise (block_size 8) lanes address their
 // own blocks.
 template <Elem KV, int D, int G, bool UB>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
   using M = Mma<KV>;
   using vec8 = typename M::vec8;
   using vec4 = typename M::vec4;
@@ -103,226 +111,327 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KC = D / 32;  // QK^T k-chunks
   constexpr int VC = D / 16;  // P.V row chunks
 
-  // grid.x walks (sequence, kv head, head chunk) fastest so that consecutive
-  // workgroups -- which the dispatcher deals round-robin to the XCDs -- carry
-  // the same partition index of different sequences and heads; grid.y walks
-  // partitions from the last to the first, so the short first partitions of
-  // short sequences are dispatched at the end.
-  const int chunks = a.group / G;
-  const int item = blockIdx.x;
-  const int per_seq = a.num_kv_heads * chunks;
-  const int b = item / per_seq;
-  const int hc = item - b * per_seq;
-  const int h = hc / chunks;
-  const int hq0 = h * a.group + (hc % chunks) * G;
-  const int part = (int)gridDim.y - 1 - (int)blockIdx.y;
-  const int lane = threadIdx.x;
-  const int n = lane & 15;
-  const int j = lane >> 4;
-
-  // Start-up loads that do not depend on the context length go out together
-  // with it: the first block-id window (clamped to the table width; entries
-  // past the sequence are never used) and the queries.
-  const int lbs = a.log2_block_size;
-  const int bs = a.block_size;
-  const int P = a.partition_size;
-  const int t_begin = part * P;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const int L_in = a.context_lens[b];
-  const int bt_first = bt[min((t_begin >> lbs) + lane, a.max_blocks_per_seq - 1)];
-
-  // queries: column n = head hq0 + n (zero beyond the group)
-  vec8 qv[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    if (n < G) {
-      const char* qp = reinterpret_cast<const char*>(a.q) +
-                       (((int64_t)b * a.num_q_heads + hq0 + n) * D + 32 * c + 8 * j) * 2;
-      qv[c] = *reinterpret_cast<const vec8*>(qp);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) qv[c][r] = (scalar)0.0f;
-    }
-  }
-
-  const int L = clamp_len(L_in, a.max_blocks_per_seq, a.block_size);
-  if (L <= 0) {
-    if (part == 0) {
-      for (int g = 0; g < G; ++g)
-        for (int e = lane; e < D; e += 64)
-          store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
-    }
-    return;
-  }
-  const int n_parts = (L + P - 1) / P;
-  if (part >= n_parts) return;
-  const int t_end = min(t_begin + P, L);
-  const int last_blk = (L - 1) >> lbs;
-  const int64_t head_tile = (int64_t)bs * D * 2;  // bytes of one (block, head) tile
-  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
-  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
-  const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
-
-  // per-lane byte offsets from the chunk's first token quad: key token n
-  // (quad n/4, row n%4) chunk j; value quad j, dim n.  Key chunk 4c + j and
-  // value dim 16c + n add 256*c and 128*c bytes.
   constexpr int CPR = D / 8;  // 16-byte key chunks per row
-  const int koff = ((n >> 2) * CPR + j) * 64 + (n & 3) * 16;
-  const int voff = (j * D + n) * 8;
 
-  int wb = t_begin >> lbs;  // first logical block of the current block-id window
-  int bt_lane = (int)clamp_block(bt_first, a.num_blocks);  // lane i: block of wb + i
-
-  // Loads of one 16-token chunk.  Issued unconditionally, so every path
-  // through the loop has the same loads in flight and the compiler's wait
-  // counts stay exact; the prefetch past the last chunk (`none`) reads
-  // through an empty buffer range, which returns zeros without touching
-  // memory (or re-reads the last chunk where plain global loads are used).
-  auto issue = [&](Buffers<KV, D>& buf, int t0, bool none) {
-    if constexpr (UB) {
-      // one block: a buffer resource based at the chunk's key / value tile,
-      // per-lane 32-bit offsets, the 16-dim row stride as the scalar offset
-      const int phys = __builtin_amdgcn_readlane(bt_lane, min(t0 >> lbs, last_blk) - wb);
-      const int64_t first_quad = (int64_t)phys * block_stride + (int64_t)(t0 & (bs - 1)) * D * 2;
-      const int range = none ? 0 : 0x7fffffff;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + first_quad, range);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + first_quad, range);
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-        buf.k[c] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rk, koff + 256 * c, 0, kNonTemporal));
-#pragma unroll
-      for (int c = 0; c < VC; ++c)
-        buf.v[c] = __builtin_bit_cast(vec4, __builtin_amdgcn_raw_buffer_load_b64(
-                                                rv, voff + 128 * c, 0, 0));
-    } else {
-      const int tk = t0 + n;      // this lane's key token
-      const int tv = t0 + 4 * j;  // first token of this lane's value quad
-      const int pk = __shfl(bt_lane, min(tk >> lbs, last_blk) - wb);
-      const int pv = __shfl(bt_lane, min(tv >> lbs, last_blk) - wb);
-      const int ik = tk & (bs - 1), iv = tv & (bs - 1);
-      const char* kp = kc + (int64_t)pk * block_stride +
-                       (((ik >> 2) * CPR + j) * 64 + (ik & 3) * 16);
-      const char* vp = vc + (int64_t)pv * block_stride + (((iv >> 2) * D + n) * 8);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) buf.k[c] = __builtin_bit_cast(vec8, ld16_nt(kp + 256 * c));
-#pragma unroll
-      for (int c = 0; c < VC; ++c) buf.v[c] = *reinterpret_cast<const vec4*>(vp + 128 * c);
-    }
-  };
-
-  f32x4_t o[VC];
-#pragma unroll
-  for (int c = 0; c < VC; ++c) o[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY;  // running max of head n (log2 domain), uniform over j
-  float lsum = 0.0f;    // this lane's share of head n's sum
-
-  auto compute = [&](Buffers<KV, D>& buf, int t0, int t_stop) {
-    f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < KC; ++c) sacc = M::qk(buf.k[c], qv[c], sacc);
-    float s[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = sacc[r] * a.scale_log2;
-    if (t0 + kChunk > t_stop) {  // uniform: mask tokens past the partition / context
-      const int nv = t_stop - t0 - 4 * j;  // valid tokens of this lane's run
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] = r < nv ? s[r] : -INFINITY;
-#pragma unroll
-      for (int c = 0; c < VC; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (r >= nv) buf.v[c][r] = (scalar)0.0f;
-    }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
-    vec4 phi, plo;
-    float ps = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(s[r] - m_new);
-      ps += p;
-      const scalar hi = (scalar)p;
-      phi[r] = hi;
-      plo[r] = (scalar)(p - (float)hi);
-    }
-    lsum = lsum * alpha + ps;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int c = 0; c < VC; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[c][r] *= alpha;
-    }
-#pragma unroll
-    for (int c = 0; c < VC; ++c) {
-      o[c] = M::pv(buf.v[c], phi, o[c]);
-      o[c] = M::pv(buf.v[c], plo, o[c]);
-    }
-  };
-
-  // Walk the partition in windows of 64 blocks (one block id per lane); inside
-  // a window, chunk i+1 is loaded while chunk i is computed.
-  Buffers<KV, D> b0, b1;
-  const int window = 64 * bs;
-  for (int w0 = t_begin; w0 < t_end; w0 += window) {
-    const int w1 = min(w0 + window, t_end);
-    if (w0 != t_begin) {  // later windows (one-pass over long contexts)
-      wb = w0 >> lbs;
-      bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
-    }
-    const int nc = (w1 - w0 + kChunk - 1) / kChunk;
-    const int last_t0 = w0 + (nc - 1) * kChunk;
-    issue(b0, w0, false);
-    for (int i = 0; i < nc; i += 2) {
-      const int t0 = w0 + i * kChunk;
-      issue(b1, min(t0 + kChunk, last_t0), t0 + kChunk > last_t0);
-      compute(b0, t0, w1);
-      if (i + 1 >= nc) break;
-      issue(b0, min(t0 + 2 * kChunk, last_t0), t0 + 2 * kChunk > last_t0);
-      compute(b1, t0 + kChunk, w1);
-    }
+  // Work items (sequence, kv head, head chunk, partition).  With a work list
+  // (a.list_ints > 0) the grid is persistent: every workgroup builds the list
+  // of the items that hold tokens and takes every gridDim.x-th one, head
+  // chunks fastest.  Without one, each workgroup runs one item: grid.x walks
+  // (sequence, kv head, head chunk) fastest so that consecutive workgroups --
+  // which the dispatcher deals round-robin to the XCDs -- carry the same
+  // partition index of different sequences and heads, and grid.y walks the
+  // partitions from the last to the first.
+  extern __shared__ __align__(16) int dyn_lds[];
+  const bool listed = args.list_ints > 0;
+  int n_work = (int)blockIdx.x + 1, step = 1;
+  if (listed) {
+    n_work = build_work_list(args, dyn_lds) * args.num_kv_heads * (args.group / G);
+    step = (int)gridDim.x;
   }
-
-  // ---- finish the work item ------------------------------------------------
-  float l = lsum + __shfl_xor(lsum, 16);
-  l += __shfl_xor(l, 32);
-  if (n < G) {
-    const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + n;
-    if (n_parts == 1) {
-      const float inv = 1.0f / l;
-#pragma unroll
-      for (int c = 0; c < VC; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          store_elem(a.out, row_id * D + 16 * c + 4 * j + r, o[c][r] * inv, a.out_dtype);
+  // Round r takes entry r * gridDim.x + blockIdx.x, or the mirrored one on
+  // odd rounds: the list runs longest first, so a workgroup that drew a long
+  // entry in one round draws a short one in the next (a snake deal).
+  int cursor = 0;
+  const int bx = (int)blockIdx.x;
+  int round = 0, it = bx;
+  while (it < n_work) {
+    {
+    KernArgs& a = *fresh_args();
+    const int chunks = a.group / G;
+    const int per_seq = a.num_kv_heads * chunks;
+    const int W = a.waves;
+    const int tid = fresh_tid();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    float* red = reinterpret_cast<float*>(dyn_lds + a.list_ints);  // wave merge area
+    const int lbs = a.log2_block_size;
+    const int bs = a.block_size;
+    const int P = a.partition_size;
+    const int64_t head_tile = (int64_t)bs * D * 2;  // bytes of one (block, head) tile
+    const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    // per-lane byte offsets from the chunk's first token quad: key token n
+    // (quad n/4, row n%4) chunk j; value quad j, dim n.  Key chunk 4c + j and
+    // value dim 16c + n add 256*c and 128*c bytes.
+    const int koff = ((n >> 2) * CPR + j) * 64 + (n & 3) * 16;
+    const int voff = (j * D + n) * 8;
+    int b, hc, part;
+    if (listed) {
+      const int item = it / per_seq;
+      hc = it - item * per_seq;
+      work_item(dyn_lds, a.max_partitions, item, cursor, b, part);
     } else {
-      const int64_t slot = row_id * a.max_partitions + part;
-      float* dst = a.ws_acc + slot * D;
+      b = it / per_seq;
+      hc = it - b * per_seq;
+      part = (int)gridDim.y - 1 - (int)blockIdx.y;
+    }
+    const int h = hc / chunks;
+    const int hq0 = h * a.group + (hc % chunks) * G;
+
+    // Start-up loads that do not depend on the context length go out together
+    // with it: the first block-id window (clamped to the table width; entries
+    // past the sequence are never used) and the queries.
+    const int t_begin = part * P;
+    const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int L_in = a.context_lens[b];
+    const int bt_first = bt[min((t_begin >> lbs) + lane, a.max_blocks_per_seq - 1)];
+
+    // queries: column n = head hq0 + n (zero beyond the group)
+    vec8 qv[KC];
 #pragma unroll
-      for (int c = 0; c < VC; ++c)
-        *reinterpret_cast<f32x4_t*>(dst + 16 * c + 4 * j) = o[c];
-      if (j == 0) {
-        a.ws_ml[slot * 2] = m;
-        a.ws_ml[slot * 2 + 1] = l;
+    for (int c = 0; c < KC; ++c) {
+      if (n < G) {
+        const char* qp = reinterpret_cast<const char*>(a.q) +
+                         (((int64_t)b * a.num_q_heads + hq0 + n) * D + 32 * c + 8 * j) * 2;
+        qv[c] = *reinterpret_cast<const vec8*>(qp);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) qv[c][r] = (scalar)0.0f;
       }
     }
-  }
+
+    const int L = clamp_len(L_in, a.max_blocks_per_seq, a.block_size);
+    if (L <= 0) {
+      if (part == 0 && wave == 0) {
+        for (int g = 0; g < G; ++g)
+          for (int e = lane; e < D; e += 64)
+            store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
+      }
+      goto next_item;
+    }
+    const int n_parts = (L + P - 1) / P;
+    if (part >= n_parts) goto next_item;
+    const int t_end = min(t_begin + P, L);
+    const int last_blk = (L - 1) >> lbs;
+    const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
+    const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
+
+    int wb = t_begin >> lbs;  // first logical block of the current block-id window
+    int bt_lane = (int)clamp_block(bt_first, a.num_blocks);  // lane i: block of wb + i
+
+    // Loads of one 16-token chunk.  Issued unconditionally, so every path
+    // through the loop has the same loads in flight and the compiler's wait
+    // counts stay exact; the prefetch past the last chunk (`none`) reads
+    // through an empty buffer range, which returns zeros without touching
+    // memory (or re-reads the last chunk where plain global loads are used).
+    auto issue = [&](Buffers<KV, D>& buf, int t0, bool none) {
+      if constexpr (UB) {
+        // one block: a buffer resource based at the chunk's key / value tile,
+        // per-lane 32-bit offsets, the 16-dim row stride as the scalar offset
+        const int phys = __builtin_amdgcn_readlane(bt_lane, min(t0 >> lbs, last_blk) - wb);
+        const int64_t first_quad = (int64_t)phys * block_stride + (int64_t)(t0 & (bs - 1)) * D * 2;
+        const int range = none ? 0 : 0x7fffffff;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + first_quad, range);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + first_quad, range);
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          buf.k[c] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rk, koff + 256 * c, 0, kNonTemporal));
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+          buf.v[c] = __builtin_bit_cast(vec4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  rv, voff + 128 * c, 0, 0));
+      } else {
+        const int tk = t0 + n;      // this lane's key token
+        const int tv = t0 + 4 * j;  // first token of this lane's value quad
+        const int pk = __shfl(bt_lane, min(tk >> lbs, last_blk) - wb);
+        const int pv = __shfl(bt_lane, min(tv >> lbs, last_blk) - wb);
+        const int ik = tk & (bs - 1), iv = tv & (bs - 1);
+        const char* kp = kc + (int64_t)pk * block_stride +
+                         (((ik >> 2) * CPR + j) * 64 + (ik & 3) * 16);
+        const char* vp = vc + (int64_t)pv * block_stride + (((iv >> 2) * D + n) * 8);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) buf.k[c] = __builtin_bit_cast(vec8, ld16_nt(kp + 256 * c));
+#pragma unroll
+        for (int c = 0; c < VC; ++c) buf.v[c] = *reinterpret_cast<const vec4*>(vp + 128 * c);
+      }
+    };
+
+    f32x4_t o[VC];
+#pragma unroll
+    for (int c = 0; c < VC; ++c) o[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY;  // running max of head n (log2 domain), uniform over j
+    float lsum = 0.0f;    // this lane's share of head n's sum
+
+    auto compute = [&](Buffers<KV, D>& buf, int t0, int t_stop) {
+      f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) sacc = M::qk(buf.k[c], qv[c], sacc);
+      float s[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = sacc[r] * a.scale_log2;
+      if (t0 + kChunk > t_stop) {  // uniform: mask tokens past the partition / context
+        const int nv = t_stop - t0 - 4 * j;  // valid tokens of this lane's run
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] = r < nv ? s[r] : -INFINITY;
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r >= nv) buf.v[c][r] = (scalar)0.0f;
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      vec4 phi, plo;
+      float ps = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(s[r] - m_new);
+        ps += p;
+        const scalar hi = (scalar)p;
+        phi[r] = hi;
+        plo[r] = (scalar)(p - (float)hi);
+      }
+      lsum = lsum * alpha + ps;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[c][r] *= alpha;
+      }
+#pragma unroll
+      for (int c = 0; c < VC; ++c) {
+        o[c] = M::pv(buf.v[c], phi, o[c]);
+        o[c] = M::pv(buf.v[c], plo, o[c]);
+      }
+    };
+
+    // Walk the partition in windows of 64 blocks (one block id per lane); inside
+    // a window this wave takes every W-th chunk, loading its next chunk while
+    // the current one is computed.  Only the last window can hold fewer than W
+    // chunks (a full window has at least 32).
+    Buffers<KV, D> b0, b1;
+    const int window = 64 * bs;
+    const int stride = W * kChunk;
+    for (int w0 = t_begin; w0 < t_end; w0 += window) {
+      const int w1 = min(w0 + window, t_end);
+      if (w0 != t_begin) {  // later windows (one-pass over long contexts)
+        wb = w0 >> lbs;
+        bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
+      }
+      const int nc = (w1 - w0 + kChunk - 1) / kChunk;
+      if (wave >= nc) continue;
+      const int nk = (nc - wave + W - 1) / W;  // chunks of this wave
+      const int first_t0 = w0 + wave * kChunk;
+      const int last_t0 = first_t0 + (nk - 1) * stride;
+      issue(b0, first_t0, false);
+      for (int i = 0; i < nk; i += 2) {
+        const int t0 = first_t0 + i * stride;
+        issue(b1, min(t0 + stride, last_t0), t0 + stride > last_t0);
+        compute(b0, t0, w1);
+        if (i + 1 >= nk) break;
+        issue(b0, min(t0 + 2 * stride, last_t0), t0 + 2 * stride > last_t0);
+        compute(b1, t0 + stride, w1);
+      }
+    }
+
+    // ---- finish the work item ------------------------------------------------
+    float l = lsum + __shfl_xor(lsum, 16);
+    l += __shfl_xor(l, 32);
+    if (W > 1) {
+      // Merge the waves: M = max_w m_w, l = sum_w 2^(m_w - M) l_w, and the
+      // accumulators likewise.  A wave without chunks has m = -inf, l = 0 and
+      // zero accumulators; wave 0 always has a chunk, so M is finite.  Every
+      // wave parks its rescaled accumulators in LDS, then the whole workgroup
+      // sums them and stores.
+      float* red_m = red;         // [W][16]
+      float* red_l = red + 64;    // [W][16]
+      float* red_o = red + 128;   // [W][G][D + 4] (rows padded against bank conflicts)
+      constexpr int RS = D + 4;
+      if (j == 0) {
+        red_m[wave * 16 + n] = m;
+        red_l[wave * 16 + n] = l;
+      }
+      __syncthreads();
+      float M = -INFINITY;
+      for (int w = 0; w < W; ++w) M = fmaxf(M, red_m[w * 16 + n]);
+      const float sc = fast_exp2(m - M);
+      if (n < G) {
+#pragma unroll
+        for (int c = 0; c < VC; ++c) {
+          f32x4_t x = o[c];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] *= sc;
+          *reinterpret_cast<f32x4_t*>(red_o + (wave * G + n) * RS + 16 * c + 4 * j) = x;
+        }
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+        const int g = e / D, d = e - g * D;
+        float Mg = -INFINITY;
+        for (int w = 0; w < W; ++w) Mg = fmaxf(Mg, red_m[w * 16 + g]);
+        float lt = 0.0f, x = 0.0f;
+        for (int w = 0; w < W; ++w) {
+          lt += red_l[w * 16 + g] * fast_exp2(red_m[w * 16 + g] - Mg);
+          x += red_o[(w * G + g) * RS + d];
+        }
+        const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
+        if (n_parts == 1) {
+          store_elem(a.out, row_id * D + d, x / lt, a.out_dtype);
+        } else {
+          const int64_t slot = row_id * a.max_partitions + part;
+          a.ws_acc[slot * D + d] = x;
+          if (d == 0) {
+            a.ws_ml[slot * 2] = Mg;
+            a.ws_ml[slot * 2 + 1] = lt;
+          }
+        }
+      }
+      __syncthreads();  // the merge area is free for the next item
+      goto next_item;
+    }
+    if (n < G) {
+      const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + n;
+      if (n_parts == 1) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            store_elem(a.out, row_id * D + 16 * c + 4 * j + r, o[c][r] * inv, a.out_dtype);
+      } else {
+        const int64_t slot = row_id * a.max_partitions + part;
+        float* dst = a.ws_acc + slot * D;
+#pragma unroll
+        for (int c = 0; c < VC; ++c)
+          *reinterpret_cast<f32x4_t*>(dst + 16 * c + 4 * j) = o[c];
+        if (j == 0) {
+          a.ws_ml[slot * 2] = m;
+          a.ws_ml[slot * 2 + 1] = l;
+        }
+      }
+    }
+    }
+  next_item:
+    if (!listed) break;
+    ++round;
+    it = round * step + ((round & 1) ? step - 1 - bx : bx);
+  }  // work items
+}
+
+// LDS of the wave merge: m and l of 16 columns per wave, then every wave's
+// padded accumulators.
+size_t merge_lds_bytes(int waves, int heads, int head_dim) {
+  if (waves <= 1) return 0;
+  return (128 + (size_t)waves * heads * (head_dim + 4)) * sizeof(float);
 }
 
 template <Elem KV, int D>
-hipError_t dispatch_g(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+hipError_t dispatch_g(const DecodeArgs& a, int64_t items_x, hipStream_t s) {
   const bool ub = a.block_size >= 16;
+  const size_t lds = (size_t)a.list_ints * sizeof(int) +
+                     merge_lds_bytes(a.waves, a.heads_per_item, D);
+  const void* fn = nullptr;
   switch (a.heads_per_item) {
-#define PA_CASE(GG)                                                                        \
-  case GG:                                                                                 \
-    if (ub)                                                                                \
-      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, GG, true>), grid, dim3(64), 0, s, a);  \
-    else                                                                                   \
-      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, GG, false>), grid, dim3(64), 0, s, a); \
+#define PA_CASE(GG)                                                                   \
+  case GG:                                                                            \
+    fn = ub ? reinterpret_cast<const void*>(&decode_mfma_kernel<KV, D, GG, true>)     \
+            : reinterpret_cast<const void*>(&decode_mfma_kernel<KV, D, GG, false>);   \
     break;
     PA_CASE(1) PA_CASE(2) PA_CASE(4) PA_CASE(8) PA_CASE(16)
     PA_CASE(3) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(10) PA_CASE(12)
@@ -330,7 +439,7 @@ hipError_t dispatch_g(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return launch_decode_grid(fn, a, items_x, lds, s);
 }
 
 }  // namespace
@@ -345,14 +454,13 @@ bool mfma_supports_heads(int heads_per_item) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s) {
-  const int chunks = a.group / a.heads_per_item;
-  dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * chunks), (unsigned)a.max_partitions);
+  const int64_t items_x = (int64_t)a.num_seqs * a.num_kv_heads * (a.group / a.heads_per_item);
   if (kv_dtype == 2) {
-    if (head_dim == 128) return dispatch_g<Elem::BF16, 128>(a, grid, s);
-    if (head_dim == 64) return dispatch_g<Elem::BF16, 64>(a, grid, s);
+    if (head_dim == 128) return dispatch_g<Elem::BF16, 128>(a, items_x, s);
+    if (head_dim == 64) return dispatch_g<Elem::BF16, 64>(a, items_x, s);
   } else if (kv_dtype == 1) {
-    if (head_dim == 128) return dispatch_g<Elem::F16, 128>(a, grid, s);
-    if (head_dim == 64) return dispatch_g<Elem::F16, 64>(a, grid, s);
+    if (head_dim == 128) return dispatch_g<Elem::F16, 128>(a, items_x, s);
+    if (head_dim == 64) return dispatch_g<Elem::F16, 64>(a, items_x, s);
   }
   return hipErrorInvalidValue;
 }

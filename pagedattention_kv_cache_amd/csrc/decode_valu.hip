@@ -1,8 +1,10 @@
 // decode_valu.hip -- paged single-query decode attention on the vector ALUs.
 //
-// One wave (64 lanes) handles one work item: a (sequence, kv head, partition)
-// with all the query heads of that kv head's group (or a chunk of at most 8 of
-// them), so every key/value byte of the item is read from HBM once.  Tokens
+// A workgroup of 1, 2 or 4 waves handles one work item: a (sequence, kv head,
+// partition) with all the query heads of that kv head's group (or a chunk of
+// at most 8 of them), so every key/value byte of the item is read from HBM
+// once.  Wave w takes tiles w, w + W, ... with its own softmax state; the
+// waves' partial results are merged through LDS by log-sum-exp at the end.  Tokens
 // are walked in tiles of 16 through the block table ("vLLM Project Update"
 // talk, PagedAttention recap: attention over fixed-size blocks of the KV
 // cache); a partition covers partition_size tokens and long or uneven contexts
@@ -31,6 +33,7 @@
 // multiplying by zero, so unused cache slots may hold anything (even NaN).
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
+#include "work_list.hpp"
 
 namespace pa {
 namespace {
@@ -81,7 +84,7 @@ __device__ __forceinline__ uint4 buf_ld_quad<4>(__amdgpu_buffer_rsrc_t r, int vo
 }
 
 template <Elem KV, int D, int G>
-__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
   using T = Tile<KV, D>;
   constexpr int EB = T::EB;
   constexpr int EPL = 16 / EB;     // elements per 16-byte chunk
@@ -94,251 +97,352 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   static_assert(RL >= 8 && RL <= 64 && 64 % RL == 0, "row layout");
   static_assert(TPI <= SEG, "a key load instruction stays inside one block");
 
-  // grid.x walks (sequence, kv head, head chunk) fastest so that consecutive
-  // workgroups -- which the dispatcher deals round-robin to the XCDs -- carry
-  // the same partition index of different sequences and heads; grid.y walks
-  // partitions from the last to the first, so the short first partitions of
-  // short sequences are dispatched at the end.
-  const int chunks = a.group / G;
-  const int item = blockIdx.x;
-  const int per_seq = a.num_kv_heads * chunks;
-  const int b = item / per_seq;
-  const int hc = item - b * per_seq;
-  const int h = hc / chunks;
-  const int hq0 = h * a.group + (hc % chunks) * G;
-  const int part = (int)gridDim.y - 1 - (int)blockIdx.y;
-  const int lane = threadIdx.x;
-  const int c = lane % RL;    // 16-byte chunk of the key row
-  const int row = lane / RL;  // token within a key load instruction
 
-  // start-up loads that do not depend on the context length go out with it
-  const int lbs = a.log2_block_size;
-  const int bs = a.block_size;
-  const int P = a.partition_size;
-  const int t_begin = part * P;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const int L_in = a.context_lens[b];
-  const int bt_first = bt[min((t_begin >> lbs) + lane, a.max_blocks_per_seq - 1)];
+  __shared__ float p_lds_all[4][G][kTile];
 
-  // query chunk for every head of the group, widened to fp32
-  float qf[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int64_t qb = ((int64_t)b * a.num_q_heads + hq0 + g) * D + c * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[g][e] = load_elem_f32(a.q, qb + e, a.q_dtype);
+  // Work items (sequence, kv head, head chunk, partition).  With a work list
+  // (a.list_ints > 0) the grid is persistent: every workgroup builds the list
+  // of the items that hold tokens and takes every gridDim.x-th one, head
+  // chunks fastest.  Without one, each workgroup runs one item: grid.x walks
+  // (sequence, kv head, head chunk) fastest so that consecutive workgroups --
+  // which the dispatcher deals round-robin to the XCDs -- carry the same
+  // partition index of different sequences and heads, and grid.y walks the
+  // partitions from the last to the first.
+  extern __shared__ __align__(16) int dyn_lds[];
+  const bool listed = args.list_ints > 0;
+  int n_work = (int)blockIdx.x + 1, step = 1;
+  if (listed) {
+    n_work = build_work_list(args, dyn_lds) * args.num_kv_heads * (args.group / G);
+    step = (int)gridDim.x;
   }
+  // Round r takes entry r * gridDim.x + blockIdx.x, or the mirrored one on
+  // odd rounds: the list runs longest first, so a workgroup that drew a long
+  // entry in one round draws a short one in the next (a snake deal).
+  int cursor = 0;
+  const int bx = (int)blockIdx.x;
+  int round = 0, it = bx;
+  while (it < n_work) {
+    {
+    KernArgs& a = *fresh_args();
+    const int chunks = a.group / G;
+    const int per_seq = a.num_kv_heads * chunks;
+    const int W = a.waves;
+    const int tid = fresh_tid();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    float* red = reinterpret_cast<float*>(dyn_lds + a.list_ints);  // wave merge area
+    float (*p_lds)[kTile] = p_lds_all[wave];  // this wave's tile probabilities
+    const int c = lane % RL;    // 16-byte chunk of the key row
+    const int row = lane / RL;  // token within a key load instruction
+    const int lbs = a.log2_block_size;
+    const int bs = a.block_size;
+    const int P = a.partition_size;
+    const int64_t head_tile = (int64_t)bs * D * EB;  // bytes of one (block, head) tile
+    const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
 
-  const int L = clamp_len(L_in, a.max_blocks_per_seq, a.block_size);
-  if (L <= 0) {
-    if (part == 0) {
-      for (int g = 0; g < G; ++g)
-        for (int e = lane; e < D; e += 64)
-          store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
+    // per-lane byte offsets from a segment's first token quad: key chunk c of
+    // token `row` (quad row/4, row row%4); the value quad of each owned dim
+    const int koff = ((row >> 2) * RL + c) * 64 + (row & 3) * 16;
+    int voff[DPL];
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) voff[dd] = (dd * 64 + lane) * 4 * EB;
+
+    int b, hc, part;
+    if (listed) {
+      const int item = it / per_seq;
+      hc = it - item * per_seq;
+      work_item(dyn_lds, a.max_partitions, item, cursor, b, part);
+    } else {
+      b = it / per_seq;
+      hc = it - b * per_seq;
+      part = (int)gridDim.y - 1 - (int)blockIdx.y;
     }
-    return;
-  }
-  const int n_parts = (L + P - 1) / P;
-  if (part >= n_parts) return;
-  const int t_end = min(t_begin + P, L);
-  const int last_blk = (L - 1) >> lbs;
-  const int64_t head_tile = (int64_t)bs * D * EB;  // bytes of one (block, head) tile
-  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
-  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
-  const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
+    const int h = hc / chunks;
+    const int hq0 = h * a.group + (hc % chunks) * G;
 
-  // per-lane byte offsets from a segment's first token quad: key chunk c of
-  // token `row` (quad row/4, row row%4); the value quad of each owned dim
-  const int koff = ((row >> 2) * RL + c) * 64 + (row & 3) * 16;
-  int voff[DPL];
-#pragma unroll
-  for (int dd = 0; dd < DPL; ++dd) voff[dd] = (dd * 64 + lane) * 4 * EB;
+    // start-up loads that do not depend on the context length go out with it
+    const int t_begin = part * P;
+    const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int L_in = a.context_lens[b];
+    const int bt_first = bt[min((t_begin >> lbs) + lane, a.max_blocks_per_seq - 1)];
 
-  int wb = t_begin >> lbs;  // block-id window: lane i holds the block of wb + i
-  int bt_lane = (int)clamp_block(bt_first, a.num_blocks);
-
-  // Loads of one 16-token tile (two 8-token segments, each inside one block),
-  // through buffer resources based at each segment.  Always issued; the
-  // prefetch past the last tile reads through an empty range (zeros, no
-  // memory access), so the wait counts are the same on every path.
-  auto issue = [&](T& buf, int t0, bool none) {
-    const int range = none ? 0 : 0x7fffffff;
-    __amdgpu_buffer_rsrc_t rk[NSEG], rv[NSEG];
-#pragma unroll
-    for (int sgm = 0; sgm < NSEG; ++sgm) {
-      const int tok = t0 + sgm * SEG;
-      const int phys = __builtin_amdgcn_readlane(bt_lane, min(tok >> lbs, last_blk) - wb);
-      const int64_t first_quad = (int64_t)phys * block_stride + (int64_t)(tok & (bs - 1)) * D * EB;
-      rk[sgm] = make_rsrc(kc + first_quad, range);
-      rv[sgm] = make_rsrc(vc + first_quad, range);
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int sgm = (i * TPI) / SEG;
-      const int l0 = (i * TPI) % SEG;  // first token of the instruction inside the segment
-      buf.k[i] = buf_ld16(rk[sgm], koff, (l0 >> 2) * RL * 64 + (l0 & 3) * 16);
-    }
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd)
-        buf.v[qd][dd] = buf_ld_quad<EB>(rv[qd >> 1], voff[dd], (qd & 1) * D * 4 * EB);
-  };
-
-  __shared__ float p_lds[G][kTile];
-
-  float m[G], lrow[G], acc[G][DPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    lrow[g] = 0.0f;
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) acc[g][dd] = 0.0f;
-  }
-
-  auto compute = [&](T& buf, int t0, int t_stop) {
-    // ---- scores ----------------------------------------------------------
-    float s[G][NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float kf[EPL];
-      widen16<KV>(buf.k[i], kf);
-      const bool valid = (t0 + i * TPI + row) < t_stop;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float part_dot = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) part_dot = fmaf(qf[g][e], kf[e], part_dot);
-        const float dot = group_sum<RL>(part_dot);
-        s[g][i] = valid ? dot * a.scale_log2 : -INFINITY;
-      }
-    }
-
-    // ---- online softmax (wave-uniform max per head) ---------------------
+    // query chunk for every head of the group, widened to fp32
+    float qf[G][EPL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mx = s[g][0];
+      const int64_t qb = ((int64_t)b * a.num_q_heads + hq0 + g) * D + c * EPL;
 #pragma unroll
-      for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[g][i]);
-      mx = across_groups_max<RL>(mx);
-      const float m_new = fmaxf(m[g], mx);
-      const float alpha = fast_exp2(m[g] - m_new);
-      m[g] = m_new;
-      float psum = 0.0f;
+      for (int e = 0; e < EPL; ++e) qf[g][e] = load_elem_f32(a.q, qb + e, a.q_dtype);
+    }
+
+    const int L = clamp_len(L_in, a.max_blocks_per_seq, a.block_size);
+    if (L <= 0) {
+      if (part == 0 && wave == 0) {
+        for (int g = 0; g < G; ++g)
+          for (int e = lane; e < D; e += 64)
+            store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
+      }
+      goto next_item;
+    }
+    const int n_parts = (L + P - 1) / P;
+    if (part >= n_parts) goto next_item;
+    const int t_end = min(t_begin + P, L);
+    const int last_blk = (L - 1) >> lbs;
+    const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
+    const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
+
+    int wb = t_begin >> lbs;  // block-id window: lane i holds the block of wb + i
+    int bt_lane = (int)clamp_block(bt_first, a.num_blocks);
+
+    // Loads of one 16-token tile (two 8-token segments, each inside one block),
+    // through buffer resources based at each segment.  Always issued; the
+    // prefetch past the last tile reads through an empty range (zeros, no
+    // memory access), so the wait counts are the same on every path.
+    auto issue = [&](T& buf, int t0, bool none) {
+      const int range = none ? 0 : 0x7fffffff;
+      __amdgpu_buffer_rsrc_t rk[NSEG], rv[NSEG];
+#pragma unroll
+      for (int sgm = 0; sgm < NSEG; ++sgm) {
+        const int tok = t0 + sgm * SEG;
+        const int phys = __builtin_amdgcn_readlane(bt_lane, min(tok >> lbs, last_blk) - wb);
+        const int64_t first_quad =
+            (int64_t)phys * block_stride + (int64_t)(tok & (bs - 1)) * D * EB;
+        rk[sgm] = make_rsrc(kc + first_quad, range);
+        rv[sgm] = make_rsrc(vc + first_quad, range);
+      }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        s[g][i] = fast_exp2(s[g][i] - m_new);
-        psum += s[g][i];
+        const int sgm = (i * TPI) / SEG;
+        const int l0 = (i * TPI) % SEG;  // first token of the instruction inside the segment
+        buf.k[i] = buf_ld16(rk[sgm], koff, (l0 >> 2) * RL * 64 + (l0 & 3) * 16);
       }
-      lrow[g] = lrow[g] * alpha + psum;
 #pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) acc[g][dd] *= alpha;
-    }
-    __syncthreads();  // the previous tile's probabilities have been read
-    if (c == 0) {
+      for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int i = 0; i < NI; ++i) p_lds[g][i * TPI + row] = s[g][i];
-    }
-    __syncthreads();
+        for (int dd = 0; dd < DPL; ++dd)
+          buf.v[qd][dd] = buf_ld_quad<EB>(rv[qd >> 1], voff[dd], (qd & 1) * D * 4 * EB);
+    };
 
-    // ---- p . V -------------------------------------------------------------
-    const int nv = min(kTile, t_stop - t0);  // valid tokens in this tile
+    float m[G], lrow[G], acc[G][DPL];
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      lrow[g] = 0.0f;
 #pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) {
-        float vf[4];
-        widen_quad<KV>(buf.v[qd][dd], vf);
+      for (int dd = 0; dd < DPL; ++dd) acc[g][dd] = 0.0f;
+    }
+
+    auto compute = [&](T& buf, int t0, int t_stop) {
+      // ---- scores ----------------------------------------------------------
+      float s[G][NI];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = qd * 4 + r;
-          if (t < nv) {
+      for (int i = 0; i < NI; ++i) {
+        float kf[EPL];
+        widen16<KV>(buf.k[i], kf);
+        const bool valid = (t0 + i * TPI + row) < t_stop;
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(p_lds[g][t], vf[r], acc[g][dd]);
+        for (int g = 0; g < G; ++g) {
+          float part_dot = 0.0f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) part_dot = fmaf(qf[g][e], kf[e], part_dot);
+          const float dot = group_sum<RL>(part_dot);
+          s[g][i] = valid ? dot * a.scale_log2 : -INFINITY;
+        }
+      }
+
+      // ---- online softmax (wave-uniform max per head) ---------------------
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = s[g][0];
+#pragma unroll
+        for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[g][i]);
+        mx = across_groups_max<RL>(mx);
+        const float m_new = fmaxf(m[g], mx);
+        const float alpha = fast_exp2(m[g] - m_new);
+        m[g] = m_new;
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          s[g][i] = fast_exp2(s[g][i] - m_new);
+          psum += s[g][i];
+        }
+        lrow[g] = lrow[g] * alpha + psum;
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) acc[g][dd] *= alpha;
+      }
+      wave_lds_sync();  // the previous tile's probabilities have been read
+      if (c == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int i = 0; i < NI; ++i) p_lds[g][i * TPI + row] = s[g][i];
+      }
+      wave_lds_sync();
+
+      // ---- p . V -------------------------------------------------------------
+      const int nv = min(kTile, t_stop - t0);  // valid tokens in this tile
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) {
+          float vf[4];
+          widen_quad<KV>(buf.v[qd][dd], vf);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = qd * 4 + r;
+            if (t < nv) {
+#pragma unroll
+              for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(p_lds[g][t], vf[r], acc[g][dd]);
+            }
           }
         }
       }
-    }
-  };
+    };
 
-  // Walk the partition in windows of 64 blocks; inside a window, tile i+1 is
-  // loaded while tile i is computed.
-  T b0, b1;
-  const int window = 64 * bs;
-  for (int w0 = t_begin; w0 < t_end; w0 += window) {
-    const int w1 = min(w0 + window, t_end);
-    if (w0 != t_begin) {
-      wb = w0 >> lbs;
-      bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
-    }
-    const int nt = (w1 - w0 + kTile - 1) / kTile;
-    const int last_t0 = w0 + (nt - 1) * kTile;
-    issue(b0, w0, false);
-    for (int i = 0; i < nt; i += 2) {
-      const int t0 = w0 + i * kTile;
-      issue(b1, min(t0 + kTile, last_t0), t0 + kTile > last_t0);
-      compute(b0, t0, w1);
-      if (i + 1 >= nt) break;
-      issue(b0, min(t0 + 2 * kTile, last_t0), t0 + 2 * kTile > last_t0);
-      compute(b1, t0 + kTile, w1);
-    }
-  }
-
-  // ---- finish the work item ------------------------------------------------
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float l = across_groups_sum<RL>(lrow[g]);
-    const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
-    if (n_parts == 1) {
-      const float inv = 1.0f / l;
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd)
-        store_elem(a.out, row_id * D + dd * 64 + lane, acc[g][dd] * inv, a.out_dtype);
-    } else {
-      const int64_t slot = row_id * a.max_partitions + part;
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) a.ws_acc[slot * D + dd * 64 + lane] = acc[g][dd];
-      if (lane == 0) {
-        a.ws_ml[slot * 2] = m[g];
-        a.ws_ml[slot * 2 + 1] = l;
+    // Walk the partition in windows of 64 blocks; inside a window this wave
+    // takes every W-th tile, loading its next tile while the current one is
+    // computed.  Only the last window can hold fewer than W tiles.
+    T b0, b1;
+    const int window = 64 * bs;
+    const int stride = W * kTile;
+    for (int w0 = t_begin; w0 < t_end; w0 += window) {
+      const int w1 = min(w0 + window, t_end);
+      if (w0 != t_begin) {
+        wb = w0 >> lbs;
+        bt_lane = (int)clamp_block(bt[min(wb + lane, last_blk)], a.num_blocks);
+      }
+      const int nt = (w1 - w0 + kTile - 1) / kTile;
+      if (wave >= nt) continue;
+      const int nk = (nt - wave + W - 1) / W;  // tiles of this wave
+      const int first_t0 = w0 + wave * kTile;
+      const int last_t0 = first_t0 + (nk - 1) * stride;
+      issue(b0, first_t0, false);
+      for (int i = 0; i < nk; i += 2) {
+        const int t0 = first_t0 + i * stride;
+        issue(b1, min(t0 + stride, last_t0), t0 + stride > last_t0);
+        compute(b0, t0, w1);
+        if (i + 1 >= nk) break;
+        issue(b0, min(t0 + 2 * stride, last_t0), t0 + 2 * stride > last_t0);
+        compute(b1, t0 + stride, w1);
       }
     }
-  }
+
+    // ---- finish the work item ------------------------------------------------
+    float lsum[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) lsum[g] = across_groups_sum<RL>(lrow[g]);
+    if (W > 1) {
+      // Merge the waves by log-sum-exp (a wave without tiles has m = -inf,
+      // l = 0 and zero accumulators; wave 0 always has a tile): every wave
+      // parks its m, l and accumulators in LDS, then the whole workgroup
+      // rescales, sums and stores.
+      float* red_m = red;               // [W][G]
+      float* red_l = red + 4 * G;       // [W][G]
+      float* red_o = red + 8 * G;       // [W][G][D]
+      if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          red_m[wave * G + g] = m[g];
+          red_l[wave * G + g] = lsum[g];
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) red_o[(wave * G + g) * D + dd * 64 + lane] = acc[g][dd];
+      __syncthreads();
+      for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+        const int g = e / D, d = e - g * D;
+        float Mg = -INFINITY;
+        for (int w = 0; w < W; ++w) Mg = fmaxf(Mg, red_m[w * G + g]);
+        float lt = 0.0f, x = 0.0f;
+        for (int w = 0; w < W; ++w) {
+          const float sc = fast_exp2(red_m[w * G + g] - Mg);
+          lt += red_l[w * G + g] * sc;
+          x += red_o[(w * G + g) * D + d] * sc;
+        }
+        const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
+        if (n_parts == 1) {
+          store_elem(a.out, row_id * D + d, x / lt, a.out_dtype);
+        } else {
+          const int64_t slot = row_id * a.max_partitions + part;
+          a.ws_acc[slot * D + d] = x;
+          if (d == 0) {
+            a.ws_ml[slot * 2] = Mg;
+            a.ws_ml[slot * 2 + 1] = lt;
+          }
+        }
+      }
+      __syncthreads();  // the merge area is free for the next item
+      goto next_item;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float l = lsum[g];
+      const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
+      if (n_parts == 1) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd)
+          store_elem(a.out, row_id * D + dd * 64 + lane, acc[g][dd] * inv, a.out_dtype);
+      } else {
+        const int64_t slot = row_id * a.max_partitions + part;
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) a.ws_acc[slot * D + dd * 64 + lane] = acc[g][dd];
+        if (lane == 0) {
+          a.ws_ml[slot * 2] = m[g];
+          a.ws_ml[slot * 2 + 1] = l;
+        }
+      }
+    }
+    }
+  next_item:
+    if (!listed) break;
+    ++round;
+    it = round * step + ((round & 1) ? step - 1 - bx : bx);
+  }  // work items
+}
+
+// LDS of the wave merge: m and l of up to 4 waves, then every wave's
+// accumulators.
+size_t merge_lds_bytes(int waves, int heads, int head_dim) {
+  if (waves <= 1) return 0;
+  return ((size_t)8 * heads + (size_t)waves * heads * head_dim) * sizeof(float);
 }
 
 template <Elem KV, int D>
-hipError_t dispatch_g(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+hipError_t dispatch_g(const DecodeArgs& a, int64_t items_x, hipStream_t s) {
+  const size_t lds = (size_t)a.list_ints * sizeof(int) +
+                     merge_lds_bytes(a.waves, a.heads_per_item, D);
+  const void* fn = nullptr;
   switch (a.heads_per_item) {
-#define PA_CASE(GG)                                                                   \
-  case GG:                                                                            \
-    hipLaunchKernelGGL((decode_valu_kernel<KV, D, GG>), grid, dim3(64), 0, s, a);     \
+#define PA_CASE(GG)                                                       \
+  case GG:                                                                \
+    fn = reinterpret_cast<const void*>(&decode_valu_kernel<KV, D, GG>);   \
     break;
     PA_CASE(1) PA_CASE(2) PA_CASE(3) PA_CASE(4) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(8)
 #undef PA_CASE
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return launch_decode_grid(fn, a, items_x, lds, s);
 }
 
 template <Elem KV>
-hipError_t dispatch_d(const DecodeArgs& a, int head_dim, dim3 grid, hipStream_t s) {
-  if (head_dim == 64) return dispatch_g<KV, 64>(a, grid, s);
-  if (head_dim == 128) return dispatch_g<KV, 128>(a, grid, s);
+hipError_t dispatch_d(const DecodeArgs& a, int head_dim, int64_t items_x, hipStream_t s) {
+  if (head_dim == 64) return dispatch_g<KV, 64>(a, items_x, s);
+  if (head_dim == 128) return dispatch_g<KV, 128>(a, items_x, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s) {
-  const int chunks = a.group / a.heads_per_item;
-  dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * chunks), (unsigned)a.max_partitions);
+  const int64_t items_x = (int64_t)a.num_seqs * a.num_kv_heads * (a.group / a.heads_per_item);
   switch (kv_dtype) {
-    case 0: return dispatch_d<Elem::F32>(a, head_dim, grid, s);
-    case 1: return dispatch_d<Elem::F16>(a, head_dim, grid, s);
-    case 2: return dispatch_d<Elem::BF16>(a, head_dim, grid, s);
+    case 0: return dispatch_d<Elem::F32>(a, head_dim, items_x, s);
+    case 1: return dispatch_d<Elem::F16>(a, head_dim, items_x, s);
+    case 2: return dispatch_d<Elem::BF16>(a, head_dim, items_x, s);
     default: return hipErrorInvalidValue;
   }
 }

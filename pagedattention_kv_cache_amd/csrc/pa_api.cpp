@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pa.h"
 #include "pa_launch.hpp"
 
@@ -51,9 +54,21 @@ int32_t mfma_heads_per_item(int32_t g) {
 // vector-ALU kernel unless the caller forces the matrix cores.
 bool use_mfma(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t group) {
   const bool eligible = kv_dtype != PA_DTYPE_F32 && q_dtype == kv_dtype;
-  if (flags == PA_DECODE_FORCE_MFMA) return eligible;
-  if (flags == PA_DECODE_FORCE_VALU) return false;
+  const uint32_t kernel = flags & PA_DECODE_KERNEL_MASK;
+  if (kernel == PA_DECODE_FORCE_MFMA) return eligible;
+  if (kernel == PA_DECODE_FORCE_VALU) return false;
   return eligible && group >= 2;
+}
+
+// Flag bits this library knows, with a valid kernel choice.
+bool valid_flags(uint32_t flags) {
+  if (flags & ~(PA_DECODE_KERNEL_MASK | PA_DECODE_WAVES_MASK | PA_DECODE_NO_WORK_LIST))
+    return false;
+  return (flags & PA_DECODE_KERNEL_MASK) != PA_DECODE_KERNEL_MASK;
+}
+
+bool forces_mfma(uint32_t flags) {
+  return (flags & PA_DECODE_KERNEL_MASK) == PA_DECODE_FORCE_MFMA;
 }
 
 struct DecodeShape {
@@ -70,8 +85,8 @@ int check_shape(const DecodeShape& s) {
   if (s.head_dim != 64 && s.head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (!valid_block_size(s.block_size)) return PA_ERR_UNSUPPORTED;
   if ((int64_t)s.max_blocks_per_seq * s.block_size > (int64_t)1 << 30) return PA_ERR_SHAPE;
-  if (s.flags > PA_DECODE_FORCE_MFMA) return PA_ERR_UNSUPPORTED;
-  if (s.flags == PA_DECODE_FORCE_MFMA && s.kv_dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
+  if (!valid_flags(s.flags)) return PA_ERR_UNSUPPORTED;
+  if (forces_mfma(s.flags) && s.kv_dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -98,9 +113,49 @@ int64_t n_partitions(const DecodeShape& s, int32_t p) {
   return (max_ctx + p - 1) / p;
 }
 
+// Waves per work item.  An explicit PA_DECODE_WAVES_* choice wins; otherwise
+// as many (1, 2 or 4) as leave every wave at least 8 chunks of 16 tokens of
+// a full partition: splitting shortens the longest items, while a wave with
+// fewer chunks spends too much of its time starting up and merging.  Measured
+// on the MHA (partition 256: 2 waves), skewed (512: 4), GQA (1024: 4) and
+// long-context (4096: 4) 16-bit workloads, this is the best split or within
+// 1% of it.
+int32_t pick_waves(const DecodeShape& s, int32_t p) {
+  switch (s.flags & PA_DECODE_WAVES_MASK) {
+    case PA_DECODE_WAVES_1: return 1;
+    case PA_DECODE_WAVES_2: return 2;
+    case PA_DECODE_WAVES_4: return 4;
+    default: break;
+  }
+  int32_t w = 1;
+  while (w < 4 && (int64_t)p >= (int64_t)256 * w) w *= 2;
+  return w;
+}
+
+// Largest work list a workgroup builds in LDS (ints); beyond it, one
+// workgroup per possible item.
+constexpr int kMaxListInts = 4096;
+
+// Grid choice.  A persistent grid over the work list skips the items that
+// hold no tokens (one workgroup per possible item launches them all, and on
+// skewed batches most of them only read a length and exit), but deals the
+// real items statically and spends a few microseconds building the list.
+// Measured: with partitions of 512 tokens or more the list wins (skewed
+// batch +40%, long contexts +1%, GQA batch even); with 256-token partitions
+// (many short items) the hardware's dynamic dispatch of a full grid wins by
+// ~5%.  One pass never has empty items.
+int32_t work_list_ints(const DecodeShape& s, int64_t np, int32_t p) {
+  if ((s.flags & PA_DECODE_NO_WORK_LIST) || np <= 1 || p < 512) return 0;
+  const int64_t ints = pa::work_list_lds_ints(s.num_seqs, (int)np);
+  if (ints > kMaxListInts) return 0;
+  return (int32_t)((ints + 3) & ~3);  // keep the merge area 16-byte aligned
+}
+
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Workspace of a partitioned decode: (m, l) and the partial output vector per
+// (sequence, q head, partition).
 size_t workspace_bytes_for(const DecodeShape& s, int32_t p) {
   const int64_t np = n_partitions(s, p);
   if (np <= 1) return 0;
@@ -202,11 +257,52 @@ int32_t pa_decode_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t q_dt
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return PA_ERR_SHAPE;
   if (!elem_bytes(q_dtype) || !elem_bytes(kv_dtype)) return PA_ERR_DTYPE;
   if (q_dtype != kv_dtype && q_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
-  if (flags > PA_DECODE_FORCE_MFMA) return PA_ERR_UNSUPPORTED;
-  if (flags == PA_DECODE_FORCE_MFMA && (kv_dtype == PA_DTYPE_F32 || q_dtype != kv_dtype))
+  if (!valid_flags(flags)) return PA_ERR_UNSUPPORTED;
+  if (forces_mfma(flags) && (kv_dtype == PA_DTYPE_F32 || q_dtype != kv_dtype))
     return PA_ERR_UNSUPPORTED;
   return use_mfma(flags, kv_dtype, q_dtype, num_q_heads / num_kv_heads) ? PA_DECODE_FORCE_MFMA
                                                                         : PA_DECODE_FORCE_VALU;
+}
+
+namespace {
+
+// Shared validation of the plan queries; the partition size pa_decode uses in *p.
+int32_t plan_args(const DecodeShape& s, int32_t partition_size, int32_t q_dtype, int32_t* p) {
+  const int st = check_shape(s);
+  if (st != PA_OK) return st;
+  if (!elem_bytes(q_dtype)) return PA_ERR_DTYPE;
+  if (q_dtype != s.kv_dtype && q_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
+  if (forces_mfma(s.flags) && q_dtype != s.kv_dtype) return PA_ERR_UNSUPPORTED;
+  if (partition_size < 0 || (partition_size > 0 && partition_size % s.block_size))
+    return PA_ERR_SHAPE;
+  const int64_t max_ctx = (int64_t)s.max_blocks_per_seq * s.block_size;
+  *p = partition_size ? partition_size : pick_partition(s);
+  if (*p > max_ctx) *p = (int32_t)max_ctx;
+  return PA_OK;
+}
+
+}  // namespace
+
+int32_t pa_decode_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        int32_t partition_size, int32_t q_dtype, int32_t kv_dtype,
+                        uint32_t flags) {
+  DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                kv_dtype, flags};
+  int32_t p = 0;
+  const int32_t st = plan_args(s, partition_size, q_dtype, &p);
+  return st != PA_OK ? st : pick_waves(s, p);
+}
+
+int32_t pa_decode_work_list(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                            int32_t partition_size, int32_t q_dtype, int32_t kv_dtype,
+                            uint32_t flags) {
+  DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                kv_dtype, flags};
+  int32_t p = 0;
+  const int32_t st = plan_args(s, partition_size, q_dtype, &p);
+  return st != PA_OK ? st : (work_list_ints(s, n_partitions(s, p), p) > 0 ? 1 : 0);
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -241,7 +337,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (out_dtype != kv_dtype && out_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
     return PA_ERR_SHAPE;
-  if (flags == PA_DECODE_FORCE_MFMA && q_dtype != kv_dtype) return PA_ERR_UNSUPPORTED;
+  if (forces_mfma(flags) && q_dtype != kv_dtype) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
@@ -263,10 +359,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
-  a.ws_ml = need ? reinterpret_cast<float*>(workspace) : nullptr;
-  a.ws_acc = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                             round_up(rows * 2 * sizeof(float)))
-                  : nullptr;
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.ws_ml = need ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_acc = need ? reinterpret_cast<float*>(ws + round_up(rows * 2 * sizeof(float))) : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
@@ -282,6 +377,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.max_partitions = (int32_t)np;
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
+  a.waves = pick_waves(s, p);
+  a.list_ints = work_list_ints(s, np, p);
 
   hipStream_t hs = (hipStream_t)stream;
   if (phase & kPartitions) {
@@ -315,3 +412,69 @@ int pa_decode_partitions(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, 
 int pa_decode_merge(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kMerge); }
 
 }  // extern "C"
+
+namespace pa {
+
+namespace {
+
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      c <= 0)
+    c = 1;
+  if (dev >= 0 && dev < 64) cached[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+// Resident workgroups per CU of a kernel, cached per (kernel, block, LDS).
+int resident_per_cu(const void* fn, int block, size_t lds) {
+  struct Entry {
+    const void* fn;
+    int block;
+    size_t lds;
+    int occ;
+  };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int next = 0;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (const Entry& e : cache)
+      if (e.fn == fn && e.block == block && e.lds == lds) return e.occ;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, block, lds) != hipSuccess ||
+      occ <= 0)
+    occ = 1;
+  std::lock_guard<std::mutex> g(mu);
+  cache[next] = Entry{fn, block, lds, occ};
+  next = (next + 1) % 64;
+  return occ;
+}
+
+}  // namespace
+
+hipError_t launch_decode_grid(const void* kernel, const DecodeArgs& a, int64_t items_x,
+                              size_t lds, hipStream_t s) {
+  const dim3 block(64 * a.waves);
+  dim3 grid;
+  if (a.list_ints > 0) {
+    const int64_t fit = (int64_t)cu_count() * resident_per_cu(kernel, (int)block.x, lds);
+    const int64_t upper = items_x * a.max_partitions;
+    const int64_t g = fit < upper ? fit : upper;
+    grid = dim3((unsigned)(g < 0x7fffffff ? g : 0x7fffffff));
+  } else {
+    grid = dim3((unsigned)items_x, (unsigned)a.max_partitions);
+  }
+  void* args[] = {const_cast<DecodeArgs*>(&a)};
+  return hipLaunchKernel(kernel, grid, block, args, lds, s);
+}
+
+}  // namespace pa

@@ -162,6 +162,21 @@ __device__ __forceinline__ int64_t clamp_block(int32_t phys, int64_t num_blocks)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders one wave's LDS stores before its later LDS loads (and the reverse).
+// A wave's LDS operations complete in issue order, so only the compiler has
+// to be kept from moving them across this point; no other wave is waited for.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Wave index inside the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+__device__ __forceinline__ int waves_per_group() { return (int)(blockDim.x >> 6); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace pa

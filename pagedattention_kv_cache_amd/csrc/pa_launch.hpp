@@ -50,10 +50,25 @@ struct DecodeArgs {
   int32_t max_partitions;  // ceil(max_blocks_per_seq * block_size / partition_size)
   int32_t q_dtype;
   int32_t out_dtype;
+  int32_t waves;  // waves per work item (1, 2 or 4): they split its chunks
+  int32_t list_ints;  // LDS ints of the work list (persistent grid), 0: one workgroup per item
 };
 
+// LDS ints a workgroup needs for the work list of a persistent launch.
+__host__ __device__ inline int work_list_lds_ints(int num_seqs, int max_partitions) {
+  return 4 * (max_partitions + 2) + 2 * num_seqs;
+}
+
+// Launches a decode kernel: with a work list, a persistent grid of as many
+// workgroups as fit on the device at once (at most one per possible item);
+// without, grid (items_x, max_partitions).  `lds` is the dynamic LDS per
+// workgroup.
+hipError_t launch_decode_grid(const void* kernel, const DecodeArgs& a, int64_t items_x,
+                              size_t lds, hipStream_t s);
+
 // Vector-ALU decode kernel: any kv dtype, head_dim 64/128, 1..8 q heads per
-// work item.  grid = (max_partitions, num_kv_heads * head_chunks, num_seqs).
+// work item.  grid = (num_seqs * num_kv_heads * head_chunks, max_partitions),
+// a.waves waves per workgroup.
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t s);
 
 // Matrix-core decode kernel: f16/bf16 KV with q in the same dtype, head_dim

@@ -39,6 +39,7 @@ def test_library_loads_and_exports_header_symbols():
     names = _declared_functions()
     assert {"pa_cache_write", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
             "pa_decode_workspace_size", "pa_decode_partition_size", "pa_decode_kernel",
+            "pa_decode_waves", "pa_decode_work_list",
             "pa_advance_step", "pa_status_string", "pa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"libpa.so does not export {n}"
@@ -131,6 +132,8 @@ def _dec(**kw):
     (dict(P=-16), ESHAPE),
     (dict(P=24), ESHAPE),
     (dict(flags=7), EUNSUP),
+    (dict(flags=3), EUNSUP),               # both kernel bits
+    (dict(flags=32), EUNSUP),              # unknown bit
     (dict(flags=pa.FORCE_MFMA, kvd=F32, qd=F32), EUNSUP),  # matrix cores: 16-bit caches only
     (dict(flags=pa.FORCE_MFMA, qd=F32), EUNSUP),           # ... queried in the same dtype
     (dict(out=None), ENULL),
@@ -162,6 +165,33 @@ def test_kernel_family_policy():
     assert L.pa_decode_kernel(32, 8, F32, F32, pa.FORCE_MFMA) == EUNSUP
     assert L.pa_decode_kernel(30, 8, BF16, BF16, 0) == ESHAPE
     assert L.pa_decode_kernel(32, 8, F16, BF16, 0) == EDTYPE
+
+
+def test_waves_flags():
+    L = pa.lib()
+    args = (256, 32, 8, 128, 16, 512, 1024, BF16, BF16)
+    for w, flag in pa.WAVES_FLAG.items():
+        assert L.pa_decode_waves(*args, flag) == w
+        assert L.pa_decode_waves(*args, flag | pa.FORCE_VALU) == w
+    # library choice: 1, 2 or 4 waves, at least 8 16-token chunks each of a full partition
+    assert L.pa_decode_waves(*args, 0) == 4                                     # 1024 tokens
+    assert L.pa_decode_waves(*args[:6], 512, BF16, BF16, 0) == 4
+    assert L.pa_decode_waves(*args[:6], 256, BF16, BF16, 0) == 2
+    assert L.pa_decode_waves(*args[:6], 384, BF16, BF16, 0) == 2
+    assert L.pa_decode_waves(*args[:6], 128, BF16, BF16, 0) == 1
+    assert L.pa_decode_waves(4, 4, 4, 64, 16, 13, 0, F32, F32, 0) == 1          # one pass of 208
+    assert L.pa_decode_waves(*args, 32) == EUNSUP
+    assert L.pa_decode_waves(*args[:6], 24, BF16, BF16, 0) == ESHAPE  # not a block multiple
+    assert L.pa_decode_waves(*args[:7], F16, BF16, pa.WAVES_2) == EDTYPE
+    # work list: partitioned launches with partitions of 512+ tokens, unless disabled
+    assert L.pa_decode_work_list(*args, 0) == 1                                 # 1024 tokens
+    assert L.pa_decode_work_list(*args, pa.NO_WORK_LIST) == 0
+    assert L.pa_decode_work_list(*args[:6], 256, BF16, BF16, 0) == 0
+    assert L.pa_decode_work_list(*args[:6], 8192, BF16, BF16, 0) == 0           # one pass
+    assert L.pa_decode_work_list(*args, 32) == EUNSUP
+    # the waves bits leave the kernel family alone
+    assert L.pa_decode_kernel(32, 8, BF16, BF16, pa.WAVES_4) == pa.FORCE_MFMA
+    assert L.pa_decode_kernel(32, 8, BF16, BF16, pa.WAVES_4 | pa.FORCE_VALU) == pa.FORCE_VALU
 
 
 def test_partition_policy_and_workspace_size():

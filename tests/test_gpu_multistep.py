@@ -84,7 +84,7 @@ def test_multistep_graph_replays_match_eager_and_oracle(kernel):
     ws_bytes = pa.decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
                                         c.block_size, wl.max_blocks_per_seq, c.partition_size,
                                         torch.bfloat16, flags)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
 
     # eager reference run
     state = _device_state(wl)

@@ -155,6 +155,65 @@ def test_decode_parity_small(case, partition, kernel):
         _check_decode(out, ref, dtype)
 
 
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1]}-bs{c[2]}-{c[3]}x{c[4]}")
+@pytest.mark.parametrize("partition", ["one-pass", "min"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("waves", [2, 4])
+def test_decode_parity_split_waves(case, partition, kernel, waves):
+    """Several waves per work item (tokens split between them, merged on chip)."""
+    dtype, d, bs, hq, hkv, lens = case
+    if kernel == "mfma" and dtype == "f32":
+        pytest.skip("the matrix-core kernel serves 16-bit caches only")
+    max_ctx = -(-max(lens) // bs) * bs
+    p = {"one-pass": max_ctx, "min": max(bs, 16) * 2}[partition]
+    cfg = custom_config(f"dw-{dtype}", lens, hq, hkv, d, dtype, bs, seed=sum(lens) + d + 5 * bs,
+                        partition_size=p)
+    wl, gs, st, res = _run_small(cfg, flags=KERNELS[kernel] | pa.WAVES_FLAG[waves])
+    for out, ref in res:
+        assert torch.isfinite(out).all()
+        _check_decode(out, ref, dtype)
+
+
+def _decode_nan_prefilled(gs, wl, P, flags):
+    """Decode into NaN-filled out and workspace (nothing left from earlier calls)."""
+    c = wl.cfg
+    kdt = gs.kc.dtype
+    wsb = pa.decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                   c.block_size, wl.max_blocks_per_seq, P, kdt, flags)
+    ws = torch.full((max(wsb, 256) // 4,), float("nan"), device="cuda")
+    out = torch.full(gs.q[0].shape, float("nan"), device="cuda")
+    pa.decode(out, gs.q[0], gs.kc, gs.vc, gs.block_tables, gs.ctx[0], c.attn_scale(),
+              c.block_size, P, ws.view(torch.uint8), flags)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("kernel,dtype,hq,hkv", [("mfma", "bf16", 32, 8), ("valu", "f16", 16, 16)])
+@pytest.mark.parametrize("waves", [1, 2, 4])
+def test_work_list_many_items_per_workgroup(kernel, dtype, hq, hkv, waves):
+    """More sequences than a wave has lanes and several items per persistent
+    workgroup: every item is computed exactly once, bit-identical to the grid
+    with one workgroup per possible item, and within tolerance of the oracle."""
+    rng = np.random.default_rng(90 + waves)
+    lens = rng.integers(1, 2600, size=300).tolist()
+    lens[:2] = [1, 2600]
+    cfg = custom_config(f"wl-{kernel}", lens, hq, hkv, 128, dtype, 16, seed=123)
+    wl = Workload(cfg)
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    gs.write_step(0)
+    st.write_step(0)
+    flags = KERNELS[kernel] | pa.WAVES_FLAG[waves]
+    P = 512
+    assert pa.decode_work_list(cfg.num_seqs, hq, hkv, 128, 16, wl.max_blocks_per_seq, P,
+                               gs.kc.dtype, gs.kc.dtype, flags)
+    out_list = _decode_nan_prefilled(gs, wl, P, flags)
+    out_grid = _decode_nan_prefilled(gs, wl, P, flags | pa.NO_WORK_LIST)
+    assert torch.isfinite(out_list).all()
+    assert torch.equal(out_list, out_grid)
+    _check_decode(out_list, st.decode(0, threads=8), dtype)
+
+
 def test_decode_multistep_parity():
     cfg = custom_config("ms", [1, 30, 31, 32, 500], 8, 2, 128, "bf16", 32, seed=9, steps=8)
     wl, gs, st, res = _run_small(cfg)
@@ -193,13 +252,14 @@ def _single_token_state(dtype, d, bs, hq, hkv, n_seqs, seed):
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("partition", [0, 16])
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
-def test_context_length_one_returns_v_bit_exact(dtype, partition, kernel):
+@pytest.mark.parametrize("waves", [1, 4])
+def test_context_length_one_returns_v_bit_exact(dtype, partition, kernel, waves):
     if kernel == "mfma" and dtype == "f32":
         pytest.skip("the matrix-core kernel serves 16-bit caches only")
     cfg, wl = _single_token_state(dtype, 128, 16, 8, 2, 6, seed=3)
     gs = GpuState(wl)
     gs.write_step(0)
-    out = gs.decode(0, partition_size=partition, flags=KERNELS[kernel])
+    out = gs.decode(0, partition_size=partition, flags=KERNELS[kernel] | pa.WAVES_FLAG[waves])
     torch.cuda.synchronize()
     v = gs.step_v[0].float()  # [B][Hkv][d]
     expect = v.repeat_interleave(cfg.group, dim=1)
@@ -209,11 +269,12 @@ def test_context_length_one_returns_v_bit_exact(dtype, partition, kernel):
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("partition", [0, 32, "one-pass"])
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
-def test_one_hot_probe_bit_exact(dtype, partition, kernel):
-    if kernel == "mfma" and dtype == "f32":
-        pytest.skip("the matrix-core kernel serves 16-bit caches only")
+@pytest.mark.parametrize("waves", [1, 4])
+def test_one_hot_probe_bit_exact(dtype, partition, kernel, waves):
     """K = 0 except one target token whose key is c*q (scale*c*|q|^2 >= 200):
     every other weight underflows, so out == V[t*] exactly, for every t*."""
+    if kernel == "mfma" and dtype == "f32":
+        pytest.skip("the matrix-core kernel serves 16-bit caches only")
     L, d, bs, H = 96, 64, 16, 1
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
     gen = torch.Generator().manual_seed(17)
@@ -236,7 +297,7 @@ def test_one_hot_probe_bit_exact(dtype, partition, kernel):
         pa.cache_write(K.cuda(), V.cuda(), slots, kc, vc)
         out = torch.empty(1, 1, d, device="cuda")
         pa.decode(out, q.cuda(), kc, vc, bt, torch.tensor([L], dtype=torch.int32, device="cuda"),
-                  scale, bs, p, flags=KERNELS[kernel])
+                  scale, bs, p, flags=KERNELS[kernel] | pa.WAVES_FLAG[waves])
         torch.cuda.synchronize()
         assert torch.equal(out[0, 0].cpu(), V[t, 0].float()), f"t*={t}"
 
