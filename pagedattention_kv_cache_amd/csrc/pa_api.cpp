@@ -90,19 +90,19 @@ int check_shape(const DecodeShape& s) {
   return PA_OK;
 }
 
-// Partition policy for partition_size == 0: about an eighth of the longest
+// Partition policy for partition_size == 0: about a quarter of the longest
 // context the block table can hold, as a power of two in [256, 4096] tokens.
-// The longest sequence then spreads over at least ~8 work items (waves),
-// while items stay long enough to amortise their start-up (context length,
-// block-id window and first chunk are three dependent loads before a wave
-// streams) and the merge traffic stays near 1% of the KV bytes.  Measured on
-// the MHA, skewed, GQA and long-context 16-bit workloads, this lands on the
-// best of the power-of-two sizes for each.  One pass when the longest context
-// fits a partition.
+// With up to four waves per item (pick_waves) the longest sequence still
+// spreads over ~16 waves, while items stay long enough to amortise their
+// start-up (context length, block-id window and first chunk are dependent
+// loads before a wave streams) and the merge traffic stays near 1% of the KV
+// bytes.  Measured on the MHA, GQA and long-context 16-bit workloads, this
+// lands on the best power-of-two size or within 2% of it.  One pass when the
+// longest context fits a partition.
 int32_t pick_partition(const DecodeShape& s) {
   const int64_t max_ctx = (int64_t)s.max_blocks_per_seq * s.block_size;
   int64_t p = 256;
-  while (p < 4096 && p * 8 < max_ctx) p *= 2;
+  while (p < 4096 && p * 4 < max_ctx) p *= 2;
   if (p % s.block_size) p = ((p + s.block_size - 1) / s.block_size) * s.block_size;
   if (max_ctx <= p) return (int32_t)max_ctx;  // one pass
   return (int32_t)p;
@@ -137,15 +137,18 @@ int32_t pick_waves(const DecodeShape& s, int32_t p) {
 constexpr int kMaxListInts = 4096;
 
 // Grid choice.  A persistent grid over the work list skips the items that
-// hold no tokens (one workgroup per possible item launches them all, and on
-// skewed batches most of them only read a length and exit), but deals the
-// real items statically and spends a few microseconds building the list.
-// Measured: with partitions of 512 tokens or more the list wins (skewed
-// batch +40%, long contexts +1%, GQA batch even); with 256-token partitions
-// (many short items) the hardware's dynamic dispatch of a full grid wins by
-// ~5%.  One pass never has empty items.
+// hold no tokens: one workgroup per possible item launches num_seqs * heads *
+// max_partitions workgroups, and the more partitions the table allows, the
+// larger the share that only reads a length and exits.  But the list deals
+// the real items statically (workgroups run at uneven speeds, which the
+// hardware's dynamic dispatch of a full grid absorbs) and every workgroup
+// spends a few microseconds building it.  Measured: at 8 or more partitions
+// the list wins (skewed batch, 8 partitions: +38%; long contexts, 9: +1%); at
+// 4 partitions the full grid wins by 1.5-4% (MHA and GQA batches).  One pass
+// never has empty items.
 int32_t work_list_ints(const DecodeShape& s, int64_t np, int32_t p) {
-  if ((s.flags & PA_DECODE_NO_WORK_LIST) || np <= 1 || p < 512) return 0;
+  (void)p;
+  if ((s.flags & PA_DECODE_NO_WORK_LIST) || np < 8) return 0;
   const int64_t ints = pa::work_list_lds_ints(s.num_seqs, (int)np);
   if (ints > kMaxListInts) return 0;
   return (int32_t)((ints + 3) & ~3);  // keep the merge area 16-byte aligned

@@ -183,10 +183,11 @@ def test_waves_flags():
     assert L.pa_decode_waves(*args, 32) == EUNSUP
     assert L.pa_decode_waves(*args[:6], 24, BF16, BF16, 0) == ESHAPE  # not a block multiple
     assert L.pa_decode_waves(*args[:7], F16, BF16, pa.WAVES_2) == EDTYPE
-    # work list: partitioned launches with partitions of 512+ tokens, unless disabled
-    assert L.pa_decode_work_list(*args, 0) == 1                                 # 1024 tokens
+    # work list: launches with 8 or more partitions, unless disabled
+    assert L.pa_decode_work_list(*args, 0) == 1                                 # 8 of 1024
     assert L.pa_decode_work_list(*args, pa.NO_WORK_LIST) == 0
-    assert L.pa_decode_work_list(*args[:6], 256, BF16, BF16, 0) == 0
+    assert L.pa_decode_work_list(*args[:6], 2048, BF16, BF16, 0) == 0          # 4 partitions
+    assert L.pa_decode_work_list(*args[:6], 256, BF16, BF16, 0) == 1           # 32 partitions
     assert L.pa_decode_work_list(*args[:6], 8192, BF16, BF16, 0) == 0           # one pass
     assert L.pa_decode_work_list(*args, 32) == EUNSUP
     # the waves bits leave the kernel family alone
@@ -199,12 +200,13 @@ def test_partition_policy_and_workspace_size():
     # one pass when the longest context fits one partition: no workspace
     assert L.pa_decode_partition_size(4, 4, 4, 64, 16, 13, F32, 0) == 208
     assert L.pa_decode_workspace_size(4, 4, 4, 64, 16, 13, 0, F32, 0) == 0
-    # about an eighth of the longest context, a power of two in [256, 4096]
-    assert L.pa_decode_partition_size(64, 32, 32, 128, 16, 128, F16, 0) == 256     # 2048 max
-    assert L.pa_decode_partition_size(32, 40, 40, 128, 16, 256, F16, 0) == 512     # 4096 max
-    assert L.pa_decode_partition_size(256, 32, 8, 128, 16, 512, BF16, 0) == 1024   # 8192 max
+    # about a quarter of the longest context, a power of two in [256, 4096]
+    assert L.pa_decode_partition_size(64, 32, 32, 128, 16, 128, F16, 0) == 512     # 2048 max
+    assert L.pa_decode_partition_size(32, 40, 40, 128, 16, 256, F16, 0) == 1024    # 4096 max
+    assert L.pa_decode_partition_size(256, 32, 8, 128, 16, 512, BF16, 0) == 2048   # 8192 max
     assert L.pa_decode_partition_size(64, 64, 8, 128, 32, 1025, BF16, 0) == 4096   # 32800 max
     assert L.pa_decode_partition_size(1, 8, 8, 128, 16, 100000, BF16, 0) == 4096   # capped
+    assert L.pa_decode_partition_size(4, 8, 8, 128, 16, 40, BF16, 0) == 256        # 640 max
     # workspace = (m, l) and a head_dim vector per (seq, q head, partition), 256-B aligned
     B, Hq, d, MB, bs, P = 256, 32, 128, 512, 16, 512
     n_part = MB * bs // P

@@ -204,7 +204,7 @@ def test_work_list_many_items_per_workgroup(kernel, dtype, hq, hkv, waves):
     gs.write_step(0)
     st.write_step(0)
     flags = KERNELS[kernel] | pa.WAVES_FLAG[waves]
-    P = 512
+    P = 256  # 11 partitions: the persistent grid
     assert pa.decode_work_list(cfg.num_seqs, hq, hkv, 128, 16, wl.max_blocks_per_seq, P,
                                gs.kc.dtype, gs.kc.dtype, flags)
     out_list = _decode_nan_prefilled(gs, wl, P, flags)
