@@ -21,8 +21,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, F16, BF16 = 0, 1, 2
-DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
+F32, F16, BF16, FP8 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 ERRORS = {
     -1: "bad argument",
@@ -63,9 +64,15 @@ def lib():
         L.orc_cache_write.argtypes = [c_void_p, c_void_p, c_void_p, i64, i64, i64, c_void_p,
                                       c_void_p, i32, i32, i64, i32, i32]
         L.orc_decode.restype = ctypes.c_int
+        f32 = ctypes.c_float
         L.orc_decode.argtypes = [c_void_p, c_void_p, i32, c_void_p, c_void_p, i32, c_void_p,
-                                 c_void_p, i32, i32, i32, i32, i64, i32, i32, ctypes.c_float,
+                                 c_void_p, i32, i32, i32, i32, i64, i32, i32, f32, f32, f32,
                                  c_void_p, i64, i32]
+        L.orc_cache_write_fp8.restype = ctypes.c_int
+        L.orc_cache_write_fp8.argtypes = [c_void_p, c_void_p, c_void_p, i64, i64, i64, c_void_p,
+                                          c_void_p, i32, i32, i64, i32, i32, f32, f32]
+        L.orc_encode_fp8.restype = None
+        L.orc_encode_fp8.argtypes = [c_void_p, i64, c_void_p]
         L.orc_advance_step.restype = ctypes.c_int
         L.orc_advance_step.argtypes = [i32, i32, i32, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_void_p, i32]
@@ -88,14 +95,15 @@ def _raw(a: np.ndarray, dtype: str) -> np.ndarray:
     """View an array holding the raw bits of `dtype` elements (uint16 for the
     16-bit types, float32/uint32 for f32) as a C-contiguous buffer."""
     a = np.ascontiguousarray(a)
-    want = 4 if dtype == "f32" else 2
+    want = ELEM_BYTES[dtype]
     if a.dtype.itemsize != want:
         raise OracleError(f"array itemsize {a.dtype.itemsize} does not match dtype {dtype}")
     return a
 
 
 def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Decode raw element bits (uint16 for f16/bf16, uint32 for f32) to float64."""
+    """Decode raw element bits (uint8 for fp8, uint16 for f16/bf16, uint32 for f32)
+    to float64."""
     bits = _raw(bits, dtype)
     out = np.empty(bits.size, dtype=np.float64)
     lib().orc_decode_bits(_ptr(bits), DTYPE_CODES[dtype], bits.size, _ptr(out))
@@ -127,10 +135,44 @@ def cache_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, k_cache:
                                  DTYPE_CODES[dtype]))
 
 
+def encode_fp8(y: np.ndarray) -> np.ndarray:
+    """float32 values -> E4M3 bit patterns (uint8): nearest, ties even, saturating."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().orc_encode_fp8(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def cache_write_fp8(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
+                    k_cache: np.ndarray, v_cache: np.ndarray, src_dtype: str, k_scale: float,
+                    v_scale: float) -> None:
+    """In-place quantizing write into E4M3 caches (uint8 arrays):
+    k_cache [NB][Hkv][bs/4][d/16][4][16], v_cache [NB][Hkv][bs/4][d][4]."""
+    k = _raw(k, src_dtype)
+    v = _raw(v, src_dtype)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    if k_cache.dtype != np.uint8 or v_cache.dtype != np.uint8:
+        raise OracleError("E4M3 caches are uint8 arrays")
+    if not (k_cache.flags.c_contiguous and v_cache.flags.c_contiguous):
+        raise OracleError("caches must be C-contiguous")
+    NB, Hkv, nq, dx, four, X = k_cache.shape
+    d, bs = dx * X, nq * 4
+    if X != 16 or four != 4 or v_cache.shape != (NB, Hkv, nq, d, 4):
+        raise OracleError("cache shapes are not the E4M3 quad layout")
+    T = slots.shape[0]
+    if k.size != T * Hkv * d or v.size != T * Hkv * d:
+        raise OracleError("k/v size does not match slot_mapping")
+    _check(lib().orc_cache_write_fp8(_ptr(k), _ptr(v), _ptr(slots), T, Hkv * d, Hkv * d,
+                                     _ptr(k_cache), _ptr(v_cache), Hkv, d, NB, bs,
+                                     DTYPE_CODES[src_dtype], float(k_scale), float(v_scale)))
+
+
 def decode(q: np.ndarray, q_dtype: str, k_cache: np.ndarray, v_cache: np.ndarray,
            kv_dtype: str, block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
-           rows: np.ndarray | None = None, threads: int = 1) -> np.ndarray:
-    """ORC-D: float64 [B][Hq][d] attention output (rows not requested stay NaN)."""
+           rows: np.ndarray | None = None, threads: int = 1, k_scale: float = 1.0,
+           v_scale: float = 1.0) -> np.ndarray:
+    """ORC-D: float64 [B][Hq][d] attention output (rows not requested stay NaN).
+    Cache elements are the stored values times k_scale / v_scale."""
     q = _raw(q, q_dtype)
     B, Hq, d = q.shape
     NB, Hkv, nq, dx, four, X = k_cache.shape
@@ -146,7 +188,8 @@ def decode(q: np.ndarray, q_dtype: str, k_cache: np.ndarray, v_cache: np.ndarray
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     _check(lib().orc_decode(_ptr(out), _ptr(q), DTYPE_CODES[q_dtype], _ptr(k_cache),
                             _ptr(v_cache), DTYPE_CODES[kv_dtype], _ptr(bt), _ptr(cl), B, Hq, Hkv,
-                            d, NB, bs, MB, float(scale), None if r is None else _ptr(r),
+                            d, NB, bs, MB, float(scale), float(k_scale), float(v_scale),
+                            None if r is None else _ptr(r),
                             0 if r is None else r.size, int(threads)))
     return out
 

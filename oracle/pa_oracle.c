@@ -31,15 +31,18 @@
  *               (value element e of offset o: quad o/4, dim e, row o%4)
  *   slot s -> block s / block_size, offset s % block_size.
  *
- * Every floating-point step is done in double precision.  Half and bfloat16
- * inputs are decoded from their bit patterns by the IEEE-754 / bfloat16
- * definitions (sign, biased exponent, significand), not by any hardware
- * conversion.  The softmax is the two-pass form: max, then exp/sum, so its
+ * Every floating-point step is done in double precision.  Half, bfloat16 and
+ * E4M3 inputs are decoded from their bit patterns by their definitions (sign,
+ * biased exponent, significand), not by any hardware conversion; E4M3 caches
+ * carry one scale per tensor (stored value * scale = cache element).  The softmax is the two-pass form: max, then exp/sum, so its
  * arithmetic differs on purpose from an online (streaming) softmax.
  *
  * Parity pins (tests/test_oracle.py): contiguous brute force in numpy, the
  * half/bfloat16 decoders against numpy/torch over all 65536 patterns, a
- * hand-worked cache-write layout fixture, block-permutation and block-size
+ * E4M3 decoder (all 256 patterns) and encoder (random values, the format's
+ * ties, subnormals and saturation) against torch's float8_e4m3fn and the
+ * format's definition, hand-worked cache-write layout fixtures (16-bit, fp32
+ * and E4M3 with scales), block-permutation and block-size
  * invariance, L=1 -> V, identical keys -> mean(V), one-hot probe -> V[t*],
  * scale 0 -> mean(V), GQA == replicated MHA; the advance step against a
  * hand-worked table and against the seeded generator's own slot arithmetic.
@@ -54,6 +57,7 @@
 #define ORC_F32 0
 #define ORC_F16 1
 #define ORC_BF16 2
+#define ORC_FP8 3 /* 8-bit float, OCP E4M3 (cache storage only) */
 
 #define ORC_OK 0
 #define ORC_ERR_ARG -1
@@ -113,10 +117,58 @@ double orc_f32_bits_to_double(uint32_t f) {
   return sign ? -v : v;
 }
 
+/* OCP 8-bit floating point, E4M3 variant: 1 sign, 4 exponent (bias 7) and 3
+ * significand bits; no infinities; the patterns S.1111.111 are NaN, so the
+ * largest finite magnitude is 1.75 * 2^8 = 448; exponent field 0 holds the
+ * subnormals man * 2^-9. */
+double orc_fp8_e4m3_bits_to_double(uint8_t c) {
+  int sign = (c >> 7) & 1;
+  int expo = (c >> 3) & 0xf;
+  int man = c & 0x7;
+  double v;
+  if (expo == 15 && man == 7) {
+    v = NAN;
+  } else if (expo == 0) {
+    v = ldexp((double)man, -9);
+  } else {
+    v = ldexp((double)(man + 8), expo - 10); /* (1.man) * 2^(expo-7) */
+  }
+  return sign ? -v : v;
+}
+
+/* A float as E4M3: the representable value nearest to y, ties to the even
+ * significand; magnitudes beyond 448 (infinities included) give +-448
+ * (saturation); NaN gives the NaN pattern with y's sign. */
+uint8_t orc_fp8_e4m3_from_float(float y) {
+  const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  if (isnan(y)) return sign | 0x7f;
+  const double a = fabs((double)y);
+  if (a >= 448.0) return sign | 0x7e;
+  /* spacing of the representable magnitudes around a */
+  double spacing;
+  if (a < ldexp(1.0, -6)) {
+    spacing = ldexp(1.0, -9);
+  } else {
+    int e2;
+    frexp(a, &e2); /* a = f * 2^e2 with f in [0.5, 1), so 2^(e2-1) <= a */
+    spacing = ldexp(1.0, e2 - 1 - 3);
+  }
+  const double n = nearbyint(a / spacing); /* default rounding: nearest, ties even */
+  const double r = n * spacing;
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, -6)) return sign | (uint8_t)n; /* subnormal: significand n */
+  int e2;
+  const double f = frexp(r, &e2); /* r = (2f) * 2^(e2-1), 2f in [1, 2) */
+  const int expo = e2 - 1 + 7;
+  const int man = (int)((2.0 * f - 1.0) * 8.0);
+  return sign | (uint8_t)(expo << 3) | (uint8_t)man;
+}
+
 /* 65536-entry decode tables, each entry produced by the decoder above; they
  * only save the repeated ldexp calls on large inputs. */
 static double g_f16_table[65536];
 static double g_bf16_table[65536];
+static double g_fp8_table[256];
 static pthread_once_t g_tables_once = PTHREAD_ONCE_INIT;
 
 static void orc_fill_tables(void) {
@@ -124,6 +176,7 @@ static void orc_fill_tables(void) {
     g_f16_table[i] = orc_f16_bits_to_double((uint16_t)i);
     g_bf16_table[i] = orc_bf16_bits_to_double((uint16_t)i);
   }
+  for (uint32_t i = 0; i < 256; ++i) g_fp8_table[i] = orc_fp8_e4m3_bits_to_double((uint8_t)i);
 }
 
 static int orc_elem_bytes(int dtype) {
@@ -131,6 +184,7 @@ static int orc_elem_bytes(int dtype) {
     case ORC_F32: return 4;
     case ORC_F16: return 2;
     case ORC_BF16: return 2;
+    case ORC_FP8: return 1;
     default: return 0;
   }
 }
@@ -142,6 +196,7 @@ static double orc_load(const void* base, int dtype, int64_t idx) {
     memcpy(&bits, (const char*)base + idx * 4, 4);
     return orc_f32_bits_to_double(bits);
   }
+  if (dtype == ORC_FP8) return g_fp8_table[((const uint8_t*)base)[idx]];
   uint16_t bits;
   memcpy(&bits, (const char*)base + idx * 2, 2);
   return dtype == ORC_F16 ? g_f16_table[bits] : g_bf16_table[bits];
@@ -187,6 +242,47 @@ int orc_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
   return ORC_OK;
 }
 
+/*
+ * The same write into E4M3 caches with per-tensor scales ("vLLM Project
+ * Update" talk, quantization update: the engine keeps the KV cache in 8-bit
+ * floating point; the talk fixes no format or scaling, the reading taken here
+ * is OCP E4M3 with one scale per cache tensor): every element x of k (v),
+ * read as src_dtype, is stored as e4m3(float(x / k_scale)), the quotient
+ * rounded once to float and then to E4M3 as orc_fp8_e4m3_from_float does.
+ * The caches use the layout above with X = 16.
+ */
+int orc_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                        int64_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
+                        uint8_t* k_cache, uint8_t* v_cache, int32_t num_kv_heads,
+                        int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                        int32_t src_dtype, float k_scale, float v_scale) {
+  if (!orc_elem_bytes(src_dtype) || src_dtype == ORC_FP8 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || num_blocks <= 0 || num_tokens < 0 ||
+      head_dim % 16 != 0 || block_size % 4 != 0 || !(k_scale > 0.0f) || !(v_scale > 0.0f))
+    return ORC_ERR_ARG;
+  pthread_once(&g_tables_once, orc_fill_tables);
+  const int64_t H = num_kv_heads, D = head_dim, BS = block_size, X = 16;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    if (slot >= num_blocks * BS) return ORC_ERR_SLOT;
+    int64_t blk = slot / BS;
+    int64_t off = slot % BS;
+    for (int64_t h = 0; h < H; ++h) {
+      for (int64_t e = 0; e < D; ++e) {
+        double xk = orc_load(k, src_dtype, i * k_token_stride + h * D + e);
+        double xv = orc_load(v, src_dtype, i * v_token_stride + h * D + e);
+        int64_t quad = (blk * H + h) * (BS / 4) + off / 4;
+        k_cache[((quad * (D / X) + e / X) * 4 + off % 4) * X + e % X] =
+            orc_fp8_e4m3_from_float((float)(xk / (double)k_scale));
+        v_cache[(quad * D + e) * 4 + off % 4] =
+            orc_fp8_e4m3_from_float((float)(xv / (double)v_scale));
+      }
+    }
+  }
+  return ORC_OK;
+}
+
 /* ---- decode attention --------------------------------------------------- */
 
 typedef struct {
@@ -202,6 +298,7 @@ typedef struct {
   int64_t num_blocks;
   int32_t block_size, max_blocks_per_seq;
   double scale;
+  double k_scale, v_scale; /* cache element = stored value * scale */
   const int64_t* rows; /* b*num_q_heads + hq, or NULL for all rows */
   int64_t n_rows;
   int32_t n_threads;
@@ -247,7 +344,8 @@ static int orc_decode_row(const orc_decode_job* J, int64_t row) {
     double dot = 0.0;
     for (int64_t e = 0; e < D; ++e)
       dot += orc_load(J->q, J->q_dtype, (b * Hq + hq) * D + e) *
-             orc_load(J->k_cache, J->kv_dtype, ((quad * (D / X) + e / X) * 4 + o % 4) * X + e % X);
+             (orc_load(J->k_cache, J->kv_dtype, ((quad * (D / X) + e / X) * 4 + o % 4) * X + e % X) *
+              J->k_scale);
     s[t] = J->scale * dot;
   }
 
@@ -269,7 +367,7 @@ static int orc_decode_row(const orc_decode_job* J, int64_t row) {
     int64_t quad = (phys * Hkv + hk) * (BS / 4) + o / 4;
     for (int64_t e = 0; e < D; ++e) {
       int64_t vidx = (quad * D + e) * 4 + o % 4;
-      acc[e] += s[t] * orc_load(J->v_cache, J->kv_dtype, vidx);
+      acc[e] += s[t] * (orc_load(J->v_cache, J->kv_dtype, vidx) * J->v_scale);
     }
   }
   for (int64_t e = 0; e < D; ++e) J->out[row * D + e] = acc[e] / z;
@@ -304,9 +402,10 @@ int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
                const int32_t* block_tables, const int32_t* context_lens,
                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                int32_t head_dim, int64_t num_blocks, int32_t block_size,
-               int32_t max_blocks_per_seq, float scale, const int64_t* rows,
-               int64_t n_rows, int32_t n_threads) {
-  if (!orc_elem_bytes(q_dtype) || !orc_elem_bytes(kv_dtype)) return ORC_ERR_ARG;
+               int32_t max_blocks_per_seq, float scale, float k_scale, float v_scale,
+               const int64_t* rows, int64_t n_rows, int32_t n_threads) {
+  if (!orc_elem_bytes(q_dtype) || q_dtype == ORC_FP8 || !orc_elem_bytes(kv_dtype))
+    return ORC_ERR_ARG;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size % 4 != 0 ||
@@ -341,6 +440,8 @@ int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
     J->block_size = block_size;
     J->max_blocks_per_seq = max_blocks_per_seq;
     J->scale = (double)scale;
+    J->k_scale = (double)k_scale;
+    J->v_scale = (double)v_scale;
     J->rows = rows;
     J->n_rows = n_rows;
     J->n_threads = n_threads;
@@ -399,6 +500,11 @@ int orc_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
     slot_mapping[i] = slot;
   }
   return ORC_OK;
+}
+
+/* Encoder exposed in bulk for the pins: out[i] = e4m3(y[i]). */
+void orc_encode_fp8(const float* y, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_e4m3_from_float(y[i]);
 }
 
 /* Decoders exposed in bulk for the pins: out[i] = decode(bits[i]). */

@@ -450,3 +450,110 @@ def test_advance_step_matches_generator_slots():
         oracle.advance_step(7, 16, st["input_tokens"], sampled[s], st["input_positions"],
                             st["seq_lens"], st["slot_mapping"], wl.block_tables)
         assert np.array_equal(st["input_tokens"], sampled[s])
+
+# ------------------------------------------------------------------ E4M3 (8-bit float) caches
+
+def test_fp8_decoder_all_codes_match_torch():
+    """All 256 E4M3 patterns decode to torch's float8_e4m3fn values (NaN where it has NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode_bits(codes, "fp8")
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_fp8_encoder_matches_torch_in_range():
+    """Inside the finite range (|y| < 448) the encoder agrees with torch's conversion on
+    random magnitudes over the whole exponent range and on every midpoint of the grid."""
+    rng = np.random.default_rng(8)
+    mag = np.exp2(rng.uniform(-13, np.log2(447.9), 100000)).astype(np.float32)
+    y = mag * rng.choice(np.array([-1, 1], np.float32), mag.size)
+    grid = np.unique(np.abs(oracle.decode_bits(np.arange(127, dtype=np.uint8), "fp8")))
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    y = np.concatenate([y, mids, -mids, grid.astype(np.float32)])
+    y = y[np.abs(y) < 448]
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode_fp8(y), ref)
+
+
+@pytest.mark.parametrize("y,code", [
+    (0.0, 0x00), (-0.0, 0x80), (448.0, 0x7E), (-448.0, 0xFE),
+    (449.0, 0x7E), (464.0, 0x7E), (1e6, 0x7E), (float("inf"), 0x7E), (float("-inf"), 0xFE),
+    (2.0 ** -9, 0x01), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (5 * 2.0 ** -10, 0x02),
+    (7 * 2.0 ** -10, 0x04), (15 * 2.0 ** -10, 0x08), (1.0625, 0x38), (1.1875, 0x3A),
+    (240.0, 0x77), (256.0, 0x78), (-0.001, 0x80 | 0x01),
+])
+def test_fp8_encoder_definition_cases(y, code):
+    """Ties to even (normal and subnormal), the subnormal/normal boundary, signed zero and
+    saturation of everything beyond 448, infinities included."""
+    assert int(oracle.encode_fp8(np.array([y], np.float32))[0]) == code
+
+
+def test_fp8_encoder_nan_keeps_sign():
+    y = np.array([np.nan, -np.nan], np.float32)
+    assert oracle.encode_fp8(y).tolist() == [0x7F, 0xFF]
+
+
+def _fp8_fixture():
+    rows = []
+    scales = None
+    for line in open(os.path.join(GOLDEN, "cache_write_fp8.txt")):
+        f = line.split()
+        if not f or f[0] == "#":
+            continue
+        if f[0] == "scales":
+            scales = (float(f[1]), float(f[2]))
+        else:
+            rows.append((int(f[1]), float(f[2]), int(f[4], 16), float(f[5]), int(f[7], 16)))
+    return scales, rows
+
+
+def test_fp8_cache_write_hand_worked_fixture():
+    (ks, vs), rows = _fp8_fixture()
+    k = np.zeros((2, 1, 16), np.float32)
+    v = np.zeros((2, 1, 16), np.float32)
+    for e, kv, _, vv, _ in rows:
+        k[0, 0, e] = kv
+        v[0, 0, e] = vv
+    k[1] = 7.0  # padding token (slot -1)
+    v[1] = 7.0
+    kb = raw_bits(torch.from_numpy(k).to(torch.bfloat16))
+    vb = raw_bits(torch.from_numpy(v).to(torch.bfloat16))
+    assert np.array_equal(torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).float().numpy(), k)
+    kc = np.full((2, 1, 1, 1, 4, 16), 0x55, np.uint8)
+    vc = np.full((2, 1, 1, 16, 4), 0x55, np.uint8)
+    oracle.cache_write_fp8(kb, vb, np.array([6, -1], np.int64), kc, vc, "bf16", ks, vs)
+    ek = np.full(128, 0x55, np.uint8)
+    ev = np.full(128, 0x55, np.uint8)
+    for e, _, kcode, _, vcode in rows:
+        ek[96 + e] = kcode
+        ev[66 + 4 * e] = vcode
+    assert np.array_equal(kc.reshape(-1), ek)
+    assert np.array_equal(vc.reshape(-1), ev)
+
+
+def test_fp8_decode_equals_decode_of_dequantized_f32_caches():
+    """Decoding E4M3 caches with scales equals decoding f32 caches that hold
+    code value * scale (exact for power-of-two scales): same doubles, same result."""
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, d, bs, NB = 3, 4, 2, 32, 8, 20
+    lens = np.array([1, 17, 40], np.int32)
+    MB = 5
+    bt = rng.permutation(NB)[:B * MB].reshape(B, MB).astype(np.int32)
+    codes_k = rng.integers(0, 256, size=(NB, Hkv, bs // 4, d // 16, 4, 16), dtype=np.uint8)
+    codes_v = rng.integers(0, 256, size=(NB, Hkv, bs // 4, d, 4), dtype=np.uint8)
+    codes_k[(codes_k & 0x7F) == 0x7F] = 0x3C  # no NaN patterns in the context
+    codes_v[(codes_v & 0x7F) == 0x7F] = 0x3C
+    ks, vs = 0.25, 8.0
+    fk = (oracle.decode_bits(codes_k, "fp8") * ks).astype(np.float32)
+    fv = (oracle.decode_bits(codes_v, "fp8") * vs).astype(np.float32)
+    kc32 = np.ascontiguousarray(fk.reshape(NB, Hkv, bs // 4, d // 16, 4, 4, 4)
+                                .transpose(0, 1, 2, 3, 5, 4, 6)
+                                .reshape(NB, Hkv, bs // 4, d // 4, 4, 4)).view(np.uint32)
+    vc32 = np.ascontiguousarray(fv).view(np.uint32)
+    q = raw_bits(torch.randn(B, Hq, d, generator=torch.Generator().manual_seed(3)))
+    ref = oracle.decode(q, "f32", kc32, vc32, "f32", bt, lens, 0.125)
+    got = oracle.decode(q, "f32", codes_k, codes_v, "fp8", bt, lens, 0.125, k_scale=ks, v_scale=vs)
+    assert np.array_equal(got, ref)
+
