@@ -62,6 +62,8 @@ def parse_args(argv=None):
     ap.add_argument("--flags", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--waves", type=int, choices=[0, 1, 2, 4], default=0,
                     help="waves per decode work item (0: library picks)")
+    ap.add_argument("--kv-cache", choices=["native", "fp8"], default="native",
+                    help="fp8: the workload's E4M3-cache variant (workloads 4 and 5)")
     ap.add_argument("--no-work-list", action="store_true",
                     help="one workgroup per possible decode item instead of the persistent grid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,6 +137,34 @@ def summarize_pmc(args):
 
 # ----------------------------------------------------------------------------- benchmark
 
+def write_kv(c, k, v, slots, kc, vc):
+    """The library's cache write for the workload's cache dtype."""
+    import pagedattention_kv_cache_amd as pa
+    if c.kv_dtype == "fp8":
+        pa.cache_write_fp8(k, v, slots, kc, vc, *c.fp8_scales)
+    else:
+        pa.cache_write(k, v, slots, kc, vc)
+
+
+def decode_partitions_kv(c, out, q, kc, vc, bt, lens, part, ws, flags):
+    """Phase 1 of the library's decode for the workload's cache dtype."""
+    import pagedattention_kv_cache_amd as pa
+    if c.kv_dtype == "fp8":
+        pa.decode_fp8_partitions(out, q, kc, vc, bt, lens, c.attn_scale(), *c.fp8_scales,
+                                 c.block_size, part, ws, flags)
+    else:
+        pa.decode_partitions(out, q, kc, vc, bt, lens, c.attn_scale(), c.block_size, part, ws,
+                             flags)
+
+
+def oracle_write(c, k, v, slots, okc, ovc):
+    import oracle
+    if c.kv_dtype == "fp8":
+        oracle.cache_write_fp8(k, v, slots, okc, ovc, c.dtype, *c.fp8_scales)
+    else:
+        oracle.cache_write(k, v, slots, okc, ovc, c.dtype)
+
+
 def fill_caches(wl, dev, kc, vc, oracle_caches=None):
     import torch
 
@@ -146,11 +176,9 @@ def fill_caches(wl, dev, kc, vc, oracle_caches=None):
         if k.shape[0] == 0:
             continue
         slots = wl.prior_slots(b)
-        pa.cache_write(k.to(dev), v.to(dev), torch.from_numpy(slots).to(dev), kc, vc)
+        write_kv(c, k.to(dev), v.to(dev), torch.from_numpy(slots).to(dev), kc, vc)
         if oracle_caches is not None:
-            import oracle
-            oracle.cache_write(raw_bits(k), raw_bits(v), slots, oracle_caches[0], oracle_caches[1],
-                               c.dtype)
+            oracle_write(c, raw_bits(k), raw_bits(v), slots, oracle_caches[0], oracle_caches[1])
 
 
 def cpu_baseline(wl, okc, ovc, threads):
@@ -168,9 +196,10 @@ def cpu_baseline(wl, okc, ovc, threads):
     t_start = time.perf_counter()
     while len(times) < 2 or (time.perf_counter() - t_start < 10.0 and len(times) < 10):
         t0 = time.perf_counter()
-        oracle.cache_write(raw_bits(sk[0]), raw_bits(sv[0]), slots, okc, ovc, c.dtype)
-        oracle.decode(q, c.dtype, okc, ovc, c.dtype, wl.block_tables, wl.context_lens(0),
-                      c.attn_scale(), threads=threads)
+        oracle_write(c, raw_bits(sk[0]), raw_bits(sv[0]), slots, okc, ovc)
+        ks, vs = c.fp8_scales if c.kv_dtype == "fp8" else (1.0, 1.0)
+        oracle.decode(q, c.dtype, okc, ovc, c.kv_dtype, wl.block_tables, wl.context_lens(0),
+                      c.attn_scale(), threads=threads, k_scale=ks, v_scale=vs)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     kv = wl.kv_bytes(0)
@@ -202,9 +231,8 @@ def graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags) -> dic
 
     def steps(k_l, v_l):
         for s in range(c.steps):
-            pa.cache_write(sk[s], sv[s], state["slot_mapping"], k_l, v_l)
-            pa.decode_partitions(out, qs[s], k_l, v_l, bt, state["seq_lens"], scale, c.block_size,
-                                 part, ws, flags)
+            write_kv(c, sk[s], sv[s], state["slot_mapping"], k_l, v_l)
+            decode_partitions_kv(c, out, qs[s], k_l, v_l, bt, state["seq_lens"], part, ws, flags)
             pa.decode_merge(out, qs[s], k_l, v_l, bt, state["seq_lens"], scale, c.block_size,
                             part, ws, flags)
             pa.advance_step(c.num_seqs, c.block_size, state["input_tokens"], sampled[s],
@@ -287,7 +315,8 @@ def run(args):
     import torch
 
     import pagedattention_kv_cache_amd as pa
-    from pagedattention_kv_cache_amd.workloads import CONFIGS, DTYPE_TORCH, Workload
+    from pagedattention_kv_cache_amd.workloads import (CONFIGS, DTYPE_TORCH, FP8_CONFIGS,
+                                                       Workload)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -300,7 +329,14 @@ def run(args):
         sys.exit(1)
     pa.lib()
     dev = torch.device("cuda:0")
-    cfg = CONFIGS[args.workload]
+    if args.kv_cache == "fp8":
+        if args.workload not in FP8_CONFIGS:
+            print(json.dumps({"error": f"no E4M3-cache variant of workload {args.workload}; "
+                              f"have {sorted(FP8_CONFIGS)}"}))
+            sys.exit(2)
+        cfg = FP8_CONFIGS[args.workload]
+    else:
+        cfg = CONFIGS[args.workload]
     wl = Workload(cfg)
     c = cfg
     flags = {"auto": pa.AUTO, "valu": pa.FORCE_VALU, "mfma": pa.FORCE_MFMA}[args.flags]
@@ -318,7 +354,8 @@ def run(args):
         torch.cuda.synchronize()
         del src, dst
 
-    kdt = DTYPE_TORCH[c.dtype]
+    qdt = DTYPE_TORCH[c.dtype]
+    kdt = DTYPE_TORCH[c.kv_dtype]
     kc = torch.empty(pa.key_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size,
                                         kdt), dtype=kdt, device=dev)
     vc = torch.empty(pa.value_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim,
@@ -329,9 +366,9 @@ def run(args):
         import oracle
         from pagedattention_kv_cache_amd.workloads import POISON_BITS
         oracle.build(force=False)
-        bits = np.uint32 if c.dtype == "f32" else np.uint16
-        okc = np.full(tuple(kc.shape), POISON_BITS[c.dtype], bits)
-        ovc = np.full(tuple(vc.shape), POISON_BITS[c.dtype], bits)
+        bits = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}[c.kv_dtype]
+        okc = np.full(tuple(kc.shape), POISON_BITS[c.kv_dtype], bits)
+        ovc = np.full(tuple(vc.shape), POISON_BITS[c.kv_dtype], bits)
     t_fill = time.perf_counter()
     fill_caches(wl, dev, kc, vc, (okc, ovc) if want_cpu else None)
     # further layers: device copies of the first one (same values, own memory)
@@ -366,11 +403,10 @@ def run(args):
         k_l, v_l = kcs[i % n_layers], vcs[i % n_layers]
         if ev is not None:
             ev[0].record(stream)
-        pa.cache_write(sk[s], sv[s], slots[s], k_l, v_l)
+        write_kv(c, sk[s], sv[s], slots[s], k_l, v_l)
         if ev is not None:
             ev[1].record(stream)
-        pa.decode_partitions(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
-                             flags)
+        decode_partitions_kv(c, out, qs[s], k_l, v_l, bt, ctx[s], part, ws, flags)
         if ev is not None:
             ev[2].record(stream)
         pa.decode_merge(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws, flags)
@@ -407,7 +443,7 @@ def run(args):
         if rec.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("traffic_bytes")
 
-    kname = f"decode_{pa.decode_kernel(c.num_q_heads, c.num_kv_heads, kdt, kdt, flags)}_kernel"
+    kname = f"decode_{pa.decode_kernel(c.num_q_heads, c.num_kv_heads, qdt, kdt, flags)}_kernel"
     result = {
         "metric": "paged decode attention: achieved KV HBM GB/s (% peak) + tokens/s, 1 MI355X",
         "value": round(value, 2),
@@ -426,11 +462,11 @@ def run(args):
                    "partition_size": int(p_eff), "kernel_flags": args.flags,
                    "work_list": pa.decode_work_list(c.num_seqs, c.num_q_heads, c.num_kv_heads,
                                                     c.head_dim, c.block_size,
-                                                    wl.max_blocks_per_seq, int(p_eff), kdt, kdt,
+                                                    wl.max_blocks_per_seq, int(p_eff), qdt, kdt,
                                                     flags),
                    "waves_per_item": pa.decode_waves(c.num_seqs, c.num_q_heads, c.num_kv_heads,
                                                      c.head_dim, c.block_size,
-                                                     wl.max_blocks_per_seq, int(p_eff), kdt, kdt,
+                                                     wl.max_blocks_per_seq, int(p_eff), qdt, kdt,
                                                      flags)},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1),

@@ -59,9 +59,12 @@ extern "C" {
 #endif
 
 typedef enum pa_dtype {
-  PA_DTYPE_F32 = 0,  /* IEEE binary32 */
-  PA_DTYPE_F16 = 1,  /* IEEE binary16 */
-  PA_DTYPE_BF16 = 2  /* bfloat16 */
+  PA_DTYPE_F32 = 0,      /* IEEE binary32 */
+  PA_DTYPE_F16 = 1,      /* IEEE binary16 */
+  PA_DTYPE_BF16 = 2,     /* bfloat16 */
+  PA_DTYPE_FP8_E4M3 = 3  /* OCP 8-bit float E4M3 (bias 7, 3 significand bits,
+                            largest finite 448, no infinities, S.1111.111 NaN);
+                            KV caches only, with one scale per cache tensor */
 } pa_dtype;
 
 typedef enum pa_status {
@@ -104,7 +107,8 @@ typedef enum pa_status {
  *                   (k_token_stride >= num_kv_heads * head_dim, in elements)
  *   slot_mapping    device int64 [num_tokens]
  *   k_cache,v_cache device, dtype, layouts above
- *   dtype           pa_dtype of k, v and both caches (must match)
+ *   dtype           pa_dtype of k, v and both caches (must match; F32, F16 or
+ *                   BF16 -- E4M3 caches are written by pa_cache_write_fp8)
  *   head_dim        64, 128 or 256;  block_size: 8, 16, 32 or 64
  * Duplicate non-negative slots within one call race (undefined which wins).
  * num_tokens == 0 is a valid no-op.
@@ -113,6 +117,27 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
                    void* v_cache, int64_t num_tokens, int64_t k_token_stride,
                    int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
                    int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * pa_cache_write_fp8 -- pa_cache_write into E4M3 caches ("vLLM Project Update"
+ * talk, quantization update: an 8-bit floating-point KV cache).  The talk
+ * fixes neither format nor scaling; here: OCP E4M3 with one scale per cache
+ * tensor.  Element x of k (v), read as src_dtype, is stored as
+ * e4m3(x / k_scale) (resp. v_scale): the quotient is the correctly rounded
+ * fp32 division, then rounded to the nearest E4M3 value with ties to the even
+ * significand; magnitudes beyond 448 (infinities too) saturate to +-448, NaN
+ * stays NaN.  Layouts as above with X = 16 (one byte per element).
+ *
+ *   k, v            device, src_dtype (F32, F16 or BF16), as in pa_cache_write
+ *   k_cache,v_cache device, E4M3 bytes
+ *   k_scale,v_scale finite, > 0; a cache element stands for stored * scale
+ * Other arguments, errors and races as pa_cache_write.
+ */
+int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                       void* v_cache, int64_t num_tokens, int64_t k_token_stride,
+                       int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t num_blocks, int32_t block_size, int32_t src_dtype, float k_scale,
+                       float v_scale, void* stream);
 
 /*
  * pa_advance_step -- advance each sequence's decode state by one step on the
@@ -215,6 +240,36 @@ int pa_decode_merge(void* out, const void* q, const void* k_cache, const void* v
                     int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
                     int32_t kv_dtype, int32_t out_dtype, void* workspace, size_t workspace_bytes,
                     uint32_t flags, void* stream);
+
+/*
+ * pa_decode_fp8 / pa_decode_fp8_partitions -- pa_decode / pa_decode_partitions
+ * over E4M3 caches written by pa_cache_write_fp8: the attention of each query
+ * over the cache elements stored * k_scale (keys) and stored * v_scale
+ * (values).  pa_decode and pa_decode_partitions reject E4M3 caches
+ * (PA_ERR_DTYPE); the merge phase is pa_decode_merge with kv_dtype
+ * PA_DTYPE_FP8_E4M3.
+ *   q_dtype        F32, F16 or BF16 (BF16 runs on the matrix cores for GQA
+ *                  groups; the E4M3 values widen exactly to bfloat16)
+ *   out_dtype      F32 or q_dtype
+ *   k_scale,v_scale the scales the caches were written with (finite, > 0)
+ * All other arguments, the workspace and errors as pa_decode with kv_dtype
+ * PA_DTYPE_FP8_E4M3 (use it in the plan queries and the workspace size).
+ */
+int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, float scale,
+                  float k_scale, float v_scale, int32_t block_size, int32_t partition_size,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
+                  int32_t out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
+                  void* stream);
+int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             float scale, float k_scale, float v_scale, int32_t block_size,
+                             int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                             int32_t max_blocks_per_seq, int32_t q_dtype, int32_t out_dtype,
+                             void* workspace, size_t workspace_bytes, uint32_t flags,
+                             void* stream);
 
 /*
  * The partition size pa_decode uses when called with partition_size == 0 and

@@ -33,7 +33,8 @@ WAVES_FLAG = {1: WAVES_1, 2: WAVES_2, 4: WAVES_4}
 # one workgroup per possible (sequence, head, partition) item instead of the
 # persistent grid over the items that hold tokens
 NO_WORK_LIST = 16
-_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+# torch.float8_e4m3fn: the OCP E4M3 KV-cache storage type (caches only)
+_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3}
 
 _lib = None
 
@@ -90,6 +91,15 @@ def lib() -> ctypes.CDLL:
         for name in ("pa_decode", "pa_decode_partitions", "pa_decode_merge"):
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name).argtypes = dec_args
+        f32 = ctypes.c_float
+        dec8_args = [vp, vp, vp, vp, vp, vp, f32, f32, f32, i32, i32, i32, i32, i32, i32, i64, i32,
+                     i32, i32, vp, sz, u32, vp]
+        for name in ("pa_decode_fp8", "pa_decode_fp8_partitions"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = dec8_args
+        L.pa_cache_write_fp8.restype = ctypes.c_int
+        L.pa_cache_write_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i64, i32,
+                                         i32, f32, f32, vp]
         L.pa_decode_partition_size.restype = i32
         L.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, u32]
         L.pa_decode_workspace_size.restype = sz
@@ -149,6 +159,27 @@ def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     _check(lib().pa_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
                                 k_cache.data_ptr(), v_cache.data_ptr(), T, k.stride(0),
                                 v.stride(0), H, d, NB, bs, _dt(k), _stream(k_cache.device)))
+
+
+def cache_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float,
+                    v_scale: float) -> None:
+    """Quantizing scatter of f32/f16/bf16 k/v [T][Hkv][d] into E4M3 caches
+    (torch.float8_e4m3fn): element x is stored as e4m3(x / scale)."""
+    _require(k.dim() == 3 and v.dim() == 3 and k.shape == v.shape, "k, v must be [T][Hkv][d]")
+    T, H, d = k.shape
+    NB, H2, bs, d2 = _cache_dims(k_cache, v_cache)
+    _require((H2, d2) == (H, d), "cache shapes do not match k/v")
+    for t in (k, v):
+        _require(t.stride(2) == 1 and t.stride(1) == d, "heads of a token must be packed")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,)
+             and slot_mapping.is_contiguous(), "slot_mapping must be contiguous int64 [T]")
+    _require(k.dtype == v.dtype and k_cache.dtype == v_cache.dtype == torch.float8_e4m3fn,
+             "E4M3 caches and k, v of one dtype")
+    _check(lib().pa_cache_write_fp8(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                    k_cache.data_ptr(), v_cache.data_ptr(), T, k.stride(0),
+                                    v.stride(0), H, d, NB, bs, _dt(k), float(k_scale),
+                                    float(v_scale), _stream(k_cache.device)))
 
 
 def advance_step(num_queries: int, block_size: int, input_tokens: torch.Tensor,
@@ -221,7 +252,7 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, he
 
 
 def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
-                 partition_size, workspace, flags):
+                 partition_size, workspace, flags, kv_scales=None):
     _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
     B, Hq, d = q.shape
     _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
@@ -236,11 +267,18 @@ def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, 
     kvd = k_cache.dtype
     need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, kvd, flags)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        if fn_name != "pa_decode":
+        if fn_name not in ("pa_decode", "pa_decode_fp8"):
             raise PAError(-5, "the phase entry points need the caller's workspace")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if kv_scales is not None:
+        _check(getattr(lib(), fn_name)(
+            out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), float(kv_scales[0]),
+            float(kv_scales[1]), block_size, partition_size, B, Hq, Hkv, d, NB, MB, _dt(q),
+            _dt(out), ws_ptr, ws_bytes, flags, _stream(q.device)))
+        return
     _check(getattr(lib(), fn_name)(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), float(scale), block_size,
@@ -270,3 +308,20 @@ def decode_merge(out, q, k_cache, v_cache, block_tables, context_lens, scale, bl
     """Phase 2 of decode (log-sum-exp merge of the partitions)."""
     _decode_call("pa_decode_merge", out, q, k_cache, v_cache, block_tables, context_lens, scale,
                  block_size, partition_size, workspace, flags)
+
+
+def decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+               block_size, partition_size=0, workspace=None, flags=AUTO) -> None:
+    """decode over E4M3 caches written with the scales k_scale / v_scale."""
+    _require(k_cache.dtype == torch.float8_e4m3fn, "decode_fp8 needs E4M3 caches")
+    _decode_call("pa_decode_fp8", out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 block_size, partition_size, workspace, flags, (k_scale, v_scale))
+
+
+def decode_fp8_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                          v_scale, block_size, partition_size=0, workspace=None,
+                          flags=AUTO) -> None:
+    """Phase 1 of decode_fp8; decode_merge is phase 2 for every cache type."""
+    _require(k_cache.dtype == torch.float8_e4m3fn, "decode_fp8 needs E4M3 caches")
+    _decode_call("pa_decode_fp8_partitions", out, q, k_cache, v_cache, block_tables, context_lens,
+                 scale, block_size, partition_size, workspace, flags, (k_scale, v_scale))

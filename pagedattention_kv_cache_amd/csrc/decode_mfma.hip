@@ -1,5 +1,6 @@
 // decode_mfma.hip -- paged decode attention for a GQA head group on the matrix
-// cores (v_mfma_f32_16x16x32_{bf16,f16}), for 16-bit KV caches.
+// cores (v_mfma_f32_16x16x32_{bf16,f16}), for 16-bit KV caches and for E4M3
+// caches (widened exactly to bfloat16 in registers).
 //
 // A grouped-query head group is a real dense tile: the g query heads that
 // share a kv head multiply the same keys and values, so per 16-token chunk
@@ -92,10 +93,88 @@ constexpr int kChunk = 16;  // tokens per iteration: one 16-row QK^T tile
 constexpr int kNonTemporal = 2;
 
 
+// How a lane's matrix operands of one chunk are stored in the caches, loaded
+// and widened to the multiply type.  Per lane and 32-dim k-chunk c: the 8
+// dims 32c + 8j .. 32c + 8j + 7 of key token n; per 16-dim row chunk c: dim
+// 16c + n of value tokens 4j .. 4j + 3 (one token quad).
+template <Elem KV> struct Store;
+template <Elem KV> struct Store16 {  // f16 / bf16: loaded as the multiply type
+  using Math = Mma<KV>;
+  using KRaw = typename Math::vec8;
+  using VRaw = typename Math::vec4;
+  static constexpr int EB = 2;
+  static constexpr int kstep = 256;  // bytes between k-chunks (4 key chunks of a quad row)
+  static constexpr int vstep = 128;  // bytes between 16-dim value row chunks
+  // offsets from the chunk's first token quad
+  static __device__ __forceinline__ int koff(int n, int j, int D) {
+    return ((n >> 2) * (D / 8) + j) * 64 + (n & 3) * 16;
+  }
+  static __device__ __forceinline__ int voff(int n, int j, int D) { return (j * D + n) * 8; }
+  static __device__ __forceinline__ KRaw load_k(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(KRaw,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+  }
+  static __device__ __forceinline__ VRaw load_v(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(VRaw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+  static __device__ __forceinline__ KRaw load_k(const char* p) {
+    return __builtin_bit_cast(KRaw, ld16_nt(p));
+  }
+  static __device__ __forceinline__ VRaw load_v(const char* p) {
+    return *reinterpret_cast<const VRaw*>(p);
+  }
+  static __device__ __forceinline__ typename Math::vec8 k(KRaw r) { return r; }
+  static __device__ __forceinline__ typename Math::vec4 v(VRaw r) { return r; }
+};
+template <> struct Store<Elem::BF16> : Store16<Elem::BF16> {};
+template <> struct Store<Elem::F16> : Store16<Elem::F16> {};
+// E4M3: half the bytes per operand; widened exactly to bfloat16 (the queries
+// are bfloat16) before the matrix cores see them.  A key chunk of 16 bytes
+// holds 16 dims, so k-chunk c of lane group j is half (j & 1) of key chunk
+// 2c + j/2.
+template <> struct Store<Elem::FP8> {
+  using Math = Mma<Elem::BF16>;
+  using KRaw = uint2;
+  using VRaw = uint32_t;
+  static constexpr int EB = 1;
+  static constexpr int kstep = 128;
+  static constexpr int vstep = 64;
+  static __device__ __forceinline__ int koff(int n, int j, int D) {
+    return ((n >> 2) * (D / 16) + (j >> 1)) * 64 + (n & 3) * 16 + (j & 1) * 8;
+  }
+  static __device__ __forceinline__ int voff(int n, int j, int D) { return (j * D + n) * 4; }
+  static __device__ __forceinline__ KRaw load_k(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(KRaw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
+  }
+  static __device__ __forceinline__ VRaw load_v(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ KRaw load_k(const char* p) {
+    return *reinterpret_cast<const KRaw*>(p);
+  }
+  static __device__ __forceinline__ VRaw load_v(const char* p) {
+    return *reinterpret_cast<const VRaw*>(p);
+  }
+  static __device__ __forceinline__ Math::vec8 k(KRaw r) {
+    float f[8];
+    fp8x4_to_f32(r.x, f);
+    fp8x4_to_f32(r.y, f + 4);
+    const uint4 w = {pack_bf16_exact(f[0], f[1]), pack_bf16_exact(f[2], f[3]),
+                     pack_bf16_exact(f[4], f[5]), pack_bf16_exact(f[6], f[7])};
+    return __builtin_bit_cast(Math::vec8, w);
+  }
+  static __device__ __forceinline__ Math::vec4 v(VRaw r) {
+    float f[4];
+    fp8x4_to_f32(r, f);
+    const uint2 w = {pack_bf16_exact(f[0], f[1]), pack_bf16_exact(f[2], f[3])};
+    return __builtin_bit_cast(Math::vec4, w);
+  }
+};
+
 template <Elem KV, int D>
 struct Buffers {
-  typename Mma<KV>::vec8 k[D / 32];  // key row chunks of this lane's token
-  typename Mma<KV>::vec4 v[D / 16];  // 4-token value runs, one per 16-dim row chunk
+  typename Store<KV>::KRaw k[D / 32];  // key row pieces of this lane's token
+  typename Store<KV>::VRaw v[D / 16];  // 4-token value runs, one per 16-dim row chunk
 };
 
 // UB: every 16-token chunk lies in one cache block (block_size >= 16), so the
@@ -104,14 +183,14 @@ struct Buffers {
 // own blocks.
 template <Elem KV, int D, int G, bool UB>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
-  using M = Mma<KV>;
+  using St = Store<KV>;
+  using M = typename St::Math;
   using vec8 = typename M::vec8;
   using vec4 = typename M::vec4;
   using scalar = typename M::scalar;
   constexpr int KC = D / 32;  // QK^T k-chunks
   constexpr int VC = D / 16;  // P.V row chunks
 
-  constexpr int CPR = D / 8;  // 16-byte key chunks per row
 
   // Work items (sequence, kv head, head chunk, partition).  With a work list
   // (a.list_ints > 0) the grid is persistent: every workgroup builds the list
@@ -147,15 +226,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     const int lbs = a.log2_block_size;
     const int bs = a.block_size;
     const int P = a.partition_size;
-    const int64_t head_tile = (int64_t)bs * D * 2;  // bytes of one (block, head) tile
+    const int64_t head_tile = (int64_t)bs * D * St::EB;  // bytes of one (block, head) tile
     const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
     const int n = lane & 15;
     const int j = lane >> 4;
     // per-lane byte offsets from the chunk's first token quad: key token n
-    // (quad n/4, row n%4) chunk j; value quad j, dim n.  Key chunk 4c + j and
-    // value dim 16c + n add 256*c and 128*c bytes.
-    const int koff = ((n >> 2) * CPR + j) * 64 + (n & 3) * 16;
-    const int voff = (j * D + n) * 8;
+    // (quad n/4, row n%4), the dims of lane group j; value quad j, dim n.
+    // k-chunk c and value row chunk c add St::kstep * c and St::vstep * c.
+    const int koff = St::koff(n, j, D);
+    const int voff = St::voff(n, j, D);
     int b, hc, part;
     if (listed) {
       const int item = it / per_seq;
@@ -220,31 +299,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         // one block: a buffer resource based at the chunk's key / value tile,
         // per-lane 32-bit offsets, the 16-dim row stride as the scalar offset
         const int phys = __builtin_amdgcn_readlane(bt_lane, min(t0 >> lbs, last_blk) - wb);
-        const int64_t first_quad = (int64_t)phys * block_stride + (int64_t)(t0 & (bs - 1)) * D * 2;
+        const int64_t first_quad =
+            (int64_t)phys * block_stride + (int64_t)(t0 & (bs - 1)) * D * St::EB;
         const int range = none ? 0 : 0x7fffffff;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + first_quad, range);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + first_quad, range);
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          buf.k[c] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rk, koff + 256 * c, 0, kNonTemporal));
+        for (int c = 0; c < KC; ++c) buf.k[c] = St::load_k(rk, koff + St::kstep * c);
 #pragma unroll
-        for (int c = 0; c < VC; ++c)
-          buf.v[c] = __builtin_bit_cast(vec4, __builtin_amdgcn_raw_buffer_load_b64(
-                                                  rv, voff + 128 * c, 0, 0));
+        for (int c = 0; c < VC; ++c) buf.v[c] = St::load_v(rv, voff + St::vstep * c);
       } else {
         const int tk = t0 + n;      // this lane's key token
         const int tv = t0 + 4 * j;  // first token of this lane's value quad
         const int pk = __shfl(bt_lane, min(tk >> lbs, last_blk) - wb);
         const int pv = __shfl(bt_lane, min(tv >> lbs, last_blk) - wb);
         const int ik = tk & (bs - 1), iv = tv & (bs - 1);
-        const char* kp = kc + (int64_t)pk * block_stride +
-                         (((ik >> 2) * CPR + j) * 64 + (ik & 3) * 16);
-        const char* vp = vc + (int64_t)pv * block_stride + (((iv >> 2) * D + n) * 8);
+        // the quad of token ik (iv) within its block, then the lane's piece
+        const char* kp = kc + (int64_t)pk * block_stride + (ik >> 2) * 4 * D * St::EB +
+                         St::koff(ik & 3, j, D);
+        const char* vp = vc + (int64_t)pv * block_stride + (iv >> 2) * 4 * D * St::EB +
+                         St::voff(n, 0, D);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) buf.k[c] = __builtin_bit_cast(vec8, ld16_nt(kp + 256 * c));
+        for (int c = 0; c < KC; ++c) buf.k[c] = St::load_k(kp + St::kstep * c);
 #pragma unroll
-        for (int c = 0; c < VC; ++c) buf.v[c] = *reinterpret_cast<const vec4*>(vp + 128 * c);
+        for (int c = 0; c < VC; ++c) buf.v[c] = St::load_v(vp + St::vstep * c);
       }
     };
 
@@ -257,10 +335,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     auto compute = [&](Buffers<KV, D>& buf, int t0, int t_stop) {
       f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) sacc = M::qk(buf.k[c], qv[c], sacc);
+      for (int c = 0; c < KC; ++c) sacc = M::qk(St::k(buf.k[c]), qv[c], sacc);
       float s[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[r] = sacc[r] * a.scale_log2;
+      vec4 vv[VC];
+#pragma unroll
+      for (int c = 0; c < VC; ++c) vv[c] = St::v(buf.v[c]);
       if (t0 + kChunk > t_stop) {  // uniform: mask tokens past the partition / context
         const int nv = t_stop - t0 - 4 * j;  // valid tokens of this lane's run
 #pragma unroll
@@ -269,7 +350,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         for (int c = 0; c < VC; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (r >= nv) buf.v[c][r] = (scalar)0.0f;
+            if (r >= nv) vv[c][r] = (scalar)0.0f;
       }
       float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -296,8 +377,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       }
 #pragma unroll
       for (int c = 0; c < VC; ++c) {
-        o[c] = M::pv(buf.v[c], phi, o[c]);
-        o[c] = M::pv(buf.v[c], plo, o[c]);
+        o[c] = M::pv(vv[c], phi, o[c]);
+        o[c] = M::pv(vv[c], plo, o[c]);
       }
     };
 
@@ -372,10 +453,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         }
         const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
         if (n_parts == 1) {
-          store_elem(a.out, row_id * D + d, x / lt, a.out_dtype);
+          store_elem(a.out, row_id * D + d, x * a.v_scale / lt, a.out_dtype);
         } else {
           const int64_t slot = row_id * a.max_partitions + part;
-          a.ws_acc[slot * D + d] = x;
+          a.ws_acc[slot * D + d] = x * a.v_scale;
           if (d == 0) {
             a.ws_ml[slot * 2] = Mg;
             a.ws_ml[slot * 2 + 1] = lt;
@@ -388,7 +469,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     if (n < G) {
       const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + n;
       if (n_parts == 1) {
-        const float inv = 1.0f / l;
+        const float inv = a.v_scale / l;
 #pragma unroll
         for (int c = 0; c < VC; ++c)
 #pragma unroll
@@ -397,9 +478,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       } else {
         const int64_t slot = row_id * a.max_partitions + part;
         float* dst = a.ws_acc + slot * D;
+        const float vs = a.v_scale;
 #pragma unroll
-        for (int c = 0; c < VC; ++c)
-          *reinterpret_cast<f32x4_t*>(dst + 16 * c + 4 * j) = o[c];
+        for (int c = 0; c < VC; ++c) {
+          f32x4_t x = o[c];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] *= vs;
+          *reinterpret_cast<f32x4_t*>(dst + 16 * c + 4 * j) = x;
+        }
         if (j == 0) {
           a.ws_ml[slot * 2] = m;
           a.ws_ml[slot * 2 + 1] = l;
@@ -458,6 +544,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int head_dim, h
   if (kv_dtype == 2) {
     if (head_dim == 128) return dispatch_g<Elem::BF16, 128>(a, items_x, s);
     if (head_dim == 64) return dispatch_g<Elem::BF16, 64>(a, items_x, s);
+  } else if (kv_dtype == 3) {  // E4M3 caches, bfloat16 queries
+    if (head_dim == 128) return dispatch_g<Elem::FP8, 128>(a, items_x, s);
+    if (head_dim == 64) return dispatch_g<Elem::FP8, 64>(a, items_x, s);
   } else if (kv_dtype == 1) {
     if (head_dim == 128) return dispatch_g<Elem::F16, 128>(a, items_x, s);
     if (head_dim == 64) return dispatch_g<Elem::F16, 64>(a, items_x, s);

@@ -40,22 +40,62 @@ namespace {
 
 constexpr int kTile = 16;
 
-// Four tokens of one value dim: 8 bytes for the 16-bit types, 16 for fp32.
+// Four tokens of one value dim: 4 bytes for E4M3, 8 for the 16-bit types,
+// 16 for fp32.
 template <int EB> struct QuadRaw;
+template <> struct QuadRaw<1> { using type = uint32_t; };
 template <> struct QuadRaw<2> { using type = uint2; };
 template <> struct QuadRaw<4> { using type = uint4; };
+
+// A lane's piece of a key row: one 16-byte chunk (16-bit and fp32 caches) or
+// half of one (E4M3, so that a row still spans at least 8 lanes).
+template <int EB> struct KeyPiece { using type = uint4; static constexpr int bytes = 16; };
+template <> struct KeyPiece<1> { using type = uint2; static constexpr int bytes = 8; };
 
 template <Elem KV, int D>
 struct Tile {
   static constexpr int EB = ElemTraits<KV>::bytes;
-  static constexpr int RL = D * EB / 16;         // lanes per key row
-  static constexpr int NI = kTile / (64 / RL);   // key load instructions per tile
-  static constexpr int DPL = D / 64;             // value dims per lane
+  static constexpr int KB = KeyPiece<EB>::bytes;  // key bytes per lane and token
+  static constexpr int RL = D * EB / KB;          // lanes per key row
+  static constexpr int CPR = D * EB / 16;         // 16-byte key chunks per row
+  static constexpr int NI = kTile / (64 / RL);    // key load instructions per tile
+  static constexpr int DPL = D / 64;              // value dims per lane
   using VQ = typename QuadRaw<EB>::type;
-  uint4 k[NI];
+  typename KeyPiece<EB>::type k[NI];
   VQ v[4][DPL];  // [token quad of the tile][owned dim]
 };
 
+// Byte offset of lane piece c of the key of token `row` (quad row/4, row
+// row%4) from its token quad.
+template <Elem KV, int D>
+__device__ __forceinline__ int key_piece_off(int row, int c) {
+  using T = Tile<KV, D>;
+  if constexpr (T::KB == 16) return ((row >> 2) * T::CPR + c) * 64 + (row & 3) * 16;
+  else return ((row >> 2) * T::CPR + (c >> 1)) * 64 + (row & 3) * 16 + (c & 1) * 8;
+}
+
+template <Elem KV>
+__device__ __forceinline__ void widen_key(const uint4& raw, float* out) {
+  widen16<KV>(raw, out);
+}
+template <Elem KV>
+__device__ __forceinline__ void widen_key(const uint2& raw, float* out) {
+  widen8_fp8(raw, out);
+}
+
+__device__ __forceinline__ uint4 load_key(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                          uint4*) {
+  return buf_ld16(r, voff, soff);
+}
+__device__ __forceinline__ uint2 load_key(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                          uint2*) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+template <Elem KV>
+__device__ __forceinline__ void widen_quad(const uint32_t& r, float* out) {
+  fp8x4_to_f32(r, out);
+}
 template <Elem KV>
 __device__ __forceinline__ void widen_quad(const uint2& r, float* out) {
   out[0] = lo_to_f32<KV>(r.x);
@@ -75,6 +115,11 @@ template <int EB>
 __device__ __forceinline__ typename QuadRaw<EB>::type buf_ld_quad(__amdgpu_buffer_rsrc_t r,
                                                                   int voff, int soff);
 template <>
+__device__ __forceinline__ uint32_t buf_ld_quad<1>(__amdgpu_buffer_rsrc_t r, int voff,
+                                                   int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+template <>
 __device__ __forceinline__ uint2 buf_ld_quad<2>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
@@ -87,8 +132,9 @@ template <Elem KV, int D, int G>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
   using T = Tile<KV, D>;
   constexpr int EB = T::EB;
-  constexpr int EPL = 16 / EB;     // elements per 16-byte chunk
+  constexpr int EPL = T::KB / EB;  // key elements per lane piece
   constexpr int RL = T::RL;        // lanes per key row
+  constexpr int CPR = T::CPR;      // 16-byte key chunks per row
   constexpr int TPI = 64 / RL;     // tokens per key load instruction
   constexpr int NI = T::NI;
   constexpr int DPL = T::DPL;
@@ -142,7 +188,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
 
     // per-lane byte offsets from a segment's first token quad: key chunk c of
     // token `row` (quad row/4, row row%4); the value quad of each owned dim
-    const int koff = ((row >> 2) * RL + c) * 64 + (row & 3) * 16;
+    const int koff = key_piece_off<KV, D>(row, c);
     int voff[DPL];
 #pragma unroll
     for (int dd = 0; dd < DPL; ++dd) voff[dd] = (dd * 64 + lane) * 4 * EB;
@@ -214,7 +260,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
       for (int i = 0; i < NI; ++i) {
         const int sgm = (i * TPI) / SEG;
         const int l0 = (i * TPI) % SEG;  // first token of the instruction inside the segment
-        buf.k[i] = buf_ld16(rk[sgm], koff, (l0 >> 2) * RL * 64 + (l0 & 3) * 16);
+        buf.k[i] = load_key(rk[sgm], koff, (l0 >> 2) * CPR * 64 + (l0 & 3) * 16, &buf.k[i]);
       }
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
@@ -238,7 +284,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         float kf[EPL];
-        widen16<KV>(buf.k[i], kf);
+        widen_key<KV>(buf.k[i], kf);
         const bool valid = (t0 + i * TPI + row) < t_stop;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -363,10 +409,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
         }
         const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
         if (n_parts == 1) {
-          store_elem(a.out, row_id * D + d, x / lt, a.out_dtype);
+          store_elem(a.out, row_id * D + d, x * a.v_scale / lt, a.out_dtype);
         } else {
           const int64_t slot = row_id * a.max_partitions + part;
-          a.ws_acc[slot * D + d] = x;
+          a.ws_acc[slot * D + d] = x * a.v_scale;
           if (d == 0) {
             a.ws_ml[slot * 2] = Mg;
             a.ws_ml[slot * 2 + 1] = lt;
@@ -381,14 +427,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
       const float l = lsum[g];
       const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
       if (n_parts == 1) {
-        const float inv = 1.0f / l;
+        const float inv = a.v_scale / l;
 #pragma unroll
         for (int dd = 0; dd < DPL; ++dd)
           store_elem(a.out, row_id * D + dd * 64 + lane, acc[g][dd] * inv, a.out_dtype);
       } else {
         const int64_t slot = row_id * a.max_partitions + part;
 #pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) a.ws_acc[slot * D + dd * 64 + lane] = acc[g][dd];
+        for (int dd = 0; dd < DPL; ++dd)
+          a.ws_acc[slot * D + dd * 64 + lane] = acc[g][dd] * a.v_scale;
         if (lane == 0) {
           a.ws_ml[slot * 2] = m[g];
           a.ws_ml[slot * 2 + 1] = l;
@@ -443,6 +490,7 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int head_dim, h
     case 0: return dispatch_d<Elem::F32>(a, head_dim, items_x, s);
     case 1: return dispatch_d<Elem::F16>(a, head_dim, items_x, s);
     case 2: return dispatch_d<Elem::BF16>(a, head_dim, items_x, s);
+    case 3: return dispatch_d<Elem::FP8>(a, head_dim, items_x, s);
     default: return hipErrorInvalidValue;
   }
 }

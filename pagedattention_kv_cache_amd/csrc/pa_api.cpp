@@ -19,6 +19,7 @@ int elem_bytes(int32_t dtype) {
     case PA_DTYPE_F32: return 4;
     case PA_DTYPE_F16: return 2;
     case PA_DTYPE_BF16: return 2;
+    case PA_DTYPE_FP8_E4M3: return 1;
     default: return 0;
   }
 }
@@ -52,8 +53,30 @@ int32_t mfma_heads_per_item(int32_t g) {
 // same dtype once a GQA group has at least two q heads per kv head (a
 // multi-column tile); plain multi-head attention and fp32 stay on the
 // vector-ALU kernel unless the caller forces the matrix cores.
+// Queries in the cache dtype or fp32; with E4M3 caches any of f32, f16, bf16.
+bool valid_q_dtype(int32_t q_dtype, int32_t kv_dtype) {
+  if (q_dtype != PA_DTYPE_F32 && q_dtype != PA_DTYPE_F16 && q_dtype != PA_DTYPE_BF16)
+    return false;
+  return q_dtype == kv_dtype || q_dtype == PA_DTYPE_F32 || kv_dtype == PA_DTYPE_FP8_E4M3;
+}
+
+// Outputs in fp32 or in the 16-bit type of the attention (the cache's, or the
+// queries' for E4M3 caches).
+bool valid_out_dtype(int32_t out_dtype, int32_t q_dtype, int32_t kv_dtype) {
+  if (out_dtype == PA_DTYPE_F32) return true;
+  return out_dtype == (kv_dtype == PA_DTYPE_FP8_E4M3 ? q_dtype : kv_dtype);
+}
+
+// The matrix-core kernel multiplies 16-bit operands: 16-bit caches queried in
+// their own dtype, or E4M3 caches (widened exactly to bfloat16) with bfloat16
+// queries.
+bool mfma_eligible(int32_t kv_dtype, int32_t q_dtype) {
+  if (kv_dtype == PA_DTYPE_FP8_E4M3) return q_dtype == PA_DTYPE_BF16;
+  return kv_dtype != PA_DTYPE_F32 && q_dtype == kv_dtype;
+}
+
 bool use_mfma(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t group) {
-  const bool eligible = kv_dtype != PA_DTYPE_F32 && q_dtype == kv_dtype;
+  const bool eligible = mfma_eligible(kv_dtype, q_dtype);
   const uint32_t kernel = flags & PA_DECODE_KERNEL_MASK;
   if (kernel == PA_DECODE_FORCE_MFMA) return eligible;
   if (kernel == PA_DECODE_FORCE_VALU) return false;
@@ -190,7 +213,7 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
                    int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
                    int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream) {
   const int eb = elem_bytes(dtype);
-  if (!eb) return PA_ERR_DTYPE;
+  if (!eb || dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_DTYPE;  // E4M3: pa_cache_write_fp8
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
   if (!valid_block_size(block_size)) return PA_ERR_UNSUPPORTED;
@@ -217,7 +240,51 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
   a.head_dim = head_dim;
   a.block_size = block_size;
   a.elem_bytes = eb;
+  a.k_scale = 1.0f;
+  a.v_scale = 1.0f;
   return pa::launch_cache_write(a, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                       void* v_cache, int64_t num_tokens, int64_t k_token_stride,
+                       int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t num_blocks, int32_t block_size, int32_t src_dtype, float k_scale,
+                       float v_scale, void* stream) {
+  if (src_dtype != PA_DTYPE_F32 && src_dtype != PA_DTYPE_F16 && src_dtype != PA_DTYPE_BF16)
+    return PA_ERR_DTYPE;
+  const int eb = elem_bytes(src_dtype);
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || k_scale > 3.0e38f || v_scale > 3.0e38f)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (!valid_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row) return PA_ERR_SHAPE;
+  if ((k_token_stride * eb) % 16 || (v_token_stride * eb) % 16) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_SHAPE;
+  const int64_t threads = num_tokens * num_kv_heads * ((int64_t)head_dim / 16);
+  if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
+  pa::CacheWriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.slots = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_tokens = num_tokens;
+  a.num_blocks = num_blocks;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.elem_bytes = 1;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return pa::launch_cache_write_fp8(a, src_dtype, (hipStream_t)stream) == hipSuccess ? PA_OK
+                                                                                      : PA_ERR_HIP;
 }
 
 int pa_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
@@ -259,10 +326,9 @@ int32_t pa_decode_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t q_dt
                          int32_t kv_dtype, uint32_t flags) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return PA_ERR_SHAPE;
   if (!elem_bytes(q_dtype) || !elem_bytes(kv_dtype)) return PA_ERR_DTYPE;
-  if (q_dtype != kv_dtype && q_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
+  if (!valid_q_dtype(q_dtype, kv_dtype)) return PA_ERR_DTYPE;
   if (!valid_flags(flags)) return PA_ERR_UNSUPPORTED;
-  if (forces_mfma(flags) && (kv_dtype == PA_DTYPE_F32 || q_dtype != kv_dtype))
-    return PA_ERR_UNSUPPORTED;
+  if (forces_mfma(flags) && !mfma_eligible(kv_dtype, q_dtype)) return PA_ERR_UNSUPPORTED;
   return use_mfma(flags, kv_dtype, q_dtype, num_q_heads / num_kv_heads) ? PA_DECODE_FORCE_MFMA
                                                                         : PA_DECODE_FORCE_VALU;
 }
@@ -273,9 +339,8 @@ namespace {
 int32_t plan_args(const DecodeShape& s, int32_t partition_size, int32_t q_dtype, int32_t* p) {
   const int st = check_shape(s);
   if (st != PA_OK) return st;
-  if (!elem_bytes(q_dtype)) return PA_ERR_DTYPE;
-  if (q_dtype != s.kv_dtype && q_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
-  if (forces_mfma(s.flags) && q_dtype != s.kv_dtype) return PA_ERR_UNSUPPORTED;
+  if (!valid_q_dtype(q_dtype, s.kv_dtype)) return PA_ERR_DTYPE;
+  if (forces_mfma(s.flags) && !mfma_eligible(s.kv_dtype, q_dtype)) return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 || (partition_size > 0 && partition_size % s.block_size))
     return PA_ERR_SHAPE;
   const int64_t max_ctx = (int64_t)s.max_blocks_per_seq * s.block_size;
@@ -329,18 +394,20 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t block_size, int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
                 int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                 int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
-                void* workspace, size_t workspace_bytes, uint32_t flags, void* stream, int phase) {
+                void* workspace, size_t workspace_bytes, uint32_t flags, void* stream, int phase,
+                float k_scale = 1.0f, float v_scale = 1.0f) {
   DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                 kv_dtype, flags};
   int st = check_shape(s);
   if (st != PA_OK) return st;
   if (num_blocks <= 0) return PA_ERR_SHAPE;
-  if (!elem_bytes(q_dtype) || !elem_bytes(out_dtype)) return PA_ERR_DTYPE;
-  if (q_dtype != kv_dtype && q_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
-  if (out_dtype != kv_dtype && out_dtype != PA_DTYPE_F32) return PA_ERR_DTYPE;
+  if (!valid_q_dtype(q_dtype, kv_dtype)) return PA_ERR_DTYPE;
+  if (!valid_out_dtype(out_dtype, q_dtype, kv_dtype)) return PA_ERR_DTYPE;
+  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || k_scale > 3.0e38f || v_scale > 3.0e38f)
+    return PA_ERR_SHAPE;
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
     return PA_ERR_SHAPE;
-  if (forces_mfma(flags) && q_dtype != kv_dtype) return PA_ERR_UNSUPPORTED;
+  if (forces_mfma(flags) && !mfma_eligible(kv_dtype, q_dtype)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
@@ -365,7 +432,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   char* ws = reinterpret_cast<char*>(workspace);
   a.ws_ml = need ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_acc = need ? reinterpret_cast<float*>(ws + round_up(rows * 2 * sizeof(float))) : nullptr;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -410,9 +478,37 @@ extern "C" {
       num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, q_dtype, \
       kv_dtype, out_dtype, workspace, workspace_bytes, flags, stream
 
-int pa_decode(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kBoth); }
-int pa_decode_partitions(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kPartitions); }
+// E4M3 caches go through pa_decode_fp8 (they need their scales)
+int pa_decode(PA_DECODE_PARAMS) {
+  if (kv_dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_DTYPE;
+  return decode_impl(PA_DECODE_ARGS, kBoth);
+}
+int pa_decode_partitions(PA_DECODE_PARAMS) {
+  if (kv_dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_DTYPE;
+  return decode_impl(PA_DECODE_ARGS, kPartitions);
+}
 int pa_decode_merge(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kMerge); }
+
+#define PA_DECODE_FP8_PARAMS                                                                   \
+  void *out, const void *q, const void *k_cache, const void *v_cache,                          \
+      const int32_t *block_tables, const int32_t *context_lens, float scale, float k_scale,    \
+      float v_scale, int32_t block_size, int32_t partition_size, int32_t num_seqs,             \
+      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,         \
+      int32_t max_blocks_per_seq, int32_t q_dtype, int32_t out_dtype, void *workspace,         \
+      size_t workspace_bytes, uint32_t flags, void *stream
+
+int pa_decode_fp8(PA_DECODE_FP8_PARAMS) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                     partition_size, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, q_dtype, PA_DTYPE_FP8_E4M3, out_dtype, workspace,
+                     workspace_bytes, flags, stream, kBoth, k_scale, v_scale);
+}
+int pa_decode_fp8_partitions(PA_DECODE_FP8_PARAMS) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                     partition_size, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, q_dtype, PA_DTYPE_FP8_E4M3, out_dtype, workspace,
+                     workspace_bytes, flags, stream, kPartitions, k_scale, v_scale);
+}
 
 }  // extern "C"
 

@@ -1,7 +1,8 @@
 // pa_device.hpp -- gfx950 device helpers shared by the paged-attention kernels.
 //
-// Element types are carried as raw bits (uint16_t for f16/bf16, float for
-// f32) and widened to fp32 with exact conversions; all accumulation is fp32.
+// Element types are carried as raw bits (uint8_t for E4M3, uint16_t for
+// f16/bf16, float for f32) and widened to fp32 with exact conversions; all
+// accumulation is fp32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,12 +10,53 @@
 
 namespace pa {
 
-enum class Elem : int { F32 = 0, F16 = 1, BF16 = 2 };
+// FP8: OCP 8-bit float E4M3 (bias 7, 3 significand bits, largest finite 448,
+// no infinities), a cache storage type only.
+enum class Elem : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
 
 template <Elem E> struct ElemTraits;
 template <> struct ElemTraits<Elem::F32> { static constexpr int bytes = 4; };
 template <> struct ElemTraits<Elem::F16> { static constexpr int bytes = 2; };
 template <> struct ElemTraits<Elem::BF16> { static constexpr int bytes = 2; };
+template <> struct ElemTraits<Elem::FP8> { static constexpr int bytes = 1; };
+
+// ---- E4M3 ----------------------------------------------------------------
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float fp8_f32x2_t;
+
+// The four E4M3 values packed in a dword, widened exactly to fp32 by the
+// hardware conversion (gfx950 converts the OCP E4M3 format).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
+  const fp8_f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const fp8_f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+// Two fp32 values that are exact in bfloat16 (every E4M3 value is: at most 4
+// significant bits, exponents -9..8), packed as two bfloat16 by keeping each
+// one's upper half.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// fp32 -> E4M3, nearest value with ties to the even significand, magnitudes
+// beyond 448 (infinities too) saturating to +-448, NaN to the NaN pattern of
+// its sign.  Integer/exact-float steps only, so the result does not depend on
+// any conversion mode: below 2^-6 the values are the multiples of 2^-9 (code
+// = the multiple, 8 being the smallest normal); above, a*2^(3-e) in [8, 16]
+// is rounded and a carry into 16 moves to the next exponent.
+__device__ __forceinline__ uint32_t fp8_e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = __builtin_fabsf(y);
+  if (!(a == a)) return sign | 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+  const float m = __builtin_rintf(a * __uint_as_float((uint32_t)(127 + 3 - e) << 23));
+  return sign | ((((uint32_t)(e + 7)) << 3) + ((uint32_t)m - 8u));
+}
 
 // ---- exact widening of the two 16-bit elements packed in one dword --------
 template <Elem E> __device__ __forceinline__ float lo_to_f32(uint32_t w);
@@ -49,6 +91,12 @@ __device__ __forceinline__ void widen16(const uint4& raw, float* out) {
       out[2 * i + 1] = hi_to_f32<E>(w[i]);
     }
   }
+}
+
+// Widen the 8 E4M3 bytes held in `raw` into fp32.
+__device__ __forceinline__ void widen8_fp8(const uint2& raw, float* out) {
+  fp8x4_to_f32(raw.x, out);
+  fp8x4_to_f32(raw.y, out + 4);
 }
 
 // One element of type E (at element index i of p) as fp32.

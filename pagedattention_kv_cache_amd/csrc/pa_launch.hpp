@@ -22,9 +22,13 @@ struct CacheWriteArgs {
   int32_t head_dim;
   int32_t block_size;
   int32_t elem_bytes;
+  float k_scale;  // E4M3 caches: stored value = x / scale
+  float v_scale;
 };
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+// Quantizing write of f32 / f16 / bf16 rows (src_dtype) into E4M3 caches.
+hipError_t launch_cache_write_fp8(const CacheWriteArgs& a, int src_dtype, hipStream_t stream);
 
 // Everything a decode kernel needs; passed by value as the kernel argument.
 struct DecodeArgs {
@@ -36,7 +40,8 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* ws_ml;   // [B][Hq][P][2] running max (log2 domain) and sum
   float* ws_acc;  // [B][Hq][P][D] unnormalised partial outputs
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // scale * k_scale * log2(e)
+  float v_scale;     // cache value = stored value * v_scale (1 for the unscaled types)
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_q_heads;

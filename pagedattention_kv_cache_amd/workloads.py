@@ -28,10 +28,13 @@ from typing import Callable, Sequence
 import numpy as np
 import torch
 
-DTYPE_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+# "fp8": OCP E4M3, a KV-cache storage type only (written from the 16-bit values
+# with per-tensor scales)
+DTYPE_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "fp8": torch.float8_e4m3fn}
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # quiet-NaN bit patterns used to poison unused cache memory in parity runs
-POISON_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+POISON_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8": 0x7F}
 
 # stream indices under SeedSequence(seed).spawn(...)
 _S_LENGTHS, _S_POOL, _S_Q, _S_STEP, _S_SEQ, _S_SAMPLED = range(6)
@@ -54,10 +57,17 @@ class DecodeConfig:
     partition_size: int = 0  # 0 = library default
     num_blocks: int | None = None  # None = ceil(1.25 * blocks needed)
     scale: float | None = None  # None = 1/sqrt(head_dim) rounded to fp32
+    cache_dtype: str = ""  # "" = dtype; "fp8" = E4M3 caches written with fp8_scales
+    fp8_scales: tuple = (1.0, 1.0)  # (k, v): cache element = stored value * scale
 
     @property
     def group(self) -> int:
         return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def kv_dtype(self) -> str:
+        """Storage dtype of the KV caches."""
+        return self.cache_dtype or self.dtype
 
     def attn_scale(self) -> float:
         s = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
@@ -103,13 +113,31 @@ CONFIGS: dict[int, DecodeConfig] = {
 }
 
 
+def fp8_variant(cfg: DecodeConfig, k_scale: float, v_scale: float) -> DecodeConfig:
+    """The same workload with E4M3 caches: the 16-bit K/V are written with the
+    per-tensor scales k_scale, v_scale (powers of two here, so x / scale is
+    exact and only the E4M3 rounding quantizes)."""
+    return dataclasses.replace(cfg, name=cfg.name.replace("-bf16", "") + "-fp8kv",
+                               cache_dtype="fp8", fp8_scales=(k_scale, v_scale))
+
+
+# E4M3-cache variants of the GQA workloads (the KV of configs 4 and 5 are
+# N(0, 0.5^2) / N(0, 1) keys and N(0, 1) values: with these scales every drawn
+# value lands well inside the E4M3 range, the largest near 200).
+FP8_CONFIGS: dict[int, DecodeConfig] = {
+    4: fp8_variant(CONFIGS[4], 2.0 ** -6, 2.0 ** -5),
+    5: fp8_variant(CONFIGS[5], 2.0 ** -5, 2.0 ** -5),
+}
+
+
 def custom_config(name: str, lengths: Sequence[int], num_q_heads: int, num_kv_heads: int,
                   head_dim: int, dtype: str, block_size: int, seed: int, steps: int = 1,
                   k_scale: float = 1.0, partition_size: int = 0,
-                  num_blocks: int | None = None, scale: float | None = None) -> DecodeConfig:
+                  num_blocks: int | None = None, scale: float | None = None,
+                  cache_dtype: str = "", fp8_scales: tuple = (1.0, 1.0)) -> DecodeConfig:
     return DecodeConfig(name, len(lengths), num_q_heads, num_kv_heads, head_dim, dtype,
                         block_size, seed, _fixed(lengths), steps, k_scale, partition_size,
-                        num_blocks, scale)
+                        num_blocks, scale, cache_dtype, fp8_scales)
 
 
 def round_to(x: np.ndarray, dtype: str) -> torch.Tensor:
@@ -119,10 +147,12 @@ def round_to(x: np.ndarray, dtype: str) -> torch.Tensor:
 
 
 def raw_bits(t: torch.Tensor) -> np.ndarray:
-    """The raw element bits of a CPU tensor as a numpy array (uint16/uint32)."""
+    """The raw element bits of a CPU tensor as a numpy array (uint8/uint16/uint32)."""
     t = t.contiguous()
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
@@ -170,7 +200,8 @@ class Workload:
     # ---- sizes ---------------------------------------------------------
     @property
     def elem_bytes(self) -> int:
-        return DTYPE_BYTES[self.cfg.dtype]
+        """Bytes per KV cache element."""
+        return DTYPE_BYTES[self.cfg.kv_dtype]
 
     def context_lens(self, step: int) -> np.ndarray:
         return (self.lens0 + step).astype(np.int32)
@@ -251,7 +282,7 @@ class Workload:
             "num_q_heads": self.cfg.num_q_heads,
             "num_kv_heads": self.cfg.num_kv_heads,
             "head_dim": self.cfg.head_dim,
-            "kv_dtype": self.cfg.dtype,
+            "kv_dtype": self.cfg.kv_dtype,
             "block_size": bs,
             "num_blocks": self.num_blocks,
             "steps": self.cfg.steps,

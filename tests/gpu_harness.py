@@ -15,6 +15,9 @@ from pagedattention_kv_cache_amd.workloads import DTYPE_TORCH, POISON_BITS, Work
 
 
 def _poison(shape, dtype: str, device) -> torch.Tensor:
+    if dtype == "fp8":
+        return torch.full(shape, POISON_BITS[dtype], dtype=torch.uint8,
+                          device=device).view(torch.float8_e4m3fn)
     if dtype == "f32":
         bits = torch.full(shape, POISON_BITS[dtype], dtype=torch.int32, device=device)
         return bits.view(torch.float32)
@@ -30,15 +33,16 @@ class GpuState:
         self.wl = wl
         c = wl.cfg
         self.device = device
+        kvd = c.kv_dtype
         shape_k = pa.key_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size,
-                                     DTYPE_TORCH[c.dtype])
+                                     DTYPE_TORCH[kvd])
         shape_v = pa.value_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size)
         if poison:
-            self.kc = _poison(shape_k, c.dtype, device)
-            self.vc = _poison(shape_v, c.dtype, device)
+            self.kc = _poison(shape_k, kvd, device)
+            self.vc = _poison(shape_v, kvd, device)
         else:
-            self.kc = torch.empty(shape_k, dtype=DTYPE_TORCH[c.dtype], device=device)
-            self.vc = torch.empty(shape_v, dtype=DTYPE_TORCH[c.dtype], device=device)
+            self.kc = torch.empty(shape_k, dtype=DTYPE_TORCH[kvd], device=device)
+            self.vc = torch.empty(shape_v, dtype=DTYPE_TORCH[kvd], device=device)
         self.block_tables = torch.from_numpy(wl.block_tables).to(device)
         self.q = wl.queries().to(device)
         sk, sv = wl.step_kv()
@@ -49,22 +53,22 @@ class GpuState:
         self._fill_prior(oracle_state, seqs_for_oracle)
 
     def _fill_prior(self, oracle_state, seqs_for_oracle):
-        import oracle as orc  # only when an oracle state is being filled
+        from tests.paged_host import oracle_write  # only when an oracle state is being filled
         c = self.wl.cfg
         for b in range(c.num_seqs):
             k, v = self.wl.prior_kv(b)
             if k.shape[0] == 0:
                 continue
             slots = self.wl.prior_slots(b)
-            pa.cache_write(k.to(self.device), v.to(self.device),
-                           torch.from_numpy(slots).to(self.device), self.kc, self.vc)
+            write_kv(c, k.to(self.device), v.to(self.device),
+                     torch.from_numpy(slots).to(self.device), self.kc, self.vc)
             if oracle_state is not None and (seqs_for_oracle is None or b in seqs_for_oracle):
-                orc.cache_write(raw_bits(k), raw_bits(v), slots, oracle_state.kc, oracle_state.vc,
-                                c.dtype)
+                oracle_write(c, raw_bits(k), raw_bits(v), slots, oracle_state.kc,
+                             oracle_state.vc)
 
     def write_step(self, step: int) -> None:
-        pa.cache_write(self.step_k[step], self.step_v[step], self.step_slots[step], self.kc,
-                       self.vc)
+        write_kv(self.wl.cfg, self.step_k[step], self.step_v[step], self.step_slots[step],
+                 self.kc, self.vc)
 
     def decode(self, step: int, out_dtype: torch.dtype = torch.float32, partition_size=None,
                flags: int = pa.AUTO, q: torch.Tensor | None = None) -> torch.Tensor:
@@ -72,9 +76,33 @@ class GpuState:
         qq = self.q[step] if q is None else q
         out = torch.empty(qq.shape, dtype=out_dtype, device=self.device)
         p = c.partition_size if partition_size is None else partition_size
-        pa.decode(out, qq, self.kc, self.vc, self.block_tables, self.ctx[step], c.attn_scale(),
-                  c.block_size, p, flags=flags)
+        decode_kv(c, out, qq, self.kc, self.vc, self.block_tables, self.ctx[step], p, flags=flags)
         return out
+
+
+def write_kv(cfg, k, v, slots, kc, vc) -> None:
+    """The library's cache write for the config's cache dtype."""
+    if cfg.kv_dtype == "fp8":
+        pa.cache_write_fp8(k, v, slots, kc, vc, *cfg.fp8_scales)
+    else:
+        pa.cache_write(k, v, slots, kc, vc)
+
+
+def decode_kv(cfg, out, q, kc, vc, block_tables, lens, partition_size, workspace=None,
+              flags=pa.AUTO, phase: str = "both") -> None:
+    """The library's decode (or one phase of it) for the config's cache dtype."""
+    args = (out, q, kc, vc, block_tables, lens, cfg.attn_scale())
+    if cfg.kv_dtype == "fp8":
+        fn = {"both": pa.decode_fp8, "partitions": pa.decode_fp8_partitions}.get(phase)
+        if fn is not None:
+            fn(*args, *cfg.fp8_scales, cfg.block_size, partition_size, workspace, flags)
+            return
+    else:
+        fn = {"both": pa.decode, "partitions": pa.decode_partitions}.get(phase)
+        if fn is not None:
+            fn(*args, cfg.block_size, partition_size, workspace, flags)
+            return
+    pa.decode_merge(*args, cfg.block_size, partition_size, workspace, flags)
 
 
 def oracle_state_empty(wl: Workload):

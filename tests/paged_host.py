@@ -12,12 +12,12 @@ import torch
 import oracle
 from pagedattention_kv_cache_amd.workloads import POISON_BITS, Workload, raw_bits
 
-_BITS_NP = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
+_BITS_NP = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
 
 
 def key_chunk(dtype: str) -> int:
     """X: elements per 16-byte chunk of the key layout."""
-    return 4 if dtype == "f32" else 8
+    return {"f32": 4, "f16": 8, "bf16": 8, "fp8": 16}[dtype]
 
 
 def key_pool_shape(NB: int, H: int, d: int, bs: int, dtype: str) -> tuple:
@@ -35,8 +35,24 @@ def poisoned_pool(wl: Workload, transposed: bool) -> np.ndarray:
     c = wl.cfg
     shape = (value_pool_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size)
              if transposed else
-             key_pool_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.dtype))
-    return np.full(shape, POISON_BITS[c.dtype], dtype=_BITS_NP[c.dtype])
+             key_pool_shape(wl.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.kv_dtype))
+    return np.full(shape, POISON_BITS[c.kv_dtype], dtype=_BITS_NP[c.kv_dtype])
+
+
+def oracle_write(cfg, k: np.ndarray, v: np.ndarray, slots: np.ndarray, kc: np.ndarray,
+                 vc: np.ndarray) -> None:
+    """The oracle's cache write for the config's cache dtype (k, v raw bits)."""
+    if cfg.kv_dtype == "fp8":
+        oracle.cache_write_fp8(k, v, slots, kc, vc, cfg.dtype, *cfg.fp8_scales)
+    else:
+        oracle.cache_write(k, v, slots, kc, vc, cfg.dtype)
+
+
+def oracle_decode(cfg, q: np.ndarray, kc: np.ndarray, vc: np.ndarray, block_tables, lens,
+                  rows=None, threads: int = 8) -> np.ndarray:
+    ks, vs = cfg.fp8_scales if cfg.kv_dtype == "fp8" else (1.0, 1.0)
+    return oracle.decode(q, cfg.dtype, kc, vc, cfg.kv_dtype, block_tables, lens,
+                         cfg.attn_scale(), rows=rows, threads=threads, k_scale=ks, v_scale=vs)
 
 
 def key_rows(kc: np.ndarray, blk: int, off: int) -> np.ndarray:
@@ -71,21 +87,19 @@ class OracleState:
         for b in (range(c.num_seqs) if seqs is None else seqs):
             k, v = wl.prior_kv(b)
             if k.shape[0]:
-                oracle.cache_write(raw_bits(k), raw_bits(v), wl.prior_slots(b), self.kc, self.vc,
-                                   c.dtype)
+                oracle_write(c, raw_bits(k), raw_bits(v), wl.prior_slots(b), self.kc, self.vc)
         self.steps_written = 0
 
     def write_step(self, step: int) -> None:
         c = self.wl.cfg
-        oracle.cache_write(raw_bits(self.step_k[step]), raw_bits(self.step_v[step]),
-                           self.wl.step_slots(step), self.kc, self.vc, c.dtype)
+        oracle_write(c, raw_bits(self.step_k[step]), raw_bits(self.step_v[step]),
+                     self.wl.step_slots(step), self.kc, self.vc)
         self.steps_written = step + 1
 
     def decode(self, step: int, rows: np.ndarray | None = None, threads: int = 8) -> np.ndarray:
         c = self.wl.cfg
-        return oracle.decode(raw_bits(self.q[step]), c.dtype, self.kc, self.vc, c.dtype,
-                             self.wl.block_tables, self.wl.context_lens(step), c.attn_scale(),
-                             rows=rows, threads=threads)
+        return oracle_decode(c, raw_bits(self.q[step]), self.kc, self.vc, self.wl.block_tables,
+                             self.wl.context_lens(step), rows=rows, threads=threads)
 
 
 def logical_kv(wl: Workload, b: int, step: int) -> tuple[np.ndarray, np.ndarray]:

@@ -242,3 +242,88 @@ def test_advance_step_validation(kw, status):
 
 def test_advance_step_empty_is_noop():
     assert _adv(B=0, nq=0, tok=None, samp=None, pos=None, lens=None, slots=None, bt=None) == OK
+
+# ------------------------------------------------------------------ E4M3 caches
+
+FP8 = 3
+
+
+def _cw8(**kw):
+    args = dict(k=FAKE, v=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, T=4, ks=512, vs=512, H=4, d=128,
+                NB=10, bs=16, src=BF16, kscale=0.5, vscale=0.25)
+    args.update(kw)
+    return pa.lib().pa_cache_write_fp8(args["k"], args["v"], args["slots"], args["kc"],
+                                       args["vc"], args["T"], args["ks"], args["vs"], args["H"],
+                                       args["d"], args["NB"], args["bs"], args["src"],
+                                       args["kscale"], args["vscale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=FP8), EDTYPE),          # sources are f32 / f16 / bf16
+    (dict(src=7), EDTYPE),
+    (dict(kscale=0.0), ESHAPE),
+    (dict(vscale=-1.0), ESHAPE),
+    (dict(kscale=float("inf")), ESHAPE),
+    (dict(vscale=float("nan")), ESHAPE),
+    (dict(d=96), EUNSUP),
+    (dict(bs=12), EUNSUP),
+    (dict(ks=100), ESHAPE),
+    (dict(k=None), ENULL),
+    (dict(kc=FAKE + 8), ESHAPE),
+])
+def test_cache_write_fp8_validation(kw, status):
+    assert _cw8(**kw) == status
+
+
+def test_plain_cache_write_rejects_fp8_caches():
+    assert _cw(dtype=FP8) == EDTYPE
+
+
+def _dec8(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, kscale=0.5,
+             vscale=0.25, bs=16, P=0, B=4, Hq=32, Hkv=8, d=128, NB=100, MB=64, qd=BF16, od=F32,
+             ws=None, wsb=0, flags=pa.FORCE_VALU)
+    a.update(kw)
+    return pa.lib().pa_decode_fp8(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"],
+                                  a["scale"], a["kscale"], a["vscale"], a["bs"], a["P"], a["B"],
+                                  a["Hq"], a["Hkv"], a["d"], a["NB"], a["MB"], a["qd"], a["od"],
+                                  a["ws"], a["wsb"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qd=FP8), EDTYPE),                        # queries are f32 / f16 / bf16
+    (dict(od=FP8), EDTYPE),
+    (dict(qd=F16, od=BF16), EDTYPE),               # out: f32 or the query dtype
+    (dict(kscale=0.0), ESHAPE),
+    (dict(vscale=float("inf")), ESHAPE),
+    (dict(flags=pa.FORCE_MFMA, qd=F16), EUNSUP),   # matrix cores: bfloat16 queries
+    (dict(d=96), EUNSUP),
+    (dict(ws=None, wsb=0, P=256), EWS),
+    (dict(out=None), ENULL),
+])
+def test_decode_fp8_validation(kw, status):
+    assert _dec8(**kw) == status
+
+
+def test_decode_fp8_valid_argument_sets_pass_validation():
+    """Argument sets that validate (B = 0 launches nothing)."""
+    for kw in (dict(qd=F16, od=F16), dict(qd=F32), dict(qd=BF16, od=BF16, flags=pa.FORCE_MFMA)):
+        assert _dec8(B=0, **kw) == OK
+
+
+def test_plain_decode_rejects_fp8_caches():
+    assert _dec(kvd=FP8) == EDTYPE
+
+
+def test_fp8_kernel_family_policy():
+    L = pa.lib()
+    assert L.pa_decode_kernel(32, 8, BF16, FP8, 0) == pa.FORCE_MFMA   # GQA, bf16 queries
+    assert L.pa_decode_kernel(32, 32, BF16, FP8, 0) == pa.FORCE_VALU  # MHA
+    assert L.pa_decode_kernel(32, 8, F16, FP8, 0) == pa.FORCE_VALU    # f16 queries
+    assert L.pa_decode_kernel(32, 8, F32, FP8, 0) == pa.FORCE_VALU
+    assert L.pa_decode_kernel(32, 8, F16, FP8, pa.FORCE_MFMA) == EUNSUP
+    assert L.pa_decode_kernel(32, 8, FP8, FP8, 0) == EDTYPE
+    # the workspace holds fp32 partials: it does not depend on the cache dtype
+    assert L.pa_decode_workspace_size(4, 32, 8, 128, 16, 64, 256, FP8, 0) == \
+        L.pa_decode_workspace_size(4, 32, 8, 128, 16, 64, 256, BF16, 0)
+
