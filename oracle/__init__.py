@@ -68,6 +68,10 @@ def lib():
         L.orc_decode.argtypes = [c_void_p, c_void_p, i32, c_void_p, c_void_p, i32, c_void_p,
                                  c_void_p, i32, i32, i32, i32, i64, i32, i32, f32, f32, f32,
                                  c_void_p, i64, i32]
+        L.orc_decode_mq.restype = ctypes.c_int
+        L.orc_decode_mq.argtypes = [c_void_p, c_void_p, i32, c_void_p, c_void_p, i32, c_void_p,
+                                    c_void_p, i32, i32, i32, i32, i32, i64, i32, i32, f32, f32,
+                                    f32, c_void_p, i64, i32]
         L.orc_cache_write_fp8.restype = ctypes.c_int
         L.orc_cache_write_fp8.argtypes = [c_void_p, c_void_p, c_void_p, i64, i64, i64, c_void_p,
                                           c_void_p, i32, i32, i64, i32, i32, f32, f32]
@@ -191,6 +195,33 @@ def decode(q: np.ndarray, q_dtype: str, k_cache: np.ndarray, v_cache: np.ndarray
                             d, NB, bs, MB, float(scale), float(k_scale), float(v_scale),
                             None if r is None else _ptr(r),
                             0 if r is None else r.size, int(threads)))
+    return out
+
+
+def decode_mq(q: np.ndarray, q_dtype: str, k_cache: np.ndarray, v_cache: np.ndarray,
+              kv_dtype: str, block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
+              rows: np.ndarray | None = None, threads: int = 1, k_scale: float = 1.0,
+              v_scale: float = 1.0) -> np.ndarray:
+    """Multi-query decode: q [B][Q][Hq][d]; query i of sequence b sits at position
+    context_lens[b] - Q + i and attends to positions 0 .. its own.  float64
+    [B][Q][Hq][d] (rows = (b*Q + i)*Hq + hq not requested stay NaN)."""
+    q = _raw(q, q_dtype)
+    B, Q, Hq, d = q.shape
+    NB, Hkv, nq, dx, four, X = k_cache.shape
+    bs = nq * 4
+    if dx * X != d or four != 4 or v_cache.shape != (NB, Hkv, nq, d, 4):
+        raise OracleError("cache shapes do not match q")
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if bt.shape[0] != B or cl.shape != (B,):
+        raise OracleError("block_tables/context_lens do not match batch")
+    out = np.full((B, Q, Hq, d), np.nan, dtype=np.float64)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    _check(lib().orc_decode_mq(_ptr(out), _ptr(q), DTYPE_CODES[q_dtype], _ptr(k_cache),
+                               _ptr(v_cache), DTYPE_CODES[kv_dtype], _ptr(bt), _ptr(cl), B, Q, Hq,
+                               Hkv, d, NB, bs, bt.shape[1], float(scale), float(k_scale),
+                               float(v_scale), None if r is None else _ptr(r),
+                               0 if r is None else r.size, int(threads)))
     return out
 
 

@@ -16,6 +16,10 @@
  *  - "vLLM Project Update" talk transcript, PagedAttention recap: attention that
  *    works on fixed-size blocks of the KV cache, with per-sequence
  *    logical->physical block maps managed like virtual memory pages.
+ *  - "vLLM Project Update" talk transcript, roadmap: multi-query attention
+ *    kernels for speculative decoding, where several proposed tokens of one
+ *    sequence are scored in one pass; each of them attends causally to the
+ *    context up to its own position (orc_decode_mq).
  *  - "[core] Multi Step Scheduling" pull request (vllm-project/vllm #7000),
  *    review thread on ops.advance_step: the per-step GPU state is a slot
  *    mapping, per-sequence block tables, sequence lengths and a block size.
@@ -295,6 +299,7 @@ typedef struct {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int32_t num_queries; /* query tokens per sequence */
   int64_t num_blocks;
   int32_t block_size, max_blocks_per_seq;
   double scale;
@@ -307,21 +312,27 @@ typedef struct {
 } orc_decode_job;
 
 /*
- * One output row (b, hq): out[e] = sum_t w_t v_t[e] / sum_t w_t with
+ * One output row (b, i, hq): out[e] = sum_t w_t v_t[e] / sum_t w_t with
  * s_t = scale * sum_e q[e] k_t[e], m = max_t s_t, w_t = exp(s_t - m),
  * t over the logical positions 0..L-1, K/V rows found through the block
  * table: position t lives in physical block block_tables[b][t / bs] at
- * offset t % bs.  q head hq reads kv head hq / (Hq / Hkv).
+ * offset t % bs.  q head hq reads kv head hq / (Hq / Hkv).  With Q query
+ * tokens per sequence (the last Q positions of its context_lens[b] tokens),
+ * query i sits at position context_lens[b] - Q + i and attends to the
+ * positions up to its own: L = context_lens[b] - Q + i + 1.  Q = 1 is plain
+ * decode.
  */
 static int orc_decode_row(const orc_decode_job* J, int64_t row) {
   const int64_t Hq = J->num_q_heads, Hkv = J->num_kv_heads, D = J->head_dim;
+  const int64_t Q = J->num_queries;
   const int64_t X = 16 / orc_elem_bytes(J->kv_dtype);
   const int64_t BS = J->block_size, MB = J->max_blocks_per_seq;
-  const int64_t b = row / Hq, hq = row % Hq;
+  const int64_t b = row / (Q * Hq), i = (row / Hq) % Q, hq = row % Hq;
   const int64_t group = Hq / Hkv;
   const int64_t hk = hq / group;
-  const int64_t L = J->context_lens[b];
-  if (L < 1 || L > MB * BS) return ORC_ERR_LEN;
+  const int64_t Lseq = J->context_lens[b];
+  if (Lseq < Q || Lseq > MB * BS) return ORC_ERR_LEN;
+  const int64_t L = Lseq - Q + i + 1;
 
   double* s = (double*)malloc((size_t)L * sizeof(double));
   double* acc = (double*)malloc((size_t)D * sizeof(double));
@@ -343,7 +354,7 @@ static int orc_decode_row(const orc_decode_job* J, int64_t row) {
     const int64_t quad = (phys * Hkv + hk) * (BS / 4) + o / 4;  // this token's quad
     double dot = 0.0;
     for (int64_t e = 0; e < D; ++e)
-      dot += orc_load(J->q, J->q_dtype, (b * Hq + hq) * D + e) *
+      dot += orc_load(J->q, J->q_dtype, row * D + e) *
              (orc_load(J->k_cache, J->kv_dtype, ((quad * (D / X) + e / X) * 4 + o % 4) * X + e % X) *
               J->k_scale);
     s[t] = J->scale * dot;
@@ -379,7 +390,8 @@ static int orc_decode_row(const orc_decode_job* J, int64_t row) {
 
 static void* orc_decode_worker(void* arg) {
   orc_decode_job* J = (orc_decode_job*)arg;
-  int64_t total = J->rows ? J->n_rows : (int64_t)J->num_seqs * J->num_q_heads;
+  int64_t total =
+      J->rows ? J->n_rows : (int64_t)J->num_seqs * J->num_queries * J->num_q_heads;
   for (int64_t i = J->thread_id; i < total; i += J->n_threads) {
     int64_t row = J->rows ? J->rows[i] : i;
     int st = orc_decode_row(J, row);
@@ -393,17 +405,19 @@ static void* orc_decode_worker(void* arg) {
 
 /*
  * Decode attention for all rows (rows == NULL) or for the listed rows
- * (row = b*num_q_heads + hq).  out is double [num_seqs][num_q_heads][head_dim];
- * only computed rows are written.  Rows are independent, so they are spread
- * over n_threads POSIX threads; each row's arithmetic is sequential.
+ * (row = (b*num_queries + i)*num_q_heads + hq).  q and out are
+ * [num_seqs][num_queries][num_q_heads][head_dim]; out is double and only
+ * computed rows are written.  Rows are independent, so they are spread over
+ * n_threads POSIX threads; each row's arithmetic is sequential.
  */
-int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
-               const void* v_cache, int32_t kv_dtype,
-               const int32_t* block_tables, const int32_t* context_lens,
-               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-               int32_t head_dim, int64_t num_blocks, int32_t block_size,
-               int32_t max_blocks_per_seq, float scale, float k_scale, float v_scale,
-               const int64_t* rows, int64_t n_rows, int32_t n_threads) {
+int orc_decode_mq(double* out, const void* q, int32_t q_dtype, const void* k_cache,
+                  const void* v_cache, int32_t kv_dtype,
+                  const int32_t* block_tables, const int32_t* context_lens,
+                  int32_t num_seqs, int32_t num_queries, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                  int32_t block_size, int32_t max_blocks_per_seq, float scale, float k_scale,
+                  float v_scale, const int64_t* rows, int64_t n_rows, int32_t n_threads) {
+  if (num_queries < 1) return ORC_ERR_ARG;
   if (!orc_elem_bytes(q_dtype) || q_dtype == ORC_FP8 || !orc_elem_bytes(kv_dtype))
     return ORC_ERR_ARG;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
@@ -413,7 +427,7 @@ int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
     return ORC_ERR_ARG;
   if (rows) {
     for (int64_t i = 0; i < n_rows; ++i)
-      if (rows[i] < 0 || rows[i] >= (int64_t)num_seqs * num_q_heads)
+      if (rows[i] < 0 || rows[i] >= (int64_t)num_seqs * num_queries * num_q_heads)
         return ORC_ERR_ARG;
   }
   pthread_once(&g_tables_once, orc_fill_tables);
@@ -435,6 +449,7 @@ int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
     J->num_seqs = num_seqs;
     J->num_q_heads = num_q_heads;
     J->num_kv_heads = num_kv_heads;
+    J->num_queries = num_queries;
     J->head_dim = head_dim;
     J->num_blocks = num_blocks;
     J->block_size = block_size;
@@ -463,6 +478,19 @@ int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
   for (int i = 0; i < n_threads; ++i)
     if (jobs[i].status != ORC_OK) return jobs[i].status;
   return ORC_OK;
+}
+
+/* Single-query decode: orc_decode_mq with one query token per sequence. */
+int orc_decode(double* out, const void* q, int32_t q_dtype, const void* k_cache,
+               const void* v_cache, int32_t kv_dtype,
+               const int32_t* block_tables, const int32_t* context_lens,
+               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+               int32_t head_dim, int64_t num_blocks, int32_t block_size,
+               int32_t max_blocks_per_seq, float scale, float k_scale, float v_scale,
+               const int64_t* rows, int64_t n_rows, int32_t n_threads) {
+  return orc_decode_mq(out, q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
+                       num_seqs, 1, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                       max_blocks_per_seq, scale, k_scale, v_scale, rows, n_rows, n_threads);
 }
 
 /* ---- advance step ------------------------------------------------------- */

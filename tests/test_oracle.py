@@ -557,3 +557,68 @@ def test_fp8_decode_equals_decode_of_dequantized_f32_caches():
     got = oracle.decode(q, "f32", codes_k, codes_v, "fp8", bt, lens, 0.125, k_scale=ks, v_scale=vs)
     assert np.array_equal(got, ref)
 
+# ------------------------------------------------------------------ multi-query decode
+
+def _mq_case(seed, B, Q, Hq, Hkv, d, bs, lens, dtype="f32"):
+    rng = np.random.default_rng(seed)
+    MB = max(-(-L // bs) for L in lens) + 1
+    NB = B * MB + 3
+    perm = rng.permutation(NB)
+    bt = np.full((B, MB), -1, np.int32)
+    X = 16 // (4 if dtype == "f32" else 2)
+    kc = np.zeros((NB, Hkv, bs // 4, d // X, 4, X), np.float32 if dtype == "f32" else np.uint16)
+    vc = np.zeros((NB, Hkv, bs // 4, d, 4), kc.dtype)
+    K, V = [], []
+    for b, L in enumerate(lens):
+        nb = -(-L // bs)
+        bt[b, :nb] = perm[b * MB:b * MB + nb]
+        k = rng.standard_normal((L, Hkv, d)).astype(np.float32)
+        v = rng.standard_normal((L, Hkv, d)).astype(np.float32)
+        slots = bt[b, np.arange(L) // bs].astype(np.int64) * bs + np.arange(L) % bs
+        oracle.cache_write(k.view(np.uint32), v.view(np.uint32), slots, kc.view(np.uint32),
+                           vc.view(np.uint32), "f32")
+        K.append(k.astype(np.float64))
+        V.append(v.astype(np.float64))
+    q = rng.standard_normal((B, Q, Hq, d)).astype(np.float32)
+    return q, kc.view(np.uint32), vc.view(np.uint32), bt, np.array(lens, np.int32), K, V
+
+
+@pytest.mark.parametrize("Q,Hq,Hkv", [(1, 4, 2), (3, 4, 2), (4, 2, 2), (7, 8, 1)])
+def test_multi_query_decode_brute_force(Q, Hq, Hkv):
+    """Query i of each sequence attends causally to positions 0 .. L - Q + i: contiguous
+    numpy softmax per (sequence, query, head) on the same K/V."""
+    lens = [Q, Q + 5, 37, 70]
+    d, bs = 16, 8
+    q, kc, vc, bt, cl, K, V = _mq_case(11 + Q, len(lens), Q, Hq, Hkv, d, bs, lens)
+    scale = float(np.float32(0.37))
+    got = oracle.decode_mq(q.view(np.uint32), "f32", kc, vc, "f32", bt, cl, scale)
+    g = Hq // Hkv
+    for b, L in enumerate(lens):
+        for i in range(Q):
+            n = L - Q + i + 1
+            for hq in range(Hq):
+                s = K[b][:n, hq // g] @ q[b, i, hq].astype(np.float64) * scale
+                w = scipy.special.softmax(s)
+                ref = w @ V[b][:n, hq // g]
+                assert np.allclose(got[b, i, hq], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_multi_query_decode_equals_single_queries_on_truncated_contexts():
+    """Row (b, i) of a Q-query decode is the single-query decode of sequence b with context
+    length L - Q + i + 1 (the oracle's plain entry, bit for bit)."""
+    Q, Hq, Hkv, d, bs = 4, 4, 2, 16, 8
+    lens = [4, 9, 33]
+    q, kc, vc, bt, cl, _, _ = _mq_case(5, len(lens), Q, Hq, Hkv, d, bs, lens)
+    got = oracle.decode_mq(q.view(np.uint32), "f32", kc, vc, "f32", bt, cl, 0.25)
+    for i in range(Q):
+        single = oracle.decode(np.ascontiguousarray(q[:, i]).view(np.uint32), "f32", kc, vc,
+                               "f32", bt, cl - Q + i + 1, 0.25)
+        assert np.array_equal(got[:, i], single)
+
+
+def test_multi_query_decode_rejects_contexts_shorter_than_the_queries():
+    q, kc, vc, bt, cl, _, _ = _mq_case(6, 2, 3, 2, 2, 16, 8, [3, 10])
+    with pytest.raises(oracle.OracleError):
+        oracle.decode_mq(q[:, :3].copy().view(np.uint32)[:, :, :, :], "f32", kc, vc, "f32", bt,
+                         np.array([2, 10], np.int32), 0.25)
+
