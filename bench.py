@@ -64,6 +64,9 @@ def parse_args(argv=None):
                     help="waves per decode work item (0: library picks)")
     ap.add_argument("--kv-cache", choices=["native", "fp8"], default="native",
                     help="fp8: the workload's E4M3-cache variant (workloads 4 and 5)")
+    ap.add_argument("--queries", type=int, default=1,
+                    help="query tokens per sequence (several: multi-query decode, as when draft "
+                         "tokens are verified; the oracle baseline is then skipped)")
     ap.add_argument("--no-work-list", action="store_true",
                     help="one workgroup per possible decode item instead of the persistent grid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -360,7 +363,8 @@ def run(args):
                                         kdt), dtype=kdt, device=dev)
     vc = torch.empty(pa.value_cache_shape(wl.num_blocks, c.num_kv_heads, c.head_dim,
                                           c.block_size), dtype=kdt, device=dev)
-    want_cpu = not args.no_cpu_baseline
+    Q = args.queries
+    want_cpu = not args.no_cpu_baseline and Q == 1
     okc = ovc = None
     if want_cpu:
         import oracle
@@ -388,10 +392,12 @@ def run(args):
     MB = wl.max_blocks_per_seq
     p_eff = part if part else pa.decode_partition_size(c.num_seqs, c.num_q_heads, c.num_kv_heads,
                                                        c.head_dim, c.block_size, MB, kdt, flags)
-    ws_bytes = pa.decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                        c.block_size, MB, part, kdt, flags)
+    ws_bytes = pa.decode_workspace_size(c.num_seqs * Q, c.num_q_heads, c.num_kv_heads,
+                                        c.head_dim, c.block_size, MB, part, kdt, flags)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # zeroed once
-    out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+    if Q > 1:
+        qs = wl.multi_queries(Q).to(dev).unsqueeze(0).expand(c.steps, -1, -1, -1, -1)
+    out = torch.empty(qs.shape[1:], dtype=torch.float32, device=dev)
     scale = c.attn_scale()
     stream = torch.cuda.current_stream(dev)
 
@@ -406,10 +412,20 @@ def run(args):
         write_kv(c, sk[s], sv[s], slots[s], k_l, v_l)
         if ev is not None:
             ev[1].record(stream)
-        decode_partitions_kv(c, out, qs[s], k_l, v_l, bt, ctx[s], part, ws, flags)
+        if Q > 1:
+            ks, vs = c.fp8_scales if c.kv_dtype == "fp8" else (1.0, 1.0)
+            pa.decode_mq_partitions(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part,
+                                    ws, flags, ks, vs)
+        else:
+            decode_partitions_kv(c, out, qs[s], k_l, v_l, bt, ctx[s], part, ws, flags)
         if ev is not None:
             ev[2].record(stream)
-        pa.decode_merge(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws, flags)
+        if Q > 1:
+            pa.decode_mq_merge(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
+                               flags)
+        else:
+            pa.decode_merge(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
+                            flags)
         if ev is not None:
             ev[3].record(stream)
 
@@ -433,7 +449,7 @@ def run(args):
     achieved = kv / (dec_ms * 1e-3) / 1e9
 
     graph = None
-    if args.graph and c.steps > 1:
+    if args.graph and c.steps > 1 and Q == 1:
         graph = graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags)
     attainable = None if args.no_stream_probe else stream_probe(dev)
     traffic = None
@@ -443,7 +459,8 @@ def run(args):
         if rec.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("traffic_bytes")
 
-    kname = f"decode_{pa.decode_kernel(c.num_q_heads, c.num_kv_heads, qdt, kdt, flags)}_kernel"
+    family = pa.decode_mq_kernel(Q, c.num_q_heads, c.num_kv_heads, qdt, kdt, flags)
+    kname = f"decode_{family}_kernel"
     result = {
         "metric": "paged decode attention: achieved KV HBM GB/s (% peak) + tokens/s, 1 MI355X",
         "value": round(value, 2),
@@ -460,6 +477,7 @@ def run(args):
         "data": "synthetic (seeded N(0,1) q/K/V, shuffled block pool; no dataset)",
         "config": {"workload": c.name, **{k: v for k, v in wl.describe().items() if k != "workload"},
                    "partition_size": int(p_eff), "kernel_flags": args.flags,
+                   "queries_per_seq": Q,
                    "work_list": pa.decode_work_list(c.num_seqs, c.num_q_heads, c.num_kv_heads,
                                                     c.head_dim, c.block_size,
                                                     wl.max_blocks_per_seq, int(p_eff), qdt, kdt,
@@ -469,7 +487,7 @@ def run(args):
                                                      wl.max_blocks_per_seq, int(p_eff), qdt, kdt,
                                                      flags)},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1),
+        "tokens_per_s": round(c.num_seqs * Q / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(kv),
         "write_ms": round(write_ms, 5),
         "decode_partitions_ms": round(dec_ms, 5),

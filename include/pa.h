@@ -242,6 +242,61 @@ int pa_decode_merge(void* out, const void* q, const void* k_cache, const void* v
                     uint32_t flags, void* stream);
 
 /*
+ * pa_decode_mq / pa_decode_mq_partitions / pa_decode_mq_merge -- decode of
+ * several query tokens per sequence ("vLLM Project Update" talk, roadmap:
+ * multi-query attention kernels for speculative decoding, which score the
+ * proposed tokens of a sequence in one pass).  q and out are
+ * [num_seqs][num_queries][num_q_heads][head_dim]; context_lens[b] counts all
+ * of sequence b's tokens including its num_queries new ones, whose K/V are
+ * already in the caches: query i sits at position context_lens[b] -
+ * num_queries + i and attends to positions 0 .. its own (causal among the
+ * new tokens):
+ *   out[b][i][hq] = softmax_t(scale * q[b][i][hq] . k_t) . v_t,
+ *                   t = 0 .. context_lens[b] - num_queries + i.
+ * A query whose position would be negative (context_lens[b] < num_queries)
+ * gets a zero row.  num_queries = 1 is pa_decode.  The (query, head) rows of
+ * a kv head form the matrix cores' columns: num_queries * heads_per_item <= 16
+ * (instantiated widths 1-8, 10, 12, 16); the vector-ALU kernel takes up to 8.
+ *   num_queries    1 .. 16
+ *   kv_dtype       any cache dtype; k_scale, v_scale as in pa_decode_fp8 (pass
+ *                  1 for the unscaled types)
+ *   workspace      pa_decode_workspace_size(num_seqs * num_queries, ...) bytes
+ * Other arguments, errors and the phase split as pa_decode.
+ */
+int pa_decode_mq(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                 float k_scale, float v_scale, int32_t block_size, int32_t partition_size,
+                 int32_t num_seqs, int32_t num_queries, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                 int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype,
+                 int32_t out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
+                 void* stream);
+int pa_decode_mq_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, float k_scale, float v_scale, int32_t block_size,
+                            int32_t partition_size, int32_t num_seqs, int32_t num_queries,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
+                            int32_t kv_dtype, int32_t out_dtype, void* workspace,
+                            size_t workspace_bytes, uint32_t flags, void* stream);
+int pa_decode_mq_merge(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, float scale,
+                       float k_scale, float v_scale, int32_t block_size, int32_t partition_size,
+                       int32_t num_seqs, int32_t num_queries, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype,
+                       int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                       uint32_t flags, void* stream);
+
+/*
+ * The decode kernel family pa_decode_mq runs with num_queries query tokens
+ * per sequence (as pa_decode_kernel, which is the num_queries = 1 case);
+ * PA_ERR_UNSUPPORTED when no kernel holds the query rows.
+ */
+int32_t pa_decode_mq_kernel(int32_t num_queries, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t q_dtype, int32_t kv_dtype, uint32_t flags);
+
+/*
  * pa_decode_fp8 / pa_decode_fp8_partitions -- pa_decode / pa_decode_partitions
  * over E4M3 caches written by pa_cache_write_fp8: the attention of each query
  * over the cache elements stored * k_scale (keys) and stored * v_scale

@@ -97,6 +97,13 @@ def lib() -> ctypes.CDLL:
         for name in ("pa_decode_fp8", "pa_decode_fp8_partitions"):
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name).argtypes = dec8_args
+        decmq_args = [vp, vp, vp, vp, vp, vp, f32, f32, f32, i32, i32, i32, i32, i32, i32, i32,
+                      i64, i32, i32, i32, i32, vp, sz, u32, vp]
+        for name in ("pa_decode_mq", "pa_decode_mq_partitions", "pa_decode_mq_merge"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = decmq_args
+        L.pa_decode_mq_kernel.restype = i32
+        L.pa_decode_mq_kernel.argtypes = [i32, i32, i32, i32, i32, u32]
         L.pa_cache_write_fp8.restype = ctypes.c_int
         L.pa_cache_write_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i64, i32,
                                          i32, f32, f32, vp]
@@ -325,3 +332,61 @@ def decode_fp8_partitions(out, q, k_cache, v_cache, block_tables, context_lens, 
     _require(k_cache.dtype == torch.float8_e4m3fn, "decode_fp8 needs E4M3 caches")
     _decode_call("pa_decode_fp8_partitions", out, q, k_cache, v_cache, block_tables, context_lens,
                  scale, block_size, partition_size, workspace, flags, (k_scale, v_scale))
+
+
+def decode_mq_kernel(num_queries: int, num_q_heads: int, num_kv_heads: int,
+                     q_dtype: torch.dtype, kv_dtype: torch.dtype, flags: int = AUTO) -> str:
+    """Kernel family of a decode with num_queries query tokens per sequence."""
+    k = lib().pa_decode_mq_kernel(num_queries, num_q_heads, num_kv_heads, _DTYPE[q_dtype],
+                                  _DTYPE[kv_dtype], flags)
+    _check(min(k, 0))
+    return {FORCE_VALU: "valu", FORCE_MFMA: "mfma"}[k]
+
+
+def _decode_mq_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                    block_size, partition_size, workspace, flags, k_scale, v_scale):
+    _require(q.dim() == 4 and q.is_contiguous(), "q must be contiguous [B][Q][Hq][d]")
+    B, Q, Hq, d = q.shape
+    _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Q][Hq][d]")
+    NB, Hkv, bs, d2 = _cache_dims(k_cache, v_cache)
+    _require(bs == block_size and d2 == d, "cache shapes do not match block_size / head_dim")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(),
+             "block_tables must be contiguous int32 [B][max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
+             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
+    MB = block_tables.shape[1]
+    need = decode_workspace_size(B * Q, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype, flags)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        if fn_name != "pa_decode_mq":
+            raise PAError(-5, "the phase entry points need the caller's workspace")
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(getattr(lib(), fn_name)(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), float(k_scale),
+        float(v_scale), block_size, partition_size, B, Q, Hq, Hkv, d, NB, MB, _dt(q),
+        _dt(k_cache), _dt(out), ws_ptr, ws_bytes, flags, _stream(q.device)))
+
+
+def decode_mq(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+              partition_size=0, workspace=None, flags=AUTO, k_scale=1.0, v_scale=1.0) -> None:
+    """Decode of Q query tokens per sequence (q, out: [B][Q][Hq][d]): query i of sequence b
+    sits at position context_lens[b] - Q + i and attends causally up to it."""
+    _decode_mq_call("pa_decode_mq", out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                    block_size, partition_size, workspace, flags, k_scale, v_scale)
+
+
+def decode_mq_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                         block_size, partition_size=0, workspace=None, flags=AUTO,
+                         k_scale=1.0, v_scale=1.0) -> None:
+    _decode_mq_call("pa_decode_mq_partitions", out, q, k_cache, v_cache, block_tables,
+                    context_lens, scale, block_size, partition_size, workspace, flags, k_scale,
+                    v_scale)
+
+
+def decode_mq_merge(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                    partition_size=0, workspace=None, flags=AUTO) -> None:
+    _decode_mq_call("pa_decode_mq_merge", out, q, k_cache, v_cache, block_tables, context_lens,
+                    scale, block_size, partition_size, workspace, flags, 1.0, 1.0)

@@ -204,7 +204,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
   const bool listed = args.list_ints > 0;
   int n_work = (int)blockIdx.x + 1, step = 1;
   if (listed) {
-    n_work = build_work_list(args, dyn_lds) * args.num_kv_heads * (args.group / G);
+    n_work = build_work_list(args, dyn_lds) * args.num_kv_heads *
+             (args.group / args.heads_per_item);
     step = (int)gridDim.x;
   }
   // Round r takes entry r * gridDim.x + blockIdx.x, or the mirrored one on
@@ -216,7 +217,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
   while (it < n_work) {
     {
     KernArgs& a = *fresh_args();
-    const int chunks = a.group / G;
+    // columns: G = Q x Gh, column n = (query n / Gh, head hq0 + n % Gh)
+    const int Q = a.num_queries;
+    const int Gh = a.heads_per_item;
+    const int chunks = a.group / Gh;
     const int per_seq = a.num_kv_heads * chunks;
     const int W = a.waves;
     const int tid = fresh_tid();
@@ -246,7 +250,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       part = (int)gridDim.y - 1 - (int)blockIdx.y;
     }
     const int h = hc / chunks;
-    const int hq0 = h * a.group + (hc % chunks) * G;
+    const int hq0 = h * a.group + (hc % chunks) * Gh;
+    // the q / out row of column c: query c / Gh, head hq0 + c % Gh
+    auto row_of = [&](int c) -> int64_t {
+      const int qc = c / Gh;
+      return ((int64_t)b * Q + qc) * a.num_q_heads + hq0 + (c - qc * Gh);
+    };
 
     // Start-up loads that do not depend on the context length go out together
     // with it: the first block-id window (clamped to the table width; entries
@@ -256,13 +265,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     const int L_in = a.context_lens[b];
     const int bt_first = bt[min((t_begin >> lbs) + lane, a.max_blocks_per_seq - 1)];
 
-    // queries: column n = head hq0 + n (zero beyond the group)
+    // queries: column n = query row row_n (zero beyond the G columns)
     vec8 qv[KC];
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       if (n < G) {
-        const char* qp = reinterpret_cast<const char*>(a.q) +
-                         (((int64_t)b * a.num_q_heads + hq0 + n) * D + 32 * c + 8 * j) * 2;
+        const char* qp =
+            reinterpret_cast<const char*>(a.q) + (row_of(n) * D + 32 * c + 8 * j) * 2;
         qv[c] = *reinterpret_cast<const vec8*>(qp);
       } else {
 #pragma unroll
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       if (part == 0 && wave == 0) {
         for (int g = 0; g < G; ++g)
           for (int e = lane; e < D; e += 64)
-            store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
+            store_elem(a.out, row_of(g) * D + e, 0.0f, a.out_dtype);
       }
       goto next_item;
     }
@@ -283,6 +292,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     if (part >= n_parts) goto next_item;
     const int t_end = min(t_begin + P, L);
     const int last_blk = (L - 1) >> lbs;
+    // query qi sits at position L - Q + qi and sees the positions up to its own
+    const int lim_lo = L - Q + 1;        // the smallest column limit (uniform)
+    const int lim_n = lim_lo + n / Gh;  // this lane's column
     const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
     const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
 
@@ -342,10 +354,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       vec4 vv[VC];
 #pragma unroll
       for (int c = 0; c < VC; ++c) vv[c] = St::v(buf.v[c]);
-      if (t0 + kChunk > t_stop) {  // uniform: mask tokens past the partition / context
-        const int nv = t_stop - t0 - 4 * j;  // valid tokens of this lane's run
+      if (t0 + kChunk > min(t_stop, lim_lo)) {  // uniform: the chunk reaches a limit
+        // scores past the partition / context or past the column's query are
+        // masked; values past the context are zeroed (they may hold anything)
+        const int nv = t_stop - t0 - 4 * j;  // tokens of this lane's run inside the range
+        const int ns = min(t_stop, lim_n) - t0 - 4 * j;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = r < nv ? s[r] : -INFINITY;
+        for (int r = 0; r < 4; ++r) s[r] = r < ns ? s[r] : -INFINITY;
 #pragma unroll
         for (int c = 0; c < VC; ++c)
 #pragma unroll
@@ -356,13 +371,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
+      // a column with every score so far masked keeps m = -inf; exponents are
+      // then taken against 0 so that they give 0, not NaN
+      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = fast_exp2(m - m_ref);
       m = m_new;
       vec4 phi, plo;
       float ps = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(s[r] - m_new);
+        const float p = fast_exp2(s[r] - m_ref);
         ps += p;
         const scalar hi = (scalar)p;
         phi[r] = hi;
@@ -416,10 +434,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     l += __shfl_xor(l, 32);
     if (W > 1) {
       // Merge the waves: M = max_w m_w, l = sum_w 2^(m_w - M) l_w, and the
-      // accumulators likewise.  A wave without chunks has m = -inf, l = 0 and
-      // zero accumulators; wave 0 always has a chunk, so M is finite.  Every
-      // wave parks its rescaled accumulators in LDS, then the whole workgroup
-      // sums them and stores.
+      // accumulators likewise.  A wave without tokens for a column has m =
+      // -inf, l = 0 and zero accumulators; when no wave has any (a query
+      // whose position lies before this partition), the column's l is 0 and
+      // exponents are taken against 0.  Every wave parks its rescaled
+      // accumulators in LDS, then the whole workgroup sums them and stores.
       float* red_m = red;         // [W][16]
       float* red_l = red + 64;    // [W][16]
       float* red_o = red + 128;   // [W][G][D + 4] (rows padded against bank conflicts)
@@ -431,7 +450,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       __syncthreads();
       float M = -INFINITY;
       for (int w = 0; w < W; ++w) M = fmaxf(M, red_m[w * 16 + n]);
-      const float sc = fast_exp2(m - M);
+      const float sc = fast_exp2(m - (M == -INFINITY ? 0.0f : M));
       if (n < G) {
 #pragma unroll
         for (int c = 0; c < VC; ++c) {
@@ -446,14 +465,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         const int g = e / D, d = e - g * D;
         float Mg = -INFINITY;
         for (int w = 0; w < W; ++w) Mg = fmaxf(Mg, red_m[w * 16 + g]);
+        const float Mref = Mg == -INFINITY ? 0.0f : Mg;
         float lt = 0.0f, x = 0.0f;
         for (int w = 0; w < W; ++w) {
-          lt += red_l[w * 16 + g] * fast_exp2(red_m[w * 16 + g] - Mg);
+          lt += red_l[w * 16 + g] * fast_exp2(red_m[w * 16 + g] - Mref);
           x += red_o[(w * G + g) * RS + d];
         }
-        const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
+        const int64_t row_id = row_of(g);
         if (n_parts == 1) {
-          store_elem(a.out, row_id * D + d, x * a.v_scale / lt, a.out_dtype);
+          store_elem(a.out, row_id * D + d, lt > 0.0f ? x * a.v_scale / lt : 0.0f, a.out_dtype);
         } else {
           const int64_t slot = row_id * a.max_partitions + part;
           a.ws_acc[slot * D + d] = x * a.v_scale;
@@ -467,9 +487,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       goto next_item;
     }
     if (n < G) {
-      const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + n;
+      const int64_t row_id = row_of(fresh_tid() & 15);  // re-derived: not held through the loop
       if (n_parts == 1) {
-        const float inv = a.v_scale / l;
+        const float inv = l > 0.0f ? a.v_scale / l : 0.0f;  // l = 0: a query before position 0
 #pragma unroll
         for (int c = 0; c < VC; ++c)
 #pragma unroll
@@ -510,10 +530,10 @@ size_t merge_lds_bytes(int waves, int heads, int head_dim) {
 template <Elem KV, int D>
 hipError_t dispatch_g(const DecodeArgs& a, int64_t items_x, hipStream_t s) {
   const bool ub = a.block_size >= 16;
-  const size_t lds = (size_t)a.list_ints * sizeof(int) +
-                     merge_lds_bytes(a.waves, a.heads_per_item, D);
+  const int cols = a.num_queries * a.heads_per_item;  // tile columns (template G)
+  const size_t lds = (size_t)a.list_ints * sizeof(int) + merge_lds_bytes(a.waves, cols, D);
   const void* fn = nullptr;
-  switch (a.heads_per_item) {
+  switch (cols) {
 #define PA_CASE(GG)                                                                   \
   case GG:                                                                            \
     fn = ub ? reinterpret_cast<const void*>(&decode_mfma_kernel<KV, D, GG, true>)     \

@@ -158,7 +158,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
   const bool listed = args.list_ints > 0;
   int n_work = (int)blockIdx.x + 1, step = 1;
   if (listed) {
-    n_work = build_work_list(args, dyn_lds) * args.num_kv_heads * (args.group / G);
+    n_work = build_work_list(args, dyn_lds) * args.num_kv_heads *
+             (args.group / args.heads_per_item);
     step = (int)gridDim.x;
   }
   // Round r takes entry r * gridDim.x + blockIdx.x, or the mirrored one on
@@ -170,7 +171,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
   while (it < n_work) {
     {
     KernArgs& a = *fresh_args();
-    const int chunks = a.group / G;
+    // rows: G = Q x Gh, row g = (query g / Gh, head hq0 + g % Gh)
+    const int Q = a.num_queries;
+    const int Gh = a.heads_per_item;
+    const int chunks = a.group / Gh;
     const int per_seq = a.num_kv_heads * chunks;
     const int W = a.waves;
     const int tid = fresh_tid();
@@ -204,7 +208,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
       part = (int)gridDim.y - 1 - (int)blockIdx.y;
     }
     const int h = hc / chunks;
-    const int hq0 = h * a.group + (hc % chunks) * G;
+    const int hq0 = h * a.group + (hc % chunks) * Gh;
+    auto row_of = [&](int g) -> int64_t {
+      return ((int64_t)b * Q + g / Gh) * a.num_q_heads + hq0 + g % Gh;
+    };
 
     // start-up loads that do not depend on the context length go out with it
     const int t_begin = part * P;
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
     float qf[G][EPL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int64_t qb = ((int64_t)b * a.num_q_heads + hq0 + g) * D + c * EPL;
+      const int64_t qb = row_of(g) * D + c * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) qf[g][e] = load_elem_f32(a.q, qb + e, a.q_dtype);
     }
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
       if (part == 0 && wave == 0) {
         for (int g = 0; g < G; ++g)
           for (int e = lane; e < D; e += 64)
-            store_elem(a.out, ((int64_t)b * a.num_q_heads + hq0 + g) * D + e, 0.0f, a.out_dtype);
+            store_elem(a.out, row_of(g) * D + e, 0.0f, a.out_dtype);
       }
       goto next_item;
     }
@@ -234,6 +241,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
     if (part >= n_parts) goto next_item;
     const int t_end = min(t_begin + P, L);
     const int last_blk = (L - 1) >> lbs;
+    // query g / Gh sits at position L - Q + g / Gh and sees the positions up to it
+    const int lim_lo = L - Q + 1;
     const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
     const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
 
@@ -285,14 +294,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
       for (int i = 0; i < NI; ++i) {
         float kf[EPL];
         widen_key<KV>(buf.k[i], kf);
-        const bool valid = (t0 + i * TPI + row) < t_stop;
+        const int t = t0 + i * TPI + row;
+        const bool valid = t < t_stop;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float part_dot = 0.0f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) part_dot = fmaf(qf[g][e], kf[e], part_dot);
           const float dot = group_sum<RL>(part_dot);
-          s[g][i] = valid ? dot * a.scale_log2 : -INFINITY;
+          s[g][i] = valid && t < lim_lo + g / Gh ? dot * a.scale_log2 : -INFINITY;
         }
       }
 
@@ -304,12 +314,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
         for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[g][i]);
         mx = across_groups_max<RL>(mx);
         const float m_new = fmaxf(m[g], mx);
-        const float alpha = fast_exp2(m[g] - m_new);
+        // a row with every score so far masked keeps m = -inf: exponents are
+        // then taken against 0 so that they give 0, not NaN
+        const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = fast_exp2(m[g] - m_ref);
         m[g] = m_new;
         float psum = 0.0f;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          s[g][i] = fast_exp2(s[g][i] - m_new);
+          s[g][i] = fast_exp2(s[g][i] - m_ref);
           psum += s[g][i];
         }
         lrow[g] = lrow[g] * alpha + psum;
@@ -378,10 +391,11 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
 #pragma unroll
     for (int g = 0; g < G; ++g) lsum[g] = across_groups_sum<RL>(lrow[g]);
     if (W > 1) {
-      // Merge the waves by log-sum-exp (a wave without tiles has m = -inf,
-      // l = 0 and zero accumulators; wave 0 always has a tile): every wave
-      // parks its m, l and accumulators in LDS, then the whole workgroup
-      // rescales, sums and stores.
+      // Merge the waves by log-sum-exp (a wave without tokens for a row has
+      // m = -inf, l = 0 and zero accumulators; when no wave has any, the row's
+      // l is 0 and exponents are taken against 0): every wave parks its m, l
+      // and accumulators in LDS, then the whole workgroup rescales, sums and
+      // stores.
       float* red_m = red;               // [W][G]
       float* red_l = red + 4 * G;       // [W][G]
       float* red_o = red + 8 * G;       // [W][G][D]
@@ -401,15 +415,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
         const int g = e / D, d = e - g * D;
         float Mg = -INFINITY;
         for (int w = 0; w < W; ++w) Mg = fmaxf(Mg, red_m[w * G + g]);
+        const float Mref = Mg == -INFINITY ? 0.0f : Mg;
         float lt = 0.0f, x = 0.0f;
         for (int w = 0; w < W; ++w) {
-          const float sc = fast_exp2(red_m[w * G + g] - Mg);
+          const float sc = fast_exp2(red_m[w * G + g] - Mref);
           lt += red_l[w * G + g] * sc;
           x += red_o[(w * G + g) * D + d] * sc;
         }
-        const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
+        const int64_t row_id = row_of(g);
         if (n_parts == 1) {
-          store_elem(a.out, row_id * D + d, x * a.v_scale / lt, a.out_dtype);
+          store_elem(a.out, row_id * D + d, lt > 0.0f ? x * a.v_scale / lt : 0.0f, a.out_dtype);
         } else {
           const int64_t slot = row_id * a.max_partitions + part;
           a.ws_acc[slot * D + d] = x * a.v_scale;
@@ -425,9 +440,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float l = lsum[g];
-      const int64_t row_id = (int64_t)b * a.num_q_heads + hq0 + g;
+      const int64_t row_id = row_of(g);
       if (n_parts == 1) {
-        const float inv = a.v_scale / l;
+        const float inv = l > 0.0f ? a.v_scale / l : 0.0f;  // l = 0: a query before position 0
 #pragma unroll
         for (int dd = 0; dd < DPL; ++dd)
           store_elem(a.out, row_id * D + dd * 64 + lane, acc[g][dd] * inv, a.out_dtype);
@@ -459,10 +474,10 @@ size_t merge_lds_bytes(int waves, int heads, int head_dim) {
 
 template <Elem KV, int D>
 hipError_t dispatch_g(const DecodeArgs& a, int64_t items_x, hipStream_t s) {
-  const size_t lds = (size_t)a.list_ints * sizeof(int) +
-                     merge_lds_bytes(a.waves, a.heads_per_item, D);
+  const int rows = a.num_queries * a.heads_per_item;  // rows per item (template G)
+  const size_t lds = (size_t)a.list_ints * sizeof(int) + merge_lds_bytes(a.waves, rows, D);
   const void* fn = nullptr;
-  switch (a.heads_per_item) {
+  switch (rows) {
 #define PA_CASE(GG)                                                       \
   case GG:                                                                \
     fn = reinterpret_cast<const void*>(&decode_valu_kernel<KV, D, GG>);   \

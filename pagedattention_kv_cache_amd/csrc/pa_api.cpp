@@ -34,25 +34,29 @@ int log2_exact(int32_t v) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Largest divisor of g that is <= cap: the q heads one work item handles.
+// Largest divisor of g that is <= cap: the q heads one work item handles
+// (0 when cap < 1).
 int32_t heads_per_item(int32_t g, int32_t cap) {
   for (int32_t h = cap < g ? cap : g; h >= 1; --h)
     if (g % h == 0) return h;
-  return 1;
+  return 0;
 }
 
-// Matrix-core tile width: the largest divisor of g that one 16-column tile
-// holds and that is instantiated.
-int32_t mfma_heads_per_item(int32_t g) {
+// Matrix-core tile: the q heads per item h, the largest divisor of g whose Q
+// x h columns (Q query tokens per sequence) fit one 16-column tile with an
+// instantiated width; 0 when there is none.
+int32_t mfma_heads_per_item(int32_t g, int32_t num_queries) {
   for (int32_t h = g < 16 ? g : 16; h >= 1; --h)
-    if (g % h == 0 && pa::mfma_supports_heads(h)) return h;
-  return 1;
+    if (g % h == 0 && num_queries * h <= 16 && pa::mfma_supports_heads(num_queries * h))
+      return h;
+  return 0;
 }
 
-// Kernel family: the matrix-core kernel serves 16-bit caches queried in the
-// same dtype once a GQA group has at least two q heads per kv head (a
-// multi-column tile); plain multi-head attention and fp32 stay on the
-// vector-ALU kernel unless the caller forces the matrix cores.
+// The vector-ALU kernel's items: up to 8 rows (Q x h).
+int32_t valu_heads_per_item(int32_t g, int32_t num_queries) {
+  return heads_per_item(g, 8 / num_queries);
+}
+
 // Queries in the cache dtype or fp32; with E4M3 caches any of f32, f16, bf16.
 bool valid_q_dtype(int32_t q_dtype, int32_t kv_dtype) {
   if (q_dtype != PA_DTYPE_F32 && q_dtype != PA_DTYPE_F16 && q_dtype != PA_DTYPE_BF16)
@@ -75,12 +79,25 @@ bool mfma_eligible(int32_t kv_dtype, int32_t q_dtype) {
   return kv_dtype != PA_DTYPE_F32 && q_dtype == kv_dtype;
 }
 
-bool use_mfma(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t group) {
-  const bool eligible = mfma_eligible(kv_dtype, q_dtype);
+// Kernel family.  The matrix-core kernel takes eligible dtypes once an item
+// has at least two query rows -- a GQA group of two or more q heads, or two
+// or more query tokens per sequence -- i.e. a multi-column tile; single-row
+// items and fp32 run on the vector-ALU kernel unless the caller forces the
+// matrix cores.  Returns 0 (neither) when no kernel can hold the Q x h rows.
+int32_t pick_kernel(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t group,
+                    int32_t num_queries) {
+  const bool mfma_ok =
+      mfma_eligible(kv_dtype, q_dtype) && mfma_heads_per_item(group, num_queries) > 0;
+  const bool valu_ok = valu_heads_per_item(group, num_queries) > 0;
   const uint32_t kernel = flags & PA_DECODE_KERNEL_MASK;
-  if (kernel == PA_DECODE_FORCE_MFMA) return eligible;
-  if (kernel == PA_DECODE_FORCE_VALU) return false;
-  return eligible && group >= 2;
+  if (kernel == PA_DECODE_FORCE_MFMA) return mfma_ok ? PA_DECODE_FORCE_MFMA : 0;
+  if (kernel == PA_DECODE_FORCE_VALU) return valu_ok ? PA_DECODE_FORCE_VALU : 0;
+  if (mfma_ok && group * num_queries >= 2) return PA_DECODE_FORCE_MFMA;
+  return valu_ok ? PA_DECODE_FORCE_VALU : (mfma_ok ? PA_DECODE_FORCE_MFMA : 0);
+}
+
+bool use_mfma(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t group) {
+  return pick_kernel(flags, kv_dtype, q_dtype, group, 1) == PA_DECODE_FORCE_MFMA;
 }
 
 // Flag bits this library knows, with a valid kernel choice.
@@ -201,7 +218,8 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_NULL: return "a required pointer is NULL";
     case PA_ERR_SHAPE: return "a size is out of range, inconsistent or misaligned";
     case PA_ERR_DTYPE: return "unknown dtype or unsupported dtype combination";
-    case PA_ERR_UNSUPPORTED: return "head_dim, block_size, group size or kernel choice not supported";
+    case PA_ERR_UNSUPPORTED:
+      return "head_dim, block_size, group size or kernel choice not supported";
     case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_size()";
     case PA_ERR_HIP: return "a HIP kernel launch failed";
     default: return "unknown pa_status";
@@ -322,15 +340,22 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return pick_partition(s);
 }
 
-int32_t pa_decode_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t q_dtype,
-                         int32_t kv_dtype, uint32_t flags) {
+int32_t pa_decode_mq_kernel(int32_t num_queries, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t q_dtype, int32_t kv_dtype, uint32_t flags) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return PA_ERR_SHAPE;
+  if (num_queries < 1 || num_queries > 16) return PA_ERR_SHAPE;
   if (!elem_bytes(q_dtype) || !elem_bytes(kv_dtype)) return PA_ERR_DTYPE;
   if (!valid_q_dtype(q_dtype, kv_dtype)) return PA_ERR_DTYPE;
   if (!valid_flags(flags)) return PA_ERR_UNSUPPORTED;
   if (forces_mfma(flags) && !mfma_eligible(kv_dtype, q_dtype)) return PA_ERR_UNSUPPORTED;
-  return use_mfma(flags, kv_dtype, q_dtype, num_q_heads / num_kv_heads) ? PA_DECODE_FORCE_MFMA
-                                                                        : PA_DECODE_FORCE_VALU;
+  const int32_t k =
+      pick_kernel(flags, kv_dtype, q_dtype, num_q_heads / num_kv_heads, num_queries);
+  return k ? k : PA_ERR_UNSUPPORTED;
+}
+
+int32_t pa_decode_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t q_dtype,
+                         int32_t kv_dtype, uint32_t flags) {
+  return pa_decode_mq_kernel(1, num_q_heads, num_kv_heads, q_dtype, kv_dtype, flags);
 }
 
 namespace {
@@ -395,7 +420,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                 int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream, int phase,
-                float k_scale = 1.0f, float v_scale = 1.0f) {
+                float k_scale = 1.0f, float v_scale = 1.0f, int32_t num_queries = 1) {
   DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                 kv_dtype, flags};
   int st = check_shape(s);
@@ -408,6 +433,10 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
     return PA_ERR_SHAPE;
   if (forces_mfma(flags) && !mfma_eligible(kv_dtype, q_dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_queries < 1 || num_queries > 16) return PA_ERR_SHAPE;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t kernel = pick_kernel(flags, kv_dtype, q_dtype, group, num_queries);
+  if (!kernel) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
@@ -416,10 +445,15 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   int32_t p = partition_size ? partition_size : pick_partition(s);
   if (p > max_ctx) p = (int32_t)max_ctx;
   const int64_t np = n_partitions(s, p);
-  const size_t need = workspace_bytes_for(s, p);
+  // the workspace holds a (m, l) pair and a partial vector per query row
+  DecodeShape rows_shape = s;
+  if ((int64_t)num_seqs * num_queries > 0x7fffffffLL) return PA_ERR_SHAPE;
+  rows_shape.num_seqs = num_seqs * num_queries;
+  const size_t need = workspace_bytes_for(rows_shape, p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
-  if (np > 65535 || (int64_t)num_seqs * num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+  if (np > 65535 || (int64_t)num_seqs * num_queries * num_q_heads > 0x7fffffffLL)
+    return PA_ERR_SHAPE;
 
   pa::DecodeArgs a;
   a.out = out;
@@ -428,7 +462,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
+  const size_t rows = (size_t)num_seqs * num_queries * num_q_heads * (size_t)np;
   char* ws = reinterpret_cast<char*>(workspace);
   a.ws_ml = need ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_acc = need ? reinterpret_cast<float*>(ws + round_up(rows * 2 * sizeof(float))) : nullptr;
@@ -438,9 +472,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
-  a.group = num_q_heads / num_kv_heads;
-  const bool mfma = use_mfma(flags, kv_dtype, q_dtype, a.group);
-  a.heads_per_item = mfma ? mfma_heads_per_item(a.group) : heads_per_item(a.group, 8);
+  a.group = group;
+  const bool mfma = kernel == PA_DECODE_FORCE_MFMA;
+  a.heads_per_item =
+      mfma ? mfma_heads_per_item(group, num_queries) : valu_heads_per_item(group, num_queries);
+  a.num_queries = num_queries;
   a.block_size = block_size;
   a.log2_block_size = log2_exact(block_size);
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -496,6 +532,25 @@ int pa_decode_merge(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kMerg
       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,         \
       int32_t max_blocks_per_seq, int32_t q_dtype, int32_t out_dtype, void *workspace,         \
       size_t workspace_bytes, uint32_t flags, void *stream
+
+#define PA_DECODE_MQ_PARAMS                                                                    \
+  void *out, const void *q, const void *k_cache, const void *v_cache,                          \
+      const int32_t *block_tables, const int32_t *context_lens, float scale, float k_scale,    \
+      float v_scale, int32_t block_size, int32_t partition_size, int32_t num_seqs,             \
+      int32_t num_queries, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,        \
+      int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype,       \
+      int32_t out_dtype, void *workspace, size_t workspace_bytes, uint32_t flags, void *stream
+#define PA_DECODE_MQ_ARGS(phase)                                                               \
+  out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, partition_size,     \
+      num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, q_dtype,   \
+      kv_dtype, out_dtype, workspace, workspace_bytes, flags, stream, phase, k_scale, v_scale,  \
+      num_queries
+
+int pa_decode_mq(PA_DECODE_MQ_PARAMS) { return decode_impl(PA_DECODE_MQ_ARGS(kBoth)); }
+int pa_decode_mq_partitions(PA_DECODE_MQ_PARAMS) {
+  return decode_impl(PA_DECODE_MQ_ARGS(kPartitions));
+}
+int pa_decode_mq_merge(PA_DECODE_MQ_PARAMS) { return decode_impl(PA_DECODE_MQ_ARGS(kMerge)); }
 
 int pa_decode_fp8(PA_DECODE_FP8_PARAMS) {
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,

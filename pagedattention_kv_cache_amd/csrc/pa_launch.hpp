@@ -48,6 +48,8 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t group;       // num_q_heads / num_kv_heads
   int32_t heads_per_item;  // q heads handled by one work item
+  int32_t num_queries;     // query tokens per sequence: q, out are [B][Q][Hq][d]; an item
+                           // handles Q x heads_per_item rows (the kernels' template G)
   int32_t block_size;
   int32_t log2_block_size;
   int32_t max_blocks_per_seq;

@@ -37,7 +37,7 @@ DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 POISON_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8": 0x7F}
 
 # stream indices under SeedSequence(seed).spawn(...)
-_S_LENGTHS, _S_POOL, _S_Q, _S_STEP, _S_SEQ, _S_SAMPLED = range(6)
+_S_LENGTHS, _S_POOL, _S_Q, _S_STEP, _S_SEQ, _S_SAMPLED, _S_MQ = range(7)
 VOCAB = 128256  # token ids drawn for the "sampled" next tokens (a Llama-3-sized vocabulary)
 
 
@@ -168,7 +168,7 @@ class Workload:
     def __init__(self, cfg: DecodeConfig):
         self.cfg = cfg
         root = np.random.SeedSequence(cfg.seed)
-        self._ss = root.spawn(6)
+        self._ss = root.spawn(7)
         n = cfg.num_seqs
         self._seq_ss = self._ss[_S_SEQ].spawn(n)
         rng_len = np.random.Generator(np.random.PCG64(self._ss[_S_LENGTHS]))
@@ -243,6 +243,14 @@ class Workload:
         rng = np.random.Generator(np.random.PCG64(self._ss[_S_Q]))
         q = rng.standard_normal((c.steps, c.num_seqs, c.num_q_heads, c.head_dim), dtype=np.float32)
         return round_to(q, c.dtype)
+
+    def multi_queries(self, num_queries: int) -> torch.Tensor:
+        """q of a multi-query decode (several new tokens per sequence, e.g. draft tokens
+        being verified): [B][num_queries][Hq][d] in the storage dtype."""
+        c = self.cfg
+        rng = np.random.Generator(np.random.PCG64(self._ss[_S_MQ]))
+        shape = (c.num_seqs, num_queries, c.num_q_heads, c.head_dim)
+        return round_to(rng.standard_normal(shape, dtype=np.float32), c.dtype)
 
     def step_kv(self) -> tuple[torch.Tensor, torch.Tensor]:
         """New-token K, V for every step: [steps][B][Hkv][d] in the storage dtype."""

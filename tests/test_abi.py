@@ -327,3 +327,63 @@ def test_fp8_kernel_family_policy():
     assert L.pa_decode_workspace_size(4, 32, 8, 128, 16, 64, 256, FP8, 0) == \
         L.pa_decode_workspace_size(4, 32, 8, 128, 16, 64, 256, BF16, 0)
 
+
+
+# ------------------------------------------------------------------ multi-query decode
+
+def _decmq(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, kscale=1.0,
+             vscale=1.0, bs=16, P=0, B=4, nq=4, Hq=32, Hkv=8, d=128, NB=100, MB=64, qd=BF16,
+             kvd=BF16, od=F32, ws=None, wsb=0, flags=pa.FORCE_MFMA, fn="pa_decode_mq")
+    a.update(kw)
+    return getattr(pa.lib(), a["fn"])(
+        a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["kscale"],
+        a["vscale"], a["bs"], a["P"], a["B"], a["nq"], a["Hq"], a["Hkv"], a["d"], a["NB"],
+        a["MB"], a["qd"], a["kvd"], a["od"], a["ws"], a["wsb"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nq=0), ESHAPE),
+    (dict(nq=17), ESHAPE),
+    (dict(nq=9, Hq=8, Hkv=8), EUNSUP),            # 9 columns: no tile width, too many rows
+    (dict(nq=5, Hq=8, Hkv=8, flags=pa.FORCE_VALU), OK),  # B = 0 below
+    (dict(nq=16, Hq=16, Hkv=8, flags=pa.FORCE_VALU), EUNSUP),  # the vector ALUs hold 8 rows
+    (dict(nq=3, flags=pa.FORCE_MFMA, qd=F32), EUNSUP),
+    (dict(kscale=0.0), ESHAPE),
+    (dict(Hq=30), ESHAPE),
+    (dict(d=96), EUNSUP),
+    (dict(out=None), ENULL),
+    (dict(ws=None, wsb=0, P=256), EWS),
+    (dict(fn="pa_decode_mq_partitions", ws=None, wsb=0, P=256), EWS),
+    (dict(fn="pa_decode_mq_merge", ws=None, wsb=0, P=256), EWS),
+])
+def test_decode_mq_validation(kw, status):
+    if status == OK:
+        kw = dict(kw, B=0)
+    assert _decmq(**kw) == status
+
+
+def test_decode_mq_workspace_counts_query_rows():
+    """The multi-query workspace is the single-query one of num_seqs * num_queries rows;
+    a buffer 16 bytes short of it is rejected."""
+    L = pa.lib()
+    need = L.pa_decode_workspace_size(4 * 4, 32, 8, 128, 16, 64, 256, BF16, 0)
+    assert need > L.pa_decode_workspace_size(4, 32, 8, 128, 16, 64, 256, BF16, 0)
+    assert _decmq(P=256, ws=FAKE, wsb=need - 16) == EWS
+
+
+def test_decode_mq_kernel_policy():
+    L = pa.lib()
+    k = L.pa_decode_mq_kernel
+    assert k(1, 32, 8, BF16, BF16, 0) == L.pa_decode_kernel(32, 8, BF16, BF16, 0)
+    assert k(2, 32, 32, F16, F16, 0) == pa.FORCE_MFMA     # MHA, 2 query tokens: 2 columns
+    assert k(4, 32, 8, BF16, BF16, 0) == pa.FORCE_MFMA
+    assert k(16, 8, 8, BF16, BF16, 0) == pa.FORCE_MFMA    # 16 columns of one head
+    assert k(16, 8, 8, BF16, BF16, pa.FORCE_VALU) == EUNSUP
+    assert k(8, 8, 8, F32, F32, 0) == pa.FORCE_VALU       # fp32: vector ALUs, up to 8 rows
+    assert k(10, 8, 8, F32, F32, 0) == EUNSUP
+    for bad in (9, 11, 13, 14, 15):                      # no instantiated tile width
+        assert k(bad, 8, 8, BF16, BF16, 0) == EUNSUP
+    assert k(4, 32, 8, BF16, FP8, 0) == pa.FORCE_MFMA
+    assert k(4, 32, 8, F16, FP8, 0) == pa.FORCE_VALU
+    assert k(0, 32, 8, BF16, BF16, 0) == ESHAPE
