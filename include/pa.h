@@ -74,7 +74,9 @@ typedef enum pa_status {
   PA_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
   PA_ERR_UNSUPPORTED = -4, /* head_dim / block_size / group size not built */
   PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
-  PA_ERR_HIP = -6          /* a HIP launch failed */
+  PA_ERR_HIP = -6,         /* a HIP launch failed */
+  PA_ERR_CAPACITY = -7,    /* block manager: not enough free blocks (nothing changed) */
+  PA_ERR_SEQUENCE = -8     /* block manager: unknown, duplicate or swapped-out sequence */
 } pa_status;
 
 /* pa_decode flags.  Bits 0-1: which decode kernel family to use. */

@@ -119,12 +119,40 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_waves.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, u32]
         L.pa_decode_work_list.restype = i32
         L.pa_decode_work_list.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, u32]
+        _declare_blocks(L)
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_status_string.argtypes = [i32]
         L.pa_abi_version.restype = i32
         L.pa_abi_version.argtypes = []
         _lib = L
     return _lib
+
+
+def _declare_blocks(L) -> None:
+    vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+    sigs = {
+        "pa_bm_create": [i64, i32, i64, u32, vp],
+        "pa_bm_add_sequence": [vp, i64, vp, i32, vp],
+        "pa_bm_append": [vp, vp, vp, i32, vp, vp, vp],
+        "pa_bm_fork": [vp, i64, i64],
+        "pa_bm_free": [vp, i64],
+        "pa_bm_mark_computed": [vp, i64],
+        "pa_bm_slots": [vp, i64, i32, i32, vp],
+        "pa_bm_block_tables": [vp, vp, i32, i32, vp, vp],
+        "pa_bm_swap_out": [vp, i64, vp, vp],
+        "pa_bm_swap_in": [vp, i64, vp, vp],
+        "pa_bm_num_free_blocks": [vp, vp],
+        "pa_bm_num_free_host_blocks": [vp, vp],
+        "pa_bm_seq_info": [vp, i64, vp, vp],
+        "pa_bm_ref_count": [vp, i32, vp],
+        "pa_copy_blocks": [vp, vp, vp, i32, i64, i64, vp],
+        "pa_swap_blocks": [vp, vp, vp, i32, i64, vp],
+    }
+    for name, args in sigs.items():
+        getattr(L, name).restype = ctypes.c_int
+        getattr(L, name).argtypes = args
+    L.pa_bm_destroy.restype = None
+    L.pa_bm_destroy.argtypes = [vp]
 
 
 def status_string(status: int) -> str:
@@ -390,3 +418,174 @@ def decode_mq_merge(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                     partition_size=0, workspace=None, flags=AUTO) -> None:
     _decode_mq_call("pa_decode_mq_merge", out, q, k_cache, v_cache, block_tables, context_lens,
                     scale, block_size, partition_size, workspace, flags, 1.0, 1.0)
+
+
+# ---------------------------------------------------------------- block management
+# (include/pa_blocks.h: a host-side block manager and the device block copies)
+
+PREFIX_CACHING = 1
+
+
+def _np():
+    import numpy
+    return numpy
+
+
+def _host_ptr(a) -> int:
+    return a.ctypes.data
+
+
+class BlockManager:
+    """Host-side allocator of a paged cache's physical blocks (libpa.so): free list,
+    reference-counted sharing with copy-on-write, prefix caching and host swap."""
+
+    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0,
+                 prefix_caching: bool = False):
+        h = ctypes.c_void_p()
+        _check(lib().pa_bm_create(num_blocks, block_size, num_host_blocks,
+                                  PREFIX_CACHING if prefix_caching else 0, ctypes.byref(h)))
+        self._h = h
+        self.block_size = block_size
+        self.prefix_caching = prefix_caching
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            lib().pa_bm_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _ids(self, tokens, n):
+        np = _np()
+        if tokens is None:
+            return None, None
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _require(t.shape == (n,), "tokens must hold one id per token")
+        return t, _host_ptr(t)
+
+    def add_sequence(self, seq_id: int, tokens=None, num_tokens: int | None = None) -> int:
+        """New sequence; returns the number of leading tokens served by cached blocks."""
+        n = len(tokens) if num_tokens is None else num_tokens
+        t, tp = self._ids(tokens, n)
+        cached = ctypes.c_int32(0)
+        _check(lib().pa_bm_add_sequence(self._h, seq_id, tp, n, ctypes.byref(cached)))
+        return cached.value
+
+    def append(self, seq_ids, tokens=None):
+        """One token per sequence: (slots int64 [n], copy-on-write pairs int32 [k][2])."""
+        np = _np()
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        t, tp = self._ids(tokens, n)
+        slots = np.empty(n, np.int64)
+        copies = np.empty((max(n, 1), 2), np.int32)
+        nc = ctypes.c_int32(0)
+        _check(lib().pa_bm_append(self._h, _host_ptr(ids), tp, n, _host_ptr(slots),
+                                  _host_ptr(copies), ctypes.byref(nc)))
+        return slots, copies[: nc.value].copy()
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pa_bm_fork(self._h, parent, child))
+
+    def free(self, seq_id: int) -> None:
+        _check(lib().pa_bm_free(self._h, seq_id))
+
+    def mark_computed(self, seq_id: int) -> None:
+        _check(lib().pa_bm_mark_computed(self._h, seq_id))
+
+    def slots(self, seq_id: int, start: int, n: int):
+        np = _np()
+        out = np.empty(n, np.int64)
+        _check(lib().pa_bm_slots(self._h, seq_id, start, n, _host_ptr(out) if n else None))
+        return out
+
+    def block_tables(self, seq_ids, max_blocks_per_seq: int):
+        """(block_tables int32 [n][max_blocks_per_seq] (-1 padded), context_lens int32 [n])."""
+        np = _np()
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        bt = np.empty((n, max_blocks_per_seq), np.int32)
+        lens = np.empty(n, np.int32)
+        _check(lib().pa_bm_block_tables(self._h, _host_ptr(ids), n, max_blocks_per_seq,
+                                        _host_ptr(bt), _host_ptr(lens)))
+        return bt, lens
+
+    def _swap(self, fn, seq_id: int):
+        np = _np()
+        length, _ = self.seq_info(seq_id)
+        pairs = np.empty((max(1, -(-length // self.block_size)), 2), np.int32)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, seq_id, _host_ptr(pairs), ctypes.byref(n)))
+        return pairs[: n.value].copy()
+
+    def swap_out(self, seq_id: int):
+        """(device block, host block) pairs to copy out."""
+        return self._swap(lib().pa_bm_swap_out, seq_id)
+
+    def swap_in(self, seq_id: int):
+        """(host block, device block) pairs to copy in."""
+        return self._swap(lib().pa_bm_swap_in, seq_id)
+
+    @property
+    def num_free_blocks(self) -> int:
+        v = ctypes.c_int64(0)
+        _check(lib().pa_bm_num_free_blocks(self._h, ctypes.byref(v)))
+        return v.value
+
+    @property
+    def num_free_host_blocks(self) -> int:
+        v = ctypes.c_int64(0)
+        _check(lib().pa_bm_num_free_host_blocks(self._h, ctypes.byref(v)))
+        return v.value
+
+    def seq_info(self, seq_id: int):
+        """(length, resident)."""
+        n, r = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pa_bm_seq_info(self._h, seq_id, ctypes.byref(n), ctypes.byref(r)))
+        return n.value, bool(r.value)
+
+    def ref_count(self, block: int) -> int:
+        v = ctypes.c_int32(0)
+        _check(lib().pa_bm_ref_count(self._h, block, ctypes.byref(v)))
+        return v.value
+
+
+def _block_bytes(cache: torch.Tensor) -> int:
+    return cache[0].numel() * cache.element_size()
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor) -> None:
+    """Copy-on-write on the device: block src -> dst of both caches for each row of pairs
+    (a device int32 tensor [n][2])."""
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    _require(k_cache.shape[0] == v_cache.shape[0] and _block_bytes(k_cache) ==
+             _block_bytes(v_cache), "caches must hold blocks of the same size")
+    _require(pairs.dtype == torch.int32 and pairs.is_contiguous() and pairs.dim() == 2
+             and pairs.shape[1] == 2 and pairs.device == k_cache.device,
+             "pairs must be a contiguous int32 [n][2] tensor on the caches' device")
+    _check(lib().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(),
+                                pairs.shape[0], k_cache.shape[0], _block_bytes(k_cache),
+                                _stream(k_cache.device)))
+
+
+def swap_blocks(dst_pool: torch.Tensor, src_pool: torch.Tensor, pairs) -> None:
+    """Block copies between a device cache and a pinned host pool of the same block layout
+    (pairs: host int32 [n][2] of (src block, dst block)), on the device's current stream."""
+    np = _np()
+    _require(dst_pool.is_contiguous() and src_pool.is_contiguous(), "pools must be contiguous")
+    _require(_block_bytes(dst_pool) == _block_bytes(src_pool) and dst_pool.dtype ==
+             src_pool.dtype, "pools must hold blocks of the same layout")
+    p = np.ascontiguousarray(pairs, dtype=np.int32)
+    _require(p.ndim == 2 and p.shape[1] == 2, "pairs must be [n][2]")
+    _require(bool((p[:, 0] < src_pool.shape[0]).all() and (p[:, 1] < dst_pool.shape[0]).all()),
+             "block ids past the pools")
+    dev = dst_pool.device if dst_pool.is_cuda else src_pool.device
+    _require(dev.type == "cuda" and (dst_pool.is_pinned() or src_pool.is_pinned()),
+             "one pool must be a device cache, the other pinned host memory")
+    _check(lib().pa_swap_blocks(dst_pool.data_ptr(), src_pool.data_ptr(),
+                                _host_ptr(p) if p.shape[0] else None, p.shape[0],
+                                _block_bytes(dst_pool), _stream(dev)))

@@ -1,4 +1,5 @@
-"""Build libpa.so (the HIP library behind include/pa.h) for gfx950 with hipcc.
+"""Build libpa.so (the HIP library behind include/pa.h and include/pa_blocks.h)
+for gfx950 with hipcc.
 
 Each source compiles to its own object in parallel, then one shared object is
 linked in-tree next to this file, where the Python binding loads it.
@@ -18,7 +19,7 @@ LIB = os.path.join(HERE, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pa_api.cpp", "cache_write.hip", "decode_valu.hip", "decode_mfma.hip",
-           "decode_reduce.hip", "advance_step.hip"]
+           "decode_reduce.hip", "advance_step.hip", "copy_blocks.hip", "block_manager.cpp"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

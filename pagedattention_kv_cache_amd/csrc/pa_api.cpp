@@ -222,6 +222,8 @@ const char* pa_status_string(int32_t status) {
       return "head_dim, block_size, group size or kernel choice not supported";
     case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_size()";
     case PA_ERR_HIP: return "a HIP kernel launch failed";
+    case PA_ERR_CAPACITY: return "not enough free KV blocks (nothing was changed)";
+    case PA_ERR_SEQUENCE: return "unknown, duplicate or swapped-out sequence id";
     default: return "unknown pa_status";
   }
 }

@@ -140,6 +140,21 @@ def custom_config(name: str, lengths: Sequence[int], num_q_heads: int, num_kv_he
                         num_blocks, scale, cache_dtype, fp8_scales)
 
 
+def token_kv(tokens, positions, num_kv_heads: int, head_dim: int, dtype: str,
+             seed: int) -> tuple[torch.Tensor, torch.Tensor]:
+    """K, V rows [n][num_kv_heads][head_dim] (storage dtype) of the given tokens at the
+    given positions: a seeded function of (token id, position) alone, so that sequences
+    with equal token prefixes have equal KV there (what block sharing relies on)."""
+    n = len(tokens)
+    k = np.empty((n, num_kv_heads, head_dim), np.float32)
+    v = np.empty_like(k)
+    for i, (t, p) in enumerate(zip(tokens, positions)):
+        rng = np.random.default_rng([seed, int(t), int(p)])
+        kv = rng.standard_normal((2, num_kv_heads, head_dim), dtype=np.float32)
+        k[i], v[i] = kv[0], kv[1]
+    return round_to(k, dtype), round_to(v, dtype)
+
+
 def round_to(x: np.ndarray, dtype: str) -> torch.Tensor:
     """float32 numpy -> CPU torch tensor of the storage dtype (RNE)."""
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))

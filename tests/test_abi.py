@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
 
 OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+ECAP, ESEQ = -7, -8
 F32, F16, BF16 = 0, 1, 2
 FAKE = 0x10000  # a 16-byte aligned non-null value; never dereferenced
 
@@ -46,6 +47,15 @@ def test_library_loads_and_exports_header_symbols():
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
 
 
+def test_library_exports_the_block_header():
+    L = pa.lib()
+    names = _declared_functions(os.path.join(ROOT, "include", "pa_blocks.h"))
+    assert {"pa_bm_create", "pa_bm_append", "pa_bm_fork", "pa_bm_mark_computed",
+            "pa_bm_swap_out", "pa_copy_blocks", "pa_swap_blocks"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libpa.so does not export {n}"
+
+
 def test_probe_library_exports_its_header():
     probe = ctypes.CDLL(os.path.join(ROOT, "pagedattention_kv_cache_amd", "libpa_probe.so"))
     names = _declared_functions(os.path.join(ROOT, "include", "pa_probe.h"))
@@ -66,7 +76,8 @@ def test_status_strings_and_version():
     assert L.pa_abi_version() == 1
     fallback = pa.status_string(-99)
     assert fallback == "unknown pa_status"
-    texts = [pa.status_string(st) for st in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP)]
+    texts = [pa.status_string(st)
+             for st in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ECAP, ESEQ)]
     assert all(t and t != fallback for t in texts)
     assert len(set(texts)) == len(texts)
 
@@ -387,3 +398,54 @@ def test_decode_mq_kernel_policy():
     assert k(4, 32, 8, BF16, FP8, 0) == pa.FORCE_MFMA
     assert k(4, 32, 8, F16, FP8, 0) == pa.FORCE_VALU
     assert k(0, 32, 8, BF16, BF16, 0) == ESHAPE
+
+
+# ------------------------------------------------------------------ block copies
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), ESHAPE),
+    (dict(nb=0), ESHAPE),
+    (dict(bb=0), ESHAPE),
+    (dict(bb=24), ESHAPE),                     # not a multiple of 16
+    (dict(kc=None), ENULL),
+    (dict(pairs=None), ENULL),
+    (dict(kc=FAKE + 8), ESHAPE),
+    (dict(n=0, kc=None, vc=None, pairs=None), OK),   # nothing to copy, nothing launched
+])
+def test_copy_blocks_validation(kw, status):
+    a = dict(kc=FAKE, vc=FAKE, pairs=FAKE, n=3, nb=10, bb=4096)
+    a.update(kw)
+    assert pa.lib().pa_copy_blocks(a["kc"], a["vc"], a["pairs"], a["n"], a["nb"], a["bb"],
+                                   None) == status
+
+
+def test_swap_blocks_validation():
+    L = pa.lib()
+    bad = (ctypes.c_int32 * 4)(0, 1, -1, 2)
+    assert L.pa_swap_blocks(FAKE, FAKE, bad, 2, 4096, None) == ESHAPE
+    assert L.pa_swap_blocks(FAKE, FAKE, bad, -1, 4096, None) == ESHAPE
+    assert L.pa_swap_blocks(FAKE, FAKE, bad, 1, 0, None) == ESHAPE
+    assert L.pa_swap_blocks(None, FAKE, bad, 1, 4096, None) == ENULL
+    assert L.pa_swap_blocks(None, None, None, 0, 4096, None) == OK
+
+
+def test_block_manager_argument_validation():
+    L = pa.lib()
+    h = ctypes.c_void_p()
+    assert L.pa_bm_create(0, 16, 0, 0, ctypes.byref(h)) == ESHAPE
+    assert L.pa_bm_create(8, 0, 0, 0, ctypes.byref(h)) == ESHAPE
+    assert L.pa_bm_create(8, 16, -1, 0, ctypes.byref(h)) == ESHAPE
+    assert L.pa_bm_create(8, 16, 0, 2, ctypes.byref(h)) == ESHAPE
+    assert L.pa_bm_create(8, 16, 0, 0, None) == ENULL
+    assert L.pa_bm_create(8, 16, 0, 1, ctypes.byref(h)) == OK
+    try:
+        assert L.pa_bm_add_sequence(h, 1, None, 5, None) == ENULL  # caching needs the ids
+        assert L.pa_bm_add_sequence(h, 1, None, -1, None) == ESHAPE
+        assert L.pa_bm_add_sequence(None, 1, None, 0, None) == ENULL
+        n = ctypes.c_int32(0)
+        assert L.pa_bm_append(h, None, None, 0, None, None, ctypes.byref(n)) == OK
+        assert L.pa_bm_append(h, None, None, 1, None, None, ctypes.byref(n)) == ENULL
+        assert L.pa_bm_ref_count(h, 8, ctypes.byref(n)) == ESHAPE
+        assert L.pa_bm_free(h, 42) == ESEQ
+    finally:
+        L.pa_bm_destroy(h)
