@@ -67,6 +67,8 @@ def parse_args(argv=None):
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per sequence (several: multi-query decode, as when draft "
                          "tokens are verified; the oracle baseline is then skipped)")
+    ap.add_argument("--grid", choices=["auto", "grid", "sorted", "work_list"], default="auto",
+                    help="how workgroups find their items (default: the library's choice)")
     ap.add_argument("--no-work-list", action="store_true",
                     help="one workgroup per possible decode item instead of the persistent grid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -347,6 +349,8 @@ def run(args):
         flags |= pa.WAVES_FLAG[args.waves]
     if args.no_work_list:
         flags |= pa.NO_WORK_LIST
+    flags |= {"auto": 0, "grid": pa.NO_WORK_LIST, "sorted": pa.SORTED_GRID,
+              "work_list": pa.WORK_LIST}[args.grid]
     part = cfg.partition_size if args.partition_size < 0 else args.partition_size
 
     if args.copy_probe:
@@ -478,10 +482,9 @@ def run(args):
         "config": {"workload": c.name, **{k: v for k, v in wl.describe().items() if k != "workload"},
                    "partition_size": int(p_eff), "kernel_flags": args.flags,
                    "queries_per_seq": Q,
-                   "work_list": pa.decode_work_list(c.num_seqs, c.num_q_heads, c.num_kv_heads,
-                                                    c.head_dim, c.block_size,
-                                                    wl.max_blocks_per_seq, int(p_eff), qdt, kdt,
-                                                    flags),
+                   "grid": pa.decode_grid(c.num_seqs * Q, c.num_q_heads, c.num_kv_heads,
+                                          c.head_dim, c.block_size, wl.max_blocks_per_seq,
+                                          int(p_eff), qdt, kdt, flags),
                    "waves_per_item": pa.decode_waves(c.num_seqs, c.num_q_heads, c.num_kv_heads,
                                                      c.head_dim, c.block_size,
                                                      wl.max_blocks_per_seq, int(p_eff), qdt, kdt,

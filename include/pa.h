@@ -91,9 +91,23 @@ typedef enum pa_status {
 #define PA_DECODE_WAVES_2 8u
 #define PA_DECODE_WAVES_4 12u
 #define PA_DECODE_WAVES_MASK 12u
-/* Bit 4: one workgroup per possible (sequence, head, partition) item instead
- * of a persistent grid walking the list of items that hold tokens. */
+/* Bits 4-5: how a partitioned launch's workgroups find their work items
+ * (sequence, kv head, head chunk, partition).  0 lets the library pick.
+ *   PA_DECODE_NO_WORK_LIST  one workgroup per possible item, in grid order
+ *                           (the items that hold no tokens exit at once);
+ *   PA_DECODE_SORTED_GRID   one workgroup per possible item, the items that
+ *                           hold tokens first and the longest first (a
+ *                           one-workgroup kernel orders them on the device
+ *                           before the decode, in the workspace);
+ *   PA_DECODE_WORK_LIST     a persistent grid (as many workgroups as fit on
+ *                           the device) walking the list of items that hold
+ *                           tokens, which each workgroup builds in LDS.
+ * A choice that does not apply (one pass; a list or order too large) falls
+ * back to grid order. */
 #define PA_DECODE_NO_WORK_LIST 16u
+#define PA_DECODE_SORTED_GRID 32u
+#define PA_DECODE_WORK_LIST 48u
+#define PA_DECODE_GRID_MASK 48u
 
 /*
  * pa_cache_write -- for every token i in [0, num_tokens) whose
@@ -197,10 +211,10 @@ int pa_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
  *                  Calls that may run at the same time need distinct
  *                  workspaces.
  *   flags          PA_DECODE_AUTO, or a PA_DECODE_FORCE_* kernel choice OR-ed
- *                  with a PA_DECODE_WAVES_* split (either part may be 0 =
- *                  library picks) and optionally PA_DECODE_NO_WORK_LIST;
- *                  other bits set, or both kernel bits, give
- *                  PA_ERR_UNSUPPORTED
+ *                  with a PA_DECODE_WAVES_* split and a grid choice
+ *                  (PA_DECODE_NO_WORK_LIST, _SORTED_GRID or _WORK_LIST; each
+ *                  part may be 0 = library picks); other bits set, or both
+ *                  kernel bits, give PA_ERR_UNSUPPORTED
  * The result does not depend on partition_size, the kernel family or the
  * waves per item beyond floating-point rounding (fp32 accumulation
  * throughout).
@@ -365,6 +379,16 @@ int32_t pa_decode_work_list(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                             int32_t partition_size, int32_t q_dtype, int32_t kv_dtype,
                             uint32_t flags);
+
+/*
+ * The grid pa_decode runs these arguments on: PA_DECODE_NO_WORK_LIST (one
+ * workgroup per possible item in grid order; also every one-pass launch),
+ * PA_DECODE_SORTED_GRID or PA_DECODE_WORK_LIST; a negative pa_status for
+ * invalid arguments.  For pa_decode_mq pass num_seqs * num_queries.
+ */
+int32_t pa_decode_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                       int32_t partition_size, int32_t q_dtype, int32_t kv_dtype, uint32_t flags);
 
 /*
  * Workspace bytes pa_decode needs for these arguments (partition_size as

@@ -33,6 +33,11 @@ WAVES_FLAG = {1: WAVES_1, 2: WAVES_2, 4: WAVES_4}
 # one workgroup per possible (sequence, head, partition) item instead of the
 # persistent grid over the items that hold tokens
 NO_WORK_LIST = 16
+# the items that hold tokens first, longest first (ordered on the device)
+SORTED_GRID = 32
+# a persistent grid walking the list of items that hold tokens
+WORK_LIST = 48
+GRID_NAMES = {NO_WORK_LIST: "grid", SORTED_GRID: "sorted", WORK_LIST: "work_list"}
 # torch.float8_e4m3fn: the OCP E4M3 KV-cache storage type (caches only)
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3}
 
@@ -119,6 +124,8 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_waves.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, u32]
         L.pa_decode_work_list.restype = i32
         L.pa_decode_work_list.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, u32]
+        L.pa_decode_grid.restype = i32
+        L.pa_decode_grid.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, u32]
         _declare_blocks(L)
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_status_string.argtypes = [i32]
@@ -276,6 +283,17 @@ def decode_work_list(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_di
                                   _DTYPE[kv_dtype], flags)
     _check(min(r, 0))
     return bool(r)
+
+
+def decode_grid(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                block_size: int, max_blocks_per_seq: int, partition_size: int,
+                q_dtype: torch.dtype, kv_dtype: torch.dtype, flags: int = AUTO) -> str:
+    """The grid decode runs: "grid" (grid order), "sorted" or "work_list"."""
+    r = lib().pa_decode_grid(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, partition_size, _DTYPE[q_dtype],
+                             _DTYPE[kv_dtype], flags)
+    _check(min(r, 0))
+    return GRID_NAMES[r]
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -244,6 +244,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       const int item = it / per_seq;
       hc = it - item * per_seq;
       work_item(dyn_lds, a.max_partitions, item, cursor, b, part);
+    } else if (a.order) {
+      const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+      const int64_t e = lin / per_seq;
+      hc = (int)(lin - e * per_seq);
+      const int entry = a.order[e];
+      if (entry < 0) goto next_item;  // every item is taken: the rest of the grid is empty
+      b = entry / a.max_partitions;
+      part = entry - b * a.max_partitions;
     } else {
       b = it / per_seq;
       hc = it - b * per_seq;

@@ -1,0 +1,77 @@
+// decode_order.hip -- longest-first order of a partitioned decode's work items.
+//
+// The host does not read the context lengths, so a partitioned decode
+// launches one workgroup per *possible* (sequence, partition) item, most of
+// which are empty on a batch of mixed lengths.  Dispatched in grid order,
+// empty workgroups that come first hold back the start of the real ones, and
+// full-size items that come last stretch the end of the launch.  This kernel
+// (one workgroup, run just before the decode on the same stream) writes the
+// non-empty items in order of decreasing token count, then -1 for the rest;
+// decode workgroup i takes entry i, so the grid starts with the longest
+// items and ends with the empty ones, which exit at once.
+//
+// Entry = b * max_partitions + partition.  Items of equal size (in 16-token
+// chunks) may come in any order: an item's result does not depend on the
+// workgroup that computes it.
+#include "pa_device.hpp"
+#include "pa_launch.hpp"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kBins = kThreads;  // item sizes in 16-token chunks; larger ones share the last bin
+
+// Size bin of partition `part` of a sequence of L tokens: its 16-token chunks.
+__device__ __forceinline__ int item_bin(int L, int part, int P) {
+  return min((min(L - part * P, P) + 15) / 16, kBins - 1);
+}
+
+// Items of a sequence of (clamped) length L: its partitions; an empty
+// sequence still has one, which writes its zero rows.
+__device__ __forceinline__ int seq_items(int L, int P, int np) {
+  return L <= 0 ? 1 : min((L + P - 1) / P, np);
+}
+
+__global__ __launch_bounds__(kThreads) void decode_order_kernel(DecodeArgs a, int32_t* order) {
+  __shared__ int hist[kBins];
+  __shared__ int start[kBins];
+  const int tid = threadIdx.x;
+  const int np = a.max_partitions, P = a.partition_size, B = a.num_seqs;
+  for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  for (int b = tid; b < B; b += kThreads) {
+    const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
+    const int n = seq_items(L, P, np);
+    for (int p = 0; p < n; ++p) atomicAdd(&hist[L <= 0 ? 0 : item_bin(L, p, P)], 1);
+  }
+  __syncthreads();
+  // start[bin] = items in larger bins (an exclusive scan from the top bin down)
+  int v = hist[kBins - 1 - tid];
+  for (int off = 1; off < kBins; off *= 2) {
+    start[tid] = v;
+    __syncthreads();
+    if (tid >= off) v += start[tid - off];
+    __syncthreads();
+  }
+  start[kBins - 1 - tid] = v - hist[kBins - 1 - tid];  // v: the tid + 1 largest bins
+  __syncthreads();
+  const int total = start[0] + hist[0];
+  __syncthreads();
+  for (int b = tid; b < B; b += kThreads) {
+    const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
+    const int n = seq_items(L, P, np);
+    for (int p = 0; p < n; ++p)
+      order[atomicAdd(&start[L <= 0 ? 0 : item_bin(L, p, P)], 1)] = b * np + p;
+  }
+  for (int e = total + tid; e < B * np; e += kThreads) order[e] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_decode_order(const DecodeArgs& a, int32_t* order, hipStream_t s) {
+  hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kThreads), 0, s, a, order);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -102,7 +102,7 @@ bool use_mfma(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t group) 
 
 // Flag bits this library knows, with a valid kernel choice.
 bool valid_flags(uint32_t flags) {
-  if (flags & ~(PA_DECODE_KERNEL_MASK | PA_DECODE_WAVES_MASK | PA_DECODE_NO_WORK_LIST))
+  if (flags & ~(PA_DECODE_KERNEL_MASK | PA_DECODE_WAVES_MASK | PA_DECODE_GRID_MASK))
     return false;
   return (flags & PA_DECODE_KERNEL_MASK) != PA_DECODE_KERNEL_MASK;
 }
@@ -176,21 +176,45 @@ int32_t pick_waves(const DecodeShape& s, int32_t p) {
 // workgroup per possible item.
 constexpr int kMaxListInts = 4096;
 
-// Grid choice.  A persistent grid over the work list skips the items that
-// hold no tokens: one workgroup per possible item launches num_seqs * heads *
-// max_partitions workgroups, and the more partitions the table allows, the
-// larger the share that only reads a length and exits.  But the list deals
-// the real items statically (workgroups run at uneven speeds, which the
-// hardware's dynamic dispatch of a full grid absorbs) and every workgroup
-// spends a few microseconds building it.  Measured: at 8 or more partitions
-// the list wins (skewed batch, 8 partitions: +38%; long contexts, 9: +1%); at
-// 4 partitions the full grid wins by 1.5-4% (MHA and GQA batches).  One pass
-// never has empty items.
-int32_t work_list_ints(const DecodeShape& s, int64_t np, int32_t p) {
-  (void)p;
-  if ((s.flags & PA_DECODE_NO_WORK_LIST) || np < 8) return 0;
+// Largest order list (num_seqs * max_partitions entries) of a sorted grid.
+constexpr int64_t kMaxOrder = 65536;
+
+enum GridMode { kGridNatural = 0, kGridSorted = 1, kGridList = 2 };
+
+// Grid choice for a launch of np partitions.  One workgroup per possible item
+// launches num_seqs * heads * max_partitions workgroups; on a batch of mixed
+// lengths most of them hold no tokens.  In grid order the empty and short
+// items are mixed with full-size ones, so the device fills slowly at the
+// start (empty workgroups hold the dispatcher) and drains slowly at the end
+// (a full-size item dispatched late).  The sorted grid runs the items longest
+// first and the empty ones last, for one small ordering kernel and one more
+// dependent load per workgroup.  A persistent grid over the work list
+// launches no empty workgroups, but deals the items statically (workgroups
+// run at uneven speeds, which dynamic dispatch absorbs) and every workgroup
+// spends a few microseconds building the list.  Measured (decode kernel,
+// grid order -> sorted -> list): skewed batch, 8 partitions 68.8 -> 48.0 ->
+// 50.6 us; GQA lognormal batch, 4 partitions 291 -> 273 -> 302 us; long
+// contexts, 9 partitions 768 -> 759 -> 764 us; MHA uniform batch, 4
+// partitions 206.5 -> 207.6 -> 216.9 us; equal lengths 290 -> 295 -> 303 us.
+// So the sorted grid wherever its order fits.  One pass never has empty
+// items.
+int grid_mode(const DecodeShape& s, int64_t np) {
+  if (np <= 1) return kGridNatural;
+  const bool list_fits = pa::work_list_lds_ints(s.num_seqs, (int)np) <= kMaxListInts;
+  const bool order_fits = (int64_t)s.num_seqs * np <= kMaxOrder;
+  switch (s.flags & PA_DECODE_GRID_MASK) {
+    case PA_DECODE_NO_WORK_LIST: return kGridNatural;
+    case PA_DECODE_SORTED_GRID: return order_fits ? kGridSorted : kGridNatural;
+    case PA_DECODE_WORK_LIST: return list_fits ? kGridList : kGridNatural;
+    default: break;
+  }
+  if (order_fits) return kGridSorted;
+  return list_fits ? kGridList : kGridNatural;
+}
+
+int32_t work_list_ints(const DecodeShape& s, int64_t np) {
+  if (grid_mode(s, np) != kGridList) return 0;
   const int64_t ints = pa::work_list_lds_ints(s.num_seqs, (int)np);
-  if (ints > kMaxListInts) return 0;
   return (int32_t)((ints + 3) & ~3);  // keep the merge area 16-byte aligned
 }
 
@@ -198,12 +222,19 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace of a partitioned decode: (m, l) and the partial output vector per
-// (sequence, q head, partition).
+// (sequence, q head, partition), then for a sorted grid the item order.
+size_t order_offset(const DecodeShape& s, int64_t np) {
+  const size_t rows = (size_t)s.num_seqs * s.num_q_heads * (size_t)np;
+  return round_up(rows * 2 * sizeof(float)) + round_up(rows * s.head_dim * sizeof(float));
+}
+
 size_t workspace_bytes_for(const DecodeShape& s, int32_t p) {
   const int64_t np = n_partitions(s, p);
   if (np <= 1) return 0;
-  const size_t rows = (size_t)s.num_seqs * s.num_q_heads * (size_t)np;
-  return round_up(rows * 2 * sizeof(float)) + round_up(rows * s.head_dim * sizeof(float));
+  size_t bytes = order_offset(s, np);
+  if (grid_mode(s, np) == kGridSorted)
+    bytes += round_up((size_t)s.num_seqs * (size_t)np * sizeof(int32_t));
+  return bytes;
 }
 
 }  // namespace
@@ -397,7 +428,22 @@ int32_t pa_decode_work_list(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
                 kv_dtype, flags};
   int32_t p = 0;
   const int32_t st = plan_args(s, partition_size, q_dtype, &p);
-  return st != PA_OK ? st : (work_list_ints(s, n_partitions(s, p), p) > 0 ? 1 : 0);
+  return st != PA_OK ? st : (work_list_ints(s, n_partitions(s, p)) > 0 ? 1 : 0);
+}
+
+int32_t pa_decode_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                       int32_t partition_size, int32_t q_dtype, int32_t kv_dtype, uint32_t flags) {
+  DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                kv_dtype, flags};
+  int32_t p = 0;
+  const int32_t st = plan_args(s, partition_size, q_dtype, &p);
+  if (st != PA_OK) return st;
+  switch (grid_mode(s, n_partitions(s, p))) {
+    case kGridSorted: return PA_DECODE_SORTED_GRID;
+    case kGridList: return PA_DECODE_WORK_LIST;
+    default: return PA_DECODE_NO_WORK_LIST;
+  }
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -487,10 +533,17 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
   a.waves = pick_waves(s, p);
-  a.list_ints = work_list_ints(s, np, p);
+  // one grid decision for the workspace and the launch (both on the query rows' shape)
+  const int mode = grid_mode(rows_shape, np);
+  a.list_ints = mode == kGridList ? work_list_ints(rows_shape, np) : 0;
+  a.order = mode == kGridSorted
+                ? reinterpret_cast<const int32_t*>(ws + order_offset(rows_shape, np))
+                : nullptr;
 
   hipStream_t hs = (hipStream_t)stream;
   if (phase & kPartitions) {
+    if (a.order && pa::launch_decode_order(a, const_cast<int32_t*>(a.order), hs) != hipSuccess)
+      return PA_ERR_HIP;
     const hipError_t e = mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, hs)
                               : pa::launch_decode_valu(a, kv_dtype, head_dim, hs);
     if (e != hipSuccess) return PA_ERR_HIP;

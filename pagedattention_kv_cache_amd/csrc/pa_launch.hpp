@@ -59,6 +59,11 @@ struct DecodeArgs {
   int32_t out_dtype;
   int32_t waves;  // waves per work item (1, 2 or 4): they split its chunks
   int32_t list_ints;  // LDS ints of the work list (persistent grid), 0: one workgroup per item
+  // One workgroup per possible item: NULL, grid order (sequence, kv head, head
+  // chunk fastest, partitions last to first); else workgroup i (linear over
+  // the grid) takes entry i / (items per sequence) of this longest-first list
+  // of b * max_partitions + partition (-1: nothing left).
+  const int32_t* order;
 };
 
 // LDS ints a workgroup needs for the work list of a persistent launch.
@@ -72,6 +77,10 @@ __host__ __device__ inline int work_list_lds_ints(int num_seqs, int max_partitio
 // workgroup.
 hipError_t launch_decode_grid(const void* kernel, const DecodeArgs& a, int64_t items_x,
                               size_t lds, hipStream_t s);
+
+// Writes the longest-first item order of a launch (one workgroup) into
+// `order` [num_seqs * max_partitions].
+hipError_t launch_decode_order(const DecodeArgs& a, int32_t* order, hipStream_t s);
 
 // Vector-ALU decode kernel: any kv dtype, head_dim 64/128, 1..8 q heads per
 // work item.  grid = (num_seqs * num_kv_heads * head_chunks, max_partitions),

@@ -144,7 +144,7 @@ def _dec(**kw):
     (dict(P=24), ESHAPE),
     (dict(flags=7), EUNSUP),
     (dict(flags=3), EUNSUP),               # both kernel bits
-    (dict(flags=32), EUNSUP),              # unknown bit
+    (dict(flags=64), EUNSUP),              # unknown bit
     (dict(flags=pa.FORCE_MFMA, kvd=F32, qd=F32), EUNSUP),  # matrix cores: 16-bit caches only
     (dict(flags=pa.FORCE_MFMA, qd=F32), EUNSUP),           # ... queried in the same dtype
     (dict(out=None), ENULL),
@@ -191,16 +191,26 @@ def test_waves_flags():
     assert L.pa_decode_waves(*args[:6], 384, BF16, BF16, 0) == 2
     assert L.pa_decode_waves(*args[:6], 128, BF16, BF16, 0) == 1
     assert L.pa_decode_waves(4, 4, 4, 64, 16, 13, 0, F32, F32, 0) == 1          # one pass of 208
-    assert L.pa_decode_waves(*args, 32) == EUNSUP
+    assert L.pa_decode_waves(*args, 64) == EUNSUP
     assert L.pa_decode_waves(*args[:6], 24, BF16, BF16, 0) == ESHAPE  # not a block multiple
     assert L.pa_decode_waves(*args[:7], F16, BF16, pa.WAVES_2) == EDTYPE
-    # work list: launches with 8 or more partitions, unless disabled
-    assert L.pa_decode_work_list(*args, 0) == 1                                 # 8 of 1024
-    assert L.pa_decode_work_list(*args, pa.NO_WORK_LIST) == 0
-    assert L.pa_decode_work_list(*args[:6], 2048, BF16, BF16, 0) == 0          # 4 partitions
-    assert L.pa_decode_work_list(*args[:6], 256, BF16, BF16, 0) == 1           # 32 partitions
-    assert L.pa_decode_work_list(*args[:6], 8192, BF16, BF16, 0) == 0           # one pass
-    assert L.pa_decode_work_list(*args, 32) == EUNSUP
+    # grid: the sorted grid for every partitioned launch whose order fits
+    # (num_seqs * partitions <= 65536); the persistent work list only on request
+    G, S, W = pa.NO_WORK_LIST, pa.SORTED_GRID, pa.WORK_LIST
+    assert L.pa_decode_grid(*args, 0) == S                                      # 8 of 1024
+    assert L.pa_decode_grid(*args[:6], 2048, BF16, BF16, 0) == S                # 4 partitions
+    assert L.pa_decode_grid(*args[:6], 8192, BF16, BF16, 0) == G                # one pass
+    assert L.pa_decode_grid(*args[:6], 8192, BF16, BF16, W) == G
+    assert L.pa_decode_grid(*args, G) == G and L.pa_decode_grid(*args, W) == W
+    assert L.pa_decode_grid(*args, S | pa.FORCE_VALU) == S
+    assert L.pa_decode_grid(4096, 32, 8, 128, 16, 512, 256, BF16, BF16, 0) == G  # order too big
+    assert L.pa_decode_grid(4096, 32, 8, 128, 16, 512, 256, BF16, BF16, W) == G  # list too
+    assert L.pa_decode_grid(1000, 32, 8, 128, 16, 512, 256, BF16, BF16, W) == W
+    assert L.pa_decode_work_list(*args, 0) == 0
+    assert L.pa_decode_work_list(*args, W) == 1
+    assert L.pa_decode_work_list(*args[:6], 8192, BF16, BF16, W) == 0           # one pass
+    assert L.pa_decode_work_list(*args, 64) == EUNSUP
+    assert L.pa_decode_grid(*args, 64) == EUNSUP
     # the waves bits leave the kernel family alone
     assert L.pa_decode_kernel(32, 8, BF16, BF16, pa.WAVES_4) == pa.FORCE_MFMA
     assert L.pa_decode_kernel(32, 8, BF16, BF16, pa.WAVES_4 | pa.FORCE_VALU) == pa.FORCE_VALU
@@ -223,7 +233,11 @@ def test_partition_policy_and_workspace_size():
     n_part = MB * bs // P
     rows = B * Hq * n_part
     expect = -(-rows * 8 // 256) * 256 + -(-rows * d * 4 // 256) * 256
-    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, 0) == expect
+    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, pa.NO_WORK_LIST) == expect
+    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, pa.WORK_LIST) == expect
+    # the sorted grid (the library's choice here) adds its order: an int per (seq, partition)
+    order = -(-B * n_part * 4 // 256) * 256
+    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, 0) == expect + order
     # forced partition sizes must be multiples of the block size; invalid -> 0
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 24, BF16, 0) == 0
     assert L.pa_decode_partition_size(4, 3, 2, 128, 16, 8, BF16, 0) == ESHAPE

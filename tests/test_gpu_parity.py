@@ -190,28 +190,55 @@ def _decode_nan_prefilled(gs, wl, P, flags):
 
 @pytest.mark.parametrize("kernel,dtype,hq,hkv", [("mfma", "bf16", 32, 8), ("valu", "f16", 16, 16)])
 @pytest.mark.parametrize("waves", [1, 2, 4])
-def test_work_list_many_items_per_workgroup(kernel, dtype, hq, hkv, waves):
-    """More sequences than a wave has lanes and several items per persistent
-    workgroup: every item is computed exactly once, bit-identical to the grid
-    with one workgroup per possible item, and within tolerance of the oracle."""
+@pytest.mark.parametrize("P", [256, 768])
+def test_grid_modes_agree_bit_for_bit(kernel, dtype, hq, hkv, waves, P):
+    """More sequences than a wave has lanes, 11 (or 4) partitions: the persistent
+    grid over the work list (several items per workgroup), the sorted grid (items
+    ordered on the device, empty workgroups last) and the grid in its own order
+    each compute every item exactly once -- bit-identical to one another, into
+    NaN-filled outputs and workspace -- and within tolerance of the oracle."""
     rng = np.random.default_rng(90 + waves)
     lens = rng.integers(1, 2600, size=300).tolist()
-    lens[:2] = [1, 2600]
-    cfg = custom_config(f"wl-{kernel}", lens, hq, hkv, 128, dtype, 16, seed=123)
+    lens[:3] = [1, 2600, 5]
+    cfg = custom_config(f"gm-{kernel}", lens, hq, hkv, 128, dtype, 16, seed=123)
     wl = Workload(cfg)
     st = oracle_state_empty(wl)
     gs = GpuState(wl, oracle_state=st)
     gs.write_step(0)
     st.write_step(0)
     flags = KERNELS[kernel] | pa.WAVES_FLAG[waves]
-    P = 256  # 11 partitions: the persistent grid
-    assert pa.decode_work_list(cfg.num_seqs, hq, hkv, 128, 16, wl.max_blocks_per_seq, P,
-                               gs.kc.dtype, gs.kc.dtype, flags)
-    out_list = _decode_nan_prefilled(gs, wl, P, flags)
-    out_grid = _decode_nan_prefilled(gs, wl, P, flags | pa.NO_WORK_LIST)
-    assert torch.isfinite(out_list).all()
-    assert torch.equal(out_list, out_grid)
-    _check_decode(out_list, st.decode(0, threads=8), dtype)
+    modes = {}
+    for mode in (pa.WORK_LIST, pa.SORTED_GRID, pa.NO_WORK_LIST):
+        assert pa.decode_grid(cfg.num_seqs, hq, hkv, 128, 16, wl.max_blocks_per_seq, P,
+                              gs.kc.dtype, gs.kc.dtype, flags | mode) == pa.GRID_NAMES[mode]
+        modes[mode] = _decode_nan_prefilled(gs, wl, P, flags | mode)
+    assert torch.isfinite(modes[pa.SORTED_GRID]).all()
+    assert torch.equal(modes[pa.WORK_LIST], modes[pa.NO_WORK_LIST])
+    assert torch.equal(modes[pa.SORTED_GRID], modes[pa.NO_WORK_LIST])
+    _check_decode(modes[pa.SORTED_GRID], st.decode(0, threads=8), dtype)
+
+
+def test_sorted_grid_with_empty_sequences():
+    """Zero-length sequences are items too (their rows are zeroed), ordered last."""
+    lens = [0, 700, 0, 1, 1500, 0]
+    cfg = custom_config("sg-empty", [max(x, 1) for x in lens], 8, 2, 128, "bf16", 16, seed=8)
+    wl = Workload(cfg)
+    gs = GpuState(wl)
+    gs.write_step(0)
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    outs = []
+    for mode in (pa.SORTED_GRID, pa.NO_WORK_LIST):
+        out = torch.full(gs.q[0].shape, float("nan"), device="cuda")
+        pa.decode(out, gs.q[0], gs.kc, gs.vc, gs.block_tables, ctx, cfg.attn_scale(), 16, 256,
+                  flags=mode)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert (outs[0][b] == 0).all()
+        else:
+            assert torch.isfinite(outs[0][b]).all()
 
 
 def test_decode_multistep_parity():
