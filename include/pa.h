@@ -95,10 +95,14 @@ typedef enum pa_status {
  * (sequence, kv head, head chunk, partition).  0 lets the library pick.
  *   PA_DECODE_NO_WORK_LIST  one workgroup per possible item, in grid order
  *                           (the items that hold no tokens exit at once);
- *   PA_DECODE_SORTED_GRID   one workgroup per possible item, the items that
- *                           hold tokens first and the longest first (a
+ *   PA_DECODE_SORTED_GRID   the items that hold tokens, longest first (a
  *                           one-workgroup kernel orders them on the device
- *                           before the decode, in the workspace);
+ *                           before the decode, in the workspace): one
+ *                           workgroup per possible item in that order, or,
+ *                           with partitions of 1024 tokens or more, a
+ *                           persistent grid whose workgroups take the next
+ *                           item of the order from a counter when they
+ *                           finish one;
  *   PA_DECODE_WORK_LIST     a persistent grid (as many workgroups as fit on
  *                           the device) walking the list of items that hold
  *                           tokens, which each workgroup builds in LDS.

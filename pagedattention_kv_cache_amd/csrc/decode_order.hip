@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kThreads) void decode_order_kernel(DecodeArgs a, in
       order[atomicAdd(&start[L <= 0 ? 0 : item_bin(L, p, P)], 1)] = b * np + p;
   }
   for (int e = total + tid; e < B * np; e += kThreads) order[e] = -1;
+  if (tid == 0 && a.order_ctr) *a.order_ctr = 0;
 }
 
 }  // namespace

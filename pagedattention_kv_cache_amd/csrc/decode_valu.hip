@@ -162,6 +162,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
              (args.group / args.heads_per_item);
     step = (int)gridDim.x;
   }
+  if (args.order_ctr) n_work = 0x7fffffff;  // a dynamic deal: until the order runs out
+  __shared__ int ticket_lds[2];
   // Round r takes entry r * gridDim.x + blockIdx.x, or the mirrored one on
   // odd rounds: the list runs longest first, so a workgroup that drew a long
   // entry in one round draws a short one in the next (a snake deal).
@@ -203,11 +205,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
       hc = it - item * per_seq;
       work_item(dyn_lds, a.max_partitions, item, cursor, b, part);
     } else if (a.order) {
-      const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+      const int64_t lin =
+          a.order_ctr ? (int64_t)it : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
       const int64_t e = lin / per_seq;
       hc = (int)(lin - e * per_seq);
+      if (e >= (int64_t)a.num_seqs * a.max_partitions) break;  // past the order: done
       const int entry = a.order[e];
-      if (entry < 0) goto next_item;  // every item is taken: the rest of the grid is empty
+      if (entry < 0) break;  // every item is taken: the rest of the order is empty
       b = entry / a.max_partitions;
       part = entry - b * a.max_partitions;
     } else {
@@ -467,6 +471,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
     }
     }
   next_item:
+    if (KernArgs& a = *fresh_args(); a.order_ctr) {
+      // A dynamic deal asks for the next item here, at the end of this one:
+      // asked for with the start-up loads instead, the counter's latency
+      // under contention held them back (measured 10% slower).
+      if (threadIdx.x == 0) ticket_lds[round & 1] = take_ticket(a.order_ctr);
+      if (a.waves > 1) __syncthreads();
+      it = (int)gridDim.x + ticket_lds[round & 1];
+      ++round;
+      continue;
+    }
     if (!listed) break;
     ++round;
     it = round * step + ((round & 1) ? step - 1 - bx : bx);

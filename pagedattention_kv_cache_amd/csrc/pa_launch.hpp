@@ -64,6 +64,11 @@ struct DecodeArgs {
   // the grid) takes entry i / (items per sequence) of this longest-first list
   // of b * max_partitions + partition (-1: nothing left).
   const int32_t* order;
+  // With an order: NULL, one workgroup per grid slot; else a persistent grid
+  // deals the order dynamically: workgroup i starts with item i, then takes
+  // gridDim.x + (the value of this counter, incremented) until the order runs
+  // out.  The ordering kernel zeroes it.
+  int32_t* order_ctr;
 };
 
 // LDS ints a workgroup needs for the work list of a persistent launch.

@@ -67,6 +67,14 @@ __device__ __forceinline__ int fresh_tid() {
   return t;
 }
 
+// Dynamic deal: the next item index of a workgroup from the launch's counter
+// (one lane asks).  The answer goes through two LDS ints used alternately, so
+// a wave that runs ahead to the next item cannot overwrite a value another
+// wave has not read yet.
+__device__ __forceinline__ int take_ticket(int32_t* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // LDS layout of the list (ints): cnt[NP + 2], tot[NP + 2], base[NP + 1],
 // fill[NP + 1], sorted[B], items[B].
 __device__ __forceinline__ const int* list_base(const int* lds, int np) {

@@ -235,8 +235,9 @@ def test_partition_policy_and_workspace_size():
     expect = -(-rows * 8 // 256) * 256 + -(-rows * d * 4 // 256) * 256
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, pa.NO_WORK_LIST) == expect
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, pa.WORK_LIST) == expect
-    # the sorted grid (the library's choice here) adds its order: an int per (seq, partition)
-    order = -(-B * n_part * 4 // 256) * 256
+    # the sorted grid (the library's choice here) adds its order, an int per (seq,
+    # partition), and a 256-byte counter
+    order = -(-B * n_part * 4 // 256) * 256 + 256
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, 0) == expect + order
     # forced partition sizes must be multiples of the block size; invalid -> 0
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 24, BF16, 0) == 0

@@ -190,13 +190,15 @@ def _decode_nan_prefilled(gs, wl, P, flags):
 
 @pytest.mark.parametrize("kernel,dtype,hq,hkv", [("mfma", "bf16", 32, 8), ("valu", "f16", 16, 16)])
 @pytest.mark.parametrize("waves", [1, 2, 4])
-@pytest.mark.parametrize("P", [256, 768])
+@pytest.mark.parametrize("P", [256, 768, 1024])
 def test_grid_modes_agree_bit_for_bit(kernel, dtype, hq, hkv, waves, P):
-    """More sequences than a wave has lanes, 11 (or 4) partitions: the persistent
+    """More sequences than a wave has lanes, 11, 4 or 3 partitions: the persistent
     grid over the work list (several items per workgroup), the sorted grid (items
-    ordered on the device, empty workgroups last) and the grid in its own order
-    each compute every item exactly once -- bit-identical to one another, into
-    NaN-filled outputs and workspace -- and within tolerance of the oracle."""
+    ordered on the device; one workgroup per possible item with the empty ones
+    last, or at 1024-token partitions a persistent grid dealing the order from a
+    counter) and the grid in its own order each compute every item exactly once --
+    bit-identical to one another, into NaN-filled outputs and workspace -- and
+    within tolerance of the oracle."""
     rng = np.random.default_rng(90 + waves)
     lens = rng.integers(1, 2600, size=300).tolist()
     lens[:3] = [1, 2600, 5]
