@@ -67,6 +67,10 @@ def parse_args(argv=None):
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per sequence (several: multi-query decode, as when draft "
                          "tokens are verified; the oracle baseline is then skipped)")
+    ap.add_argument("--fused-step", action="store_true",
+                    help="one pa_decode_step call for write + decode partitions (its cache write "
+                         "shares the launch that orders the decode's items); default: separate "
+                         "pa_cache_write and pa_decode_partitions calls, timed one by one")
     ap.add_argument("--grid", choices=["auto", "grid", "sorted", "work_list"], default="auto",
                     help="how workgroups find their items (default: the library's choice)")
     ap.add_argument("--no-work-list", action="store_true",
@@ -406,6 +410,7 @@ def run(args):
     stream = torch.cuda.current_stream(dev)
 
     n_layers = len(kcs)
+    fused = args.fused_step and Q == 1 and c.kv_dtype != "fp8"
 
     def step(i, ev=None):
         # step i: decode step (i // n_layers) % steps of layer i % n_layers
@@ -413,10 +418,18 @@ def run(args):
         k_l, v_l = kcs[i % n_layers], vcs[i % n_layers]
         if ev is not None:
             ev[0].record(stream)
-        write_kv(c, sk[s], sv[s], slots[s], k_l, v_l)
-        if ev is not None:
-            ev[1].record(stream)
-        if Q > 1:
+        if fused:
+            if ev is not None:
+                ev[1].record(stream)
+            pa.decode_step_partitions(sk[s], sv[s], slots[s], out, qs[s], k_l, v_l, bt, ctx[s],
+                                      scale, c.block_size, part, ws, flags)
+        else:
+            write_kv(c, sk[s], sv[s], slots[s], k_l, v_l)
+            if ev is not None:
+                ev[1].record(stream)
+        if fused:
+            pass
+        elif Q > 1:
             ks, vs = c.fp8_scales if c.kv_dtype == "fp8" else (1.0, 1.0)
             pa.decode_mq_partitions(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part,
                                     ws, flags, ks, vs)
@@ -492,7 +505,8 @@ def run(args):
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(c.num_seqs * Q / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(kv),
-        "write_ms": round(write_ms, 5),
+        "write_ms": None if fused else round(write_ms, 5),
+        "fused_write": fused,
         "decode_partitions_ms": round(dec_ms, 5),
         "decode_merge_ms": round(merge_ms, 5),
         "roofline": {

@@ -262,6 +262,37 @@ int pa_decode_merge(void* out, const void* q, const void* k_cache, const void* v
                     uint32_t flags, void* stream);
 
 /*
+ * pa_decode_step / pa_decode_step_partitions -- one decode step: pa_cache_write
+ * of the step's new tokens (k, v, slot_mapping, num_tokens and the strides as
+ * there, kv_dtype the cache dtype, 16-bit or fp32) followed by pa_decode (or
+ * pa_decode_partitions) over the updated caches, with the same arguments and
+ * results as those calls made one after the other on `stream`.  Where the
+ * decode orders its work items on the device (PA_DECODE_SORTED_GRID), the
+ * write runs in the same launch as the ordering, saving a launch per step.
+ * Nothing is launched unless both the write's and the decode's arguments
+ * validate (errors as either call).  E4M3 caches: PA_ERR_DTYPE.
+ */
+int pa_decode_step(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                   int64_t k_token_stride, int64_t v_token_stride, void* out, const void* q,
+                   void* k_cache, void* v_cache, const int32_t* block_tables,
+                   const int32_t* context_lens, float scale, int32_t block_size,
+                   int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                   int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype,
+                   int32_t out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
+                   void* stream);
+int pa_decode_step_partitions(const void* k, const void* v, const int64_t* slot_mapping,
+                              int64_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
+                              void* out, const void* q, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, int32_t block_size, int32_t partition_size,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
+                              void* workspace, size_t workspace_bytes, uint32_t flags,
+                              void* stream);
+
+/*
  * pa_decode_mq / pa_decode_mq_partitions / pa_decode_mq_merge -- decode of
  * several query tokens per sequence ("vLLM Project Update" talk, roadmap:
  * multi-query attention kernels for speculative decoding, which score the

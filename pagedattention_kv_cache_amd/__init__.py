@@ -107,6 +107,10 @@ def lib() -> ctypes.CDLL:
         for name in ("pa_decode_mq", "pa_decode_mq_partitions", "pa_decode_mq_merge"):
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name).argtypes = decmq_args
+        step_args = [vp, vp, vp, i64, i64, i64] + dec_args
+        for name in ("pa_decode_step", "pa_decode_step_partitions"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = step_args
         L.pa_decode_mq_kernel.restype = i32
         L.pa_decode_mq_kernel.argtypes = [i32, i32, i32, i32, i32, u32]
         L.pa_cache_write_fp8.restype = ctypes.c_int
@@ -378,6 +382,60 @@ def decode_fp8_partitions(out, q, k_cache, v_cache, block_tables, context_lens, 
     _require(k_cache.dtype == torch.float8_e4m3fn, "decode_fp8 needs E4M3 caches")
     _decode_call("pa_decode_fp8_partitions", out, q, k_cache, v_cache, block_tables, context_lens,
                  scale, block_size, partition_size, workspace, flags, (k_scale, v_scale))
+
+
+def _decode_step_call(fn_name, k, v, slot_mapping, out, q, k_cache, v_cache, block_tables,
+                      context_lens, scale, block_size, partition_size, workspace, flags):
+    _require(k.dim() == 3 and v.dim() == 3 and k.shape == v.shape, "k, v must be [T][Hkv][d]")
+    T = k.shape[0]
+    for t in (k, v):
+        _require(t.stride(2) == 1 and t.stride(1) == k.shape[2], "heads of a token must be packed")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,)
+             and slot_mapping.is_contiguous(), "slot_mapping must be contiguous int64 [T]")
+    _require(k.dtype == v.dtype == k_cache.dtype == v_cache.dtype, "dtype mismatch")
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
+    B, Hq, d = q.shape
+    _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
+    NB, Hkv, bs, d2 = _cache_dims(k_cache, v_cache)
+    _require(bs == block_size and d2 == d and tuple(k.shape[1:]) == (Hkv, d),
+             "cache shapes do not match k/v, q or block_size")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(),
+             "block_tables must be contiguous int32 [B][max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
+             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
+    MB = block_tables.shape[1]
+    need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype, flags)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        if fn_name != "pa_decode_step":
+            raise PAError(-5, "the phase entry points need the caller's workspace")
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(getattr(lib(), fn_name)(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), T, k.stride(0), v.stride(0),
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), block_size,
+        partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(k_cache), _dt(out), ws_ptr, ws_bytes,
+        flags, _stream(q.device)))
+
+
+def decode_step(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, context_lens,
+                scale, block_size, partition_size=0, workspace=None, flags=AUTO) -> None:
+    """cache_write(k, v, slot_mapping, ...) then decode(out, q, ...) in as few launches as
+    the grid allows (the write shares the launch that orders the decode's items)."""
+    _decode_step_call("pa_decode_step", k, v, slot_mapping, out, q, k_cache, v_cache,
+                      block_tables, context_lens, scale, block_size, partition_size, workspace,
+                      flags)
+
+
+def decode_step_partitions(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables,
+                           context_lens, scale, block_size, partition_size=0, workspace=None,
+                           flags=AUTO) -> None:
+    """decode_step without the merge phase (decode_merge completes it)."""
+    _decode_step_call("pa_decode_step_partitions", k, v, slot_mapping, out, q, k_cache, v_cache,
+                      block_tables, context_lens, scale, block_size, partition_size, workspace,
+                      flags)
 
 
 def decode_mq_kernel(num_queries: int, num_q_heads: int, num_kv_heads: int,

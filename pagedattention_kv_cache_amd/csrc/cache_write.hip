@@ -13,6 +13,7 @@
 // chunk's elements go to consecutive dims of row o%4, four elements apart.
 // A single token therefore fills 32 of every 128 bytes it touches, not a
 // single 16- or 2-byte slot of each line.
+#include "cache_write.hpp"
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
 
@@ -21,48 +22,7 @@ namespace {
 
 template <int EB>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int chunks_per_row) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_token = (int64_t)a.num_kv_heads * chunks_per_row;
-  const int64_t total = a.num_tokens * per_token;
-  if (gid >= total) return;
-  const int64_t t = gid / per_token;
-  const int rem = (int)(gid - t * per_token);
-  const int h = rem / chunks_per_row;
-  const int c = rem - h * chunks_per_row;
-  const int64_t slot = a.slots[t];
-  // negative = padding; a slot past the pool breaks the caller's contract and
-  // is dropped rather than written out of bounds
-  if (slot < 0 || slot >= a.num_blocks * a.block_size) return;
-  const int64_t blk = slot / a.block_size;
-  const int off = (int)(slot - blk * a.block_size);
-  constexpr int EPC = 16 / EB;  // elements per chunk
-  const int64_t D = a.head_dim;
-  const int e0 = c * EPC;
-
-  const char* ksrc = reinterpret_cast<const char*>(a.k) + ((t * a.k_stride) + h * D + e0) * EB;
-  const char* vsrc = reinterpret_cast<const char*>(a.v) + ((t * a.v_stride) + h * D + e0) * EB;
-  const uint4 kraw = ld16(ksrc);
-  const uint4 vraw = ld16(vsrc);
-
-  const int64_t quad = (blk * a.num_kv_heads + h) * (a.block_size / 4) + off / 4;
-  const int row = off % 4;
-  char* kdst = reinterpret_cast<char*>(a.k_cache) + ((quad * chunks_per_row + c) * 4 + row) * 16;
-  *reinterpret_cast<uint4*>(kdst) = kraw;
-
-  char* vrow = reinterpret_cast<char*>(a.v_cache) + ((quad * D + e0) * 4 + row) * EB;
-  const int64_t vstep = 4 * EB;  // next dim of the same row
-  if constexpr (EB == 4) {
-    const uint32_t w[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(vrow + i * vstep) = w[i];
-  } else {
-    const uint32_t w[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint16_t*>(vrow + (2 * i) * vstep) = (uint16_t)(w[i] & 0xffffu);
-      *reinterpret_cast<uint16_t*>(vrow + (2 * i + 1) * vstep) = (uint16_t)(w[i] >> 16);
-    }
-  }
+  cache_write_chunk<EB>(a, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, chunks_per_row);
 }
 
 // Quantizing write into E4M3 caches ("vLLM Project Update" talk, quantization

@@ -13,6 +13,7 @@
 // Entry = b * max_partitions + partition.  Items of equal size (in 16-token
 // chunks) may come in any order: an item's result does not depend on the
 // workgroup that computes it.
+#include "cache_write.hpp"
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
 
@@ -33,7 +34,8 @@ __device__ __forceinline__ int seq_items(int L, int P, int np) {
   return L <= 0 ? 1 : min((L + P - 1) / P, np);
 }
 
-__global__ __launch_bounds__(kThreads) void decode_order_kernel(DecodeArgs a, int32_t* order) {
+// The order, by one workgroup of kThreads threads.
+__device__ __forceinline__ void order_items(const DecodeArgs& a, int32_t* order) {
   __shared__ int hist[kBins];
   __shared__ int start[kBins];
   const int tid = threadIdx.x;
@@ -68,10 +70,45 @@ __global__ __launch_bounds__(kThreads) void decode_order_kernel(DecodeArgs a, in
   if (tid == 0 && a.order_ctr) *a.order_ctr = 0;
 }
 
+__global__ __launch_bounds__(kThreads) void decode_order_kernel(DecodeArgs a, int32_t* order) {
+  order_items(a, order);
+}
+
+// A decode step's cache write and the order in one launch: workgroup 0
+// orders (it reads only the context lengths), the others write the step's
+// new tokens, one 16-byte chunk per thread.  The decode that follows on the
+// stream sees both.
+template <int EB>
+__global__ __launch_bounds__(kThreads) void decode_prologue_kernel(DecodeArgs a, int32_t* order,
+                                                                   CacheWriteArgs w,
+                                                                   int chunks_per_row) {
+  if (blockIdx.x == 0) {
+    order_items(a, order);
+  } else {
+    cache_write_chunk<EB>(w, (int64_t)(blockIdx.x - 1) * kThreads + threadIdx.x,
+                          chunks_per_row);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_decode_order(const DecodeArgs& a, int32_t* order, hipStream_t s) {
-  hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kThreads), 0, s, a, order);
+hipError_t launch_decode_order(const DecodeArgs& a, int32_t* order, const CacheWriteArgs* write,
+                               hipStream_t s) {
+  if (!write || write->num_tokens == 0) {
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kThreads), 0, s, a, order);
+    return hipGetLastError();
+  }
+  const int chunks = write->head_dim * write->elem_bytes / 16;
+  const int64_t total = write->num_tokens * write->num_kv_heads * chunks;
+  const int64_t blocks = 1 + (total + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (write->elem_bytes == 4) {
+    hipLaunchKernelGGL(decode_prologue_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       a, order, *write, chunks);
+  } else {
+    hipLaunchKernelGGL(decode_prologue_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       a, order, *write, chunks);
+  }
   return hipGetLastError();
 }
 

@@ -268,10 +268,15 @@ const char* pa_status_string(int32_t status) {
   }
 }
 
-int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
-                   void* v_cache, int64_t num_tokens, int64_t k_token_stride,
-                   int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
-                   int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and arguments of a 16-bit / fp32 cache write (pa_cache_write).
+int write_args(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+               void* v_cache, int64_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
+               int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+               int32_t dtype, pa::CacheWriteArgs* a) {
   const int eb = elem_bytes(dtype);
   if (!eb || dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_DTYPE;  // E4M3: pa_cache_write_fp8
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
@@ -280,28 +285,44 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
   const int64_t row = (int64_t)num_kv_heads * head_dim;
   if (k_token_stride < row || v_token_stride < row) return PA_ERR_SHAPE;
   if ((k_token_stride * eb) % 16 || (v_token_stride * eb) % 16) return PA_ERR_SHAPE;
-  if (num_tokens == 0) return PA_OK;
-  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
-    return PA_ERR_SHAPE;
-  const int64_t threads = num_tokens * num_kv_heads * ((int64_t)head_dim * eb / 16);
-  if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
+  if (num_tokens > 0) {
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+      return PA_ERR_SHAPE;
+    const int64_t threads = num_tokens * num_kv_heads * ((int64_t)head_dim * eb / 16);
+    if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
+  }
+  a->k = k;
+  a->v = v;
+  a->slots = slot_mapping;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->num_tokens = num_tokens;
+  a->num_blocks = num_blocks;
+  a->k_stride = k_token_stride;
+  a->v_stride = v_token_stride;
+  a->num_kv_heads = num_kv_heads;
+  a->head_dim = head_dim;
+  a->block_size = block_size;
+  a->elem_bytes = eb;
+  a->k_scale = 1.0f;
+  a->v_scale = 1.0f;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int64_t num_tokens, int64_t k_token_stride,
+                   int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
+                   int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream) {
   pa::CacheWriteArgs a;
-  a.k = k;
-  a.v = v;
-  a.slots = slot_mapping;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.num_tokens = num_tokens;
-  a.num_blocks = num_blocks;
-  a.k_stride = k_token_stride;
-  a.v_stride = v_token_stride;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.elem_bytes = eb;
-  a.k_scale = 1.0f;
-  a.v_scale = 1.0f;
+  const int st = write_args(k, v, slot_mapping, k_cache, v_cache, num_tokens, k_token_stride,
+                            v_token_stride, num_kv_heads, head_dim, num_blocks, block_size, dtype,
+                            &a);
+  if (st != PA_OK || num_tokens == 0) return st;
   return pa::launch_cache_write(a, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -477,7 +498,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                 int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream, int phase,
-                float k_scale = 1.0f, float v_scale = 1.0f, int32_t num_queries = 1) {
+                float k_scale = 1.0f, float v_scale = 1.0f, int32_t num_queries = 1,
+                const pa::CacheWriteArgs* pre_write = nullptr) {
   DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                 kv_dtype, flags};
   int st = check_shape(s);
@@ -494,7 +516,12 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t kernel = pick_kernel(flags, kv_dtype, q_dtype, group, num_queries);
   if (!kernel) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0) {  // nothing to attend; a step's cache write still runs
+    if (pre_write && pre_write->num_tokens > 0 && (phase & kPartitions))
+      return pa::launch_cache_write(*pre_write, (hipStream_t)stream) == hipSuccess ? PA_OK
+                                                                                  : PA_ERR_HIP;
+    return PA_OK;
+  }
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
 
@@ -556,8 +583,14 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
 
   hipStream_t hs = (hipStream_t)stream;
   if (phase & kPartitions) {
-    if (a.order && pa::launch_decode_order(a, const_cast<int32_t*>(a.order), hs) != hipSuccess)
+    // a step's cache write goes first: in the launch that orders the items, or on its own
+    if (a.order) {
+      if (pa::launch_decode_order(a, const_cast<int32_t*>(a.order), pre_write, hs) != hipSuccess)
+        return PA_ERR_HIP;
+    } else if (pre_write && pre_write->num_tokens > 0 &&
+               pa::launch_cache_write(*pre_write, hs) != hipSuccess) {
       return PA_ERR_HIP;
+    }
     const hipError_t e = mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, hs)
                               : pa::launch_decode_valu(a, kv_dtype, head_dim, hs);
     if (e != hipSuccess) return PA_ERR_HIP;
@@ -593,6 +626,36 @@ int pa_decode_partitions(PA_DECODE_PARAMS) {
   return decode_impl(PA_DECODE_ARGS, kPartitions);
 }
 int pa_decode_merge(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kMerge); }
+
+#define PA_STEP_PARAMS                                                                         \
+  const void *k, const void *v, const int64_t *slot_mapping, int64_t num_tokens,              \
+      int64_t k_token_stride, int64_t v_token_stride, void *out, const void *q, void *k_cache, \
+      void *v_cache, const int32_t *block_tables, const int32_t *context_lens, float scale,    \
+      int32_t block_size, int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,       \
+      int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,  \
+      int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype, void *workspace,                   \
+      size_t workspace_bytes, uint32_t flags, void *stream
+
+// A decode step: the step's cache write, then the decode; nothing is launched
+// unless both validate.
+static int step_impl(PA_STEP_PARAMS, int phase) {
+  if (kv_dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_DTYPE;
+  pa::CacheWriteArgs w;
+  const int st = write_args(k, v, slot_mapping, k_cache, v_cache, num_tokens, k_token_stride,
+                            v_token_stride, num_kv_heads, head_dim, num_blocks, block_size,
+                            kv_dtype, &w);
+  if (st != PA_OK) return st;
+  return decode_impl(PA_DECODE_ARGS, phase, 1.0f, 1.0f, 1, &w);
+}
+
+int pa_decode_step(PA_STEP_PARAMS) {
+  return step_impl(k, v, slot_mapping, num_tokens, k_token_stride, v_token_stride, PA_DECODE_ARGS,
+                   kBoth);
+}
+int pa_decode_step_partitions(PA_STEP_PARAMS) {
+  return step_impl(k, v, slot_mapping, num_tokens, k_token_stride, v_token_stride, PA_DECODE_ARGS,
+                   kPartitions);
+}
 
 #define PA_DECODE_FP8_PARAMS                                                                   \
   void *out, const void *q, const void *k_cache, const void *v_cache,                          \

@@ -84,8 +84,10 @@ hipError_t launch_decode_grid(const void* kernel, const DecodeArgs& a, int64_t i
                               size_t lds, hipStream_t s);
 
 // Writes the longest-first item order of a launch (one workgroup) into
-// `order` [num_seqs * max_partitions].
-hipError_t launch_decode_order(const DecodeArgs& a, int32_t* order, hipStream_t s);
+// `order` [num_seqs * max_partitions]; with `write` (16-bit or fp32 caches),
+// the same launch also runs that cache write.
+hipError_t launch_decode_order(const DecodeArgs& a, int32_t* order, const CacheWriteArgs* write,
+                               hipStream_t s);
 
 // Vector-ALU decode kernel: any kv dtype, head_dim 64/128, 1..8 q heads per
 // work item.  grid = (num_seqs * num_kv_heads * head_chunks, max_partitions),

@@ -464,3 +464,33 @@ def test_block_manager_argument_validation():
         assert L.pa_bm_free(h, 42) == ESEQ
     finally:
         L.pa_bm_destroy(h)
+
+
+# ------------------------------------------------------------------ decode step
+
+def _step(**kw):
+    a = dict(k=FAKE, v=FAKE, slots=FAKE, T=4, ks=1024, vs=1024, out=FAKE, q=FAKE, kc=FAKE,
+             vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, bs=16, P=0, B=4, Hq=32, Hkv=8, d=128, NB=100,
+             MB=64, qd=BF16, kvd=BF16, od=F32, ws=None, wsb=0, flags=pa.FORCE_VALU,
+             fn="pa_decode_step")
+    a.update(kw)
+    return getattr(pa.lib(), a["fn"])(
+        a["k"], a["v"], a["slots"], a["T"], a["ks"], a["vs"], a["out"], a["q"], a["kc"], a["vc"],
+        a["bt"], a["cl"], a["scale"], a["bs"], a["P"], a["B"], a["Hq"], a["Hkv"], a["d"],
+        a["NB"], a["MB"], a["qd"], a["kvd"], a["od"], a["ws"], a["wsb"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kvd=FP8, qd=BF16), EDTYPE),          # E4M3 caches: write and decode separately
+    (dict(ks=100), ESHAPE),                    # the write's arguments ...
+    (dict(k=None), ENULL),
+    (dict(T=-1), ESHAPE),
+    (dict(Hq=30), ESHAPE),                     # ... and the decode's
+    (dict(qd=F16), EDTYPE),
+    (dict(ws=None, wsb=0, P=256), EWS),
+    (dict(fn="pa_decode_step_partitions", ws=None, wsb=0, P=256), EWS),
+    (dict(flags=64), EUNSUP),
+    (dict(T=0, B=0, out=None, q=None, bt=None, cl=None), OK),   # nothing to do
+])
+def test_decode_step_validation(kw, status):
+    assert _step(**kw) == status
