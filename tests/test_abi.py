@@ -168,7 +168,7 @@ def test_kernel_family_policy():
     L = pa.lib()
     assert L.pa_decode_kernel(32, 8, BF16, BF16, 0) == pa.FORCE_MFMA   # GQA group of 4
     assert L.pa_decode_kernel(64, 8, BF16, BF16, 0) == pa.FORCE_MFMA
-    assert L.pa_decode_kernel(32, 32, F16, F16, 0) == pa.FORCE_VALU    # plain MHA
+    assert L.pa_decode_kernel(32, 32, F16, F16, 0) == pa.FORCE_MFMA    # plain MHA: one column
     assert L.pa_decode_kernel(4, 4, F32, F32, 0) == pa.FORCE_VALU      # fp32 cache
     assert L.pa_decode_kernel(32, 8, F32, BF16, 0) == pa.FORCE_VALU    # fp32 queries
     assert L.pa_decode_kernel(32, 32, F16, F16, pa.FORCE_MFMA) == pa.FORCE_MFMA
@@ -344,7 +344,7 @@ def test_plain_decode_rejects_fp8_caches():
 def test_fp8_kernel_family_policy():
     L = pa.lib()
     assert L.pa_decode_kernel(32, 8, BF16, FP8, 0) == pa.FORCE_MFMA   # GQA, bf16 queries
-    assert L.pa_decode_kernel(32, 32, BF16, FP8, 0) == pa.FORCE_VALU  # MHA
+    assert L.pa_decode_kernel(32, 32, BF16, FP8, 0) == pa.FORCE_MFMA  # MHA
     assert L.pa_decode_kernel(32, 8, F16, FP8, 0) == pa.FORCE_VALU    # f16 queries
     assert L.pa_decode_kernel(32, 8, F32, FP8, 0) == pa.FORCE_VALU
     assert L.pa_decode_kernel(32, 8, F16, FP8, pa.FORCE_MFMA) == EUNSUP
