@@ -306,8 +306,9 @@ int pa_decode_step_partitions(const void* k, const void* v, const int64_t* slot_
  *                   t = 0 .. context_lens[b] - num_queries + i.
  * A query whose position would be negative (context_lens[b] < num_queries)
  * gets a zero row.  num_queries = 1 is pa_decode.  The (query, head) rows of
- * a kv head form the matrix cores' columns: num_queries * heads_per_item <= 16
- * (instantiated widths 1-8, 10, 12, 16); the vector-ALU kernel takes up to 8.
+ * a kv head form the matrix cores' columns: num_queries * heads_per_item <= 32
+ * (instantiated widths 1-8, 10, 12, 16 on one 16-column tile, 24 and 32 on
+ * two tiles sharing each key/value load); the vector-ALU kernel takes up to 8.
  *   num_queries    1 .. 16
  *   kv_dtype       any cache dtype; k_scale, v_scale as in pa_decode_fp8 (pass
  *                  1 for the unscaled types)

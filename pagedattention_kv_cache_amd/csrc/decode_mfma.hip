@@ -190,6 +190,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
   using scalar = typename M::scalar;
   constexpr int KC = D / 32;  // QK^T k-chunks
   constexpr int VC = D / 16;  // P.V row chunks
+  constexpr int NT = (G + 15) / 16;  // 16-column tiles: every key and value load feeds all
 
 
   // Work items (sequence, kv head, head chunk, partition).  With a work list
@@ -277,19 +278,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     const int L_in = a.context_lens[b];
     const int bt_first = bt[min((t_begin >> lbs) + lane, a.max_blocks_per_seq - 1)];
 
-    // queries: column n = query row row_n (zero beyond the G columns)
-    vec8 qv[KC];
+    // queries: column 16t + n of tile t = query row row_of(16t + n) (zero beyond the G
+    // columns)
+    vec8 qv[NT][KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      if (n < G) {
-        const char* qp =
-            reinterpret_cast<const char*>(a.q) + (row_of(n) * D + 32 * c + 8 * j) * 2;
-        qv[c] = *reinterpret_cast<const vec8*>(qp);
-      } else {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) qv[c][r] = (scalar)0.0f;
+      for (int c = 0; c < KC; ++c) {
+        if (16 * t + n < G) {
+          const char* qp = reinterpret_cast<const char*>(a.q) +
+                           (row_of(16 * t + n) * D + 32 * c + 8 * j) * 2;
+          qv[t][c] = *reinterpret_cast<const vec8*>(qp);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) qv[t][c][r] = (scalar)0.0f;
+        }
       }
-    }
 
     const int L = clamp_len(L_in, a.max_blocks_per_seq, a.block_size);
     if (L <= 0) {
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     const int last_blk = (L - 1) >> lbs;
     // query qi sits at position L - Q + qi and sees the positions up to its own
     const int lim_lo = L - Q + 1;        // the smallest column limit (uniform)
-    const int lim_n = lim_lo + n / Gh;  // this lane's column
+    const int lim_n = lim_lo + n / Gh;  // this lane's column of tile 0
     const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * head_tile;
     const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * head_tile;
 
@@ -350,65 +354,79 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       }
     };
 
-    f32x4_t o[VC];
+    f32x4_t o[NT][VC];
 #pragma unroll
-    for (int c = 0; c < VC; ++c) o[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m = -INFINITY;  // running max of head n (log2 domain), uniform over j
-    float lsum = 0.0f;    // this lane's share of head n's sum
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int c = 0; c < VC; ++c) o[t][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m[NT];     // running max of column 16t + n (log2 domain), uniform over j
+    float lsum[NT];  // this lane's share of that column's sum
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      m[t] = -INFINITY;
+      lsum[t] = 0.0f;
+    }
 
     auto compute = [&](Buffers<KV, D>& buf, int t0, int t_stop) {
-      f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) sacc = M::qk(St::k(buf.k[c]), qv[c], sacc);
-      float s[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] = sacc[r] * a.scale_log2;
       vec4 vv[VC];
 #pragma unroll
       for (int c = 0; c < VC; ++c) vv[c] = St::v(buf.v[c]);
-      if (t0 + kChunk > min(t_stop, lim_lo)) {  // uniform: the chunk reaches a limit
-        // scores past the partition / context or past the column's query are
-        // masked; values past the context are zeroed (they may hold anything)
+      // uniform: the chunk reaches the context end, the partition end or a query's limit
+      const bool edge = t0 + kChunk > min(t_stop, lim_lo);
+      if (edge) {
+        // values past the context are zeroed (they may hold anything)
         const int nv = t_stop - t0 - 4 * j;  // tokens of this lane's run inside the range
-        const int ns = min(t_stop, lim_n) - t0 - 4 * j;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = r < ns ? s[r] : -INFINITY;
 #pragma unroll
         for (int c = 0; c < VC; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (r >= nv) vv[c][r] = (scalar)0.0f;
       }
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      // a column with every score so far masked keeps m = -inf; exponents are
-      // then taken against 0 so that they give 0, not NaN
-      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = fast_exp2(m - m_ref);
-      m = m_new;
-      vec4 phi, plo;
-      float ps = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(s[r] - m_ref);
-        ps += p;
-        const scalar hi = (scalar)p;
-        phi[r] = hi;
-        plo[r] = (scalar)(p - (float)hi);
-      }
-      lsum = lsum * alpha + ps;
-      if (__any(alpha != 1.0f)) {
+      for (int t = 0; t < NT; ++t) {
+        f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c = 0; c < VC; ++c)
+        for (int c = 0; c < KC; ++c) sacc = M::qk(St::k(buf.k[c]), qv[t][c], sacc);
+        float s[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[c][r] *= alpha;
-      }
+        for (int r = 0; r < 4; ++r) s[r] = sacc[r] * a.scale_log2;
+        if (edge) {  // scores past the range or past the column's query are masked
+          const int lim = t == 0 ? lim_n : lim_lo + (16 * t + n) / Gh;
+          const int ns = min(t_stop, lim) - t0 - 4 * j;
 #pragma unroll
-      for (int c = 0; c < VC; ++c) {
-        o[c] = M::pv(vv[c], phi, o[c]);
-        o[c] = M::pv(vv[c], plo, o[c]);
+          for (int r = 0; r < 4; ++r) s[r] = r < ns ? s[r] : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m[t], mx);
+        // a column with every score so far masked keeps m = -inf; exponents are
+        // then taken against 0 so that they give 0, not NaN
+        const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = fast_exp2(m[t] - m_ref);
+        m[t] = m_new;
+        vec4 phi, plo;
+        float ps = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(s[r] - m_ref);
+          ps += p;
+          const scalar hi = (scalar)p;
+          phi[r] = hi;
+          plo[r] = (scalar)(p - (float)hi);
+        }
+        lsum[t] = lsum[t] * alpha + ps;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int c = 0; c < VC; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[t][c][r] *= alpha;
+        }
+#pragma unroll
+        for (int c = 0; c < VC; ++c) {
+          o[t][c] = M::pv(vv[c], phi, o[t][c]);
+          o[t][c] = M::pv(vv[c], plo, o[t][c]);
+        }
       }
     };
 
@@ -442,8 +460,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     }
 
     // ---- finish the work item ------------------------------------------------
-    float l = lsum + __shfl_xor(lsum, 16);
-    l += __shfl_xor(l, 32);
+    float l[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      l[t] = lsum[t] + __shfl_xor(lsum[t], 16);
+      l[t] += __shfl_xor(l[t], 32);
+    }
     if (W > 1) {
       // Merge the waves: M = max_w m_w, l = sum_w 2^(m_w - M) l_w, and the
       // accumulators likewise.  A wave without tokens for a column has m =
@@ -451,36 +473,44 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       // whose position lies before this partition), the column's l is 0 and
       // exponents are taken against 0.  Every wave parks its rescaled
       // accumulators in LDS, then the whole workgroup sums them and stores.
-      float* red_m = red;         // [W][16]
-      float* red_l = red + 64;    // [W][16]
-      float* red_o = red + 128;   // [W][G][D + 4] (rows padded against bank conflicts)
+      constexpr int CW = 16 * NT;  // columns per wave row of red_m / red_l
+      float* red_m = red;               // [W][CW]
+      float* red_l = red + 4 * CW;      // [W][CW]
+      float* red_o = red + 8 * CW;      // [W][G][D + 4] (rows padded against bank conflicts)
       constexpr int RS = D + 4;
-      if (j == 0) {
-        red_m[wave * 16 + n] = m;
-        red_l[wave * 16 + n] = l;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (j == 0) {
+          red_m[wave * CW + 16 * t + n] = m[t];
+          red_l[wave * CW + 16 * t + n] = l[t];
+        }
       }
       __syncthreads();
-      float M = -INFINITY;
-      for (int w = 0; w < W; ++w) M = fmaxf(M, red_m[w * 16 + n]);
-      const float sc = fast_exp2(m - (M == -INFINITY ? 0.0f : M));
-      if (n < G) {
 #pragma unroll
-        for (int c = 0; c < VC; ++c) {
-          f32x4_t x = o[c];
+      for (int t = 0; t < NT; ++t) {
+        float M = -INFINITY;
+        for (int w = 0; w < W; ++w) M = fmaxf(M, red_m[w * CW + 16 * t + n]);
+        const float sc = fast_exp2(m[t] - (M == -INFINITY ? 0.0f : M));
+        if (16 * t + n < G) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] *= sc;
-          *reinterpret_cast<f32x4_t*>(red_o + (wave * G + n) * RS + 16 * c + 4 * j) = x;
+          for (int c = 0; c < VC; ++c) {
+            f32x4_t x = o[t][c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] *= sc;
+            *reinterpret_cast<f32x4_t*>(red_o + (wave * G + 16 * t + n) * RS + 16 * c + 4 * j) =
+                x;
+          }
         }
       }
       __syncthreads();
       for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
         const int g = e / D, d = e - g * D;
         float Mg = -INFINITY;
-        for (int w = 0; w < W; ++w) Mg = fmaxf(Mg, red_m[w * 16 + g]);
+        for (int w = 0; w < W; ++w) Mg = fmaxf(Mg, red_m[w * CW + g]);
         const float Mref = Mg == -INFINITY ? 0.0f : Mg;
         float lt = 0.0f, x = 0.0f;
         for (int w = 0; w < W; ++w) {
-          lt += red_l[w * 16 + g] * fast_exp2(red_m[w * 16 + g] - Mref);
+          lt += red_l[w * CW + g] * fast_exp2(red_m[w * CW + g] - Mref);
           x += red_o[(w * G + g) * RS + d];
         }
         const int64_t row_id = row_of(g);
@@ -498,29 +528,34 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       __syncthreads();  // the merge area is free for the next item
       goto next_item;
     }
-    if (n < G) {
-      const int64_t row_id = row_of(fresh_tid() & 15);  // re-derived: not held through the loop
-      if (n_parts == 1) {
-        const float inv = l > 0.0f ? a.v_scale / l : 0.0f;  // l = 0: a query before position 0
 #pragma unroll
-        for (int c = 0; c < VC; ++c)
+    for (int t = 0; t < NT; ++t) {
+      const int col = 16 * t + (fresh_tid() & 15);  // re-derived: not held through the loop
+      if (col < G) {
+        const int64_t row_id = row_of(col);
+        if (n_parts == 1) {
+          // l = 0: a query before position 0
+          const float inv = l[t] > 0.0f ? a.v_scale / l[t] : 0.0f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            store_elem(a.out, row_id * D + 16 * c + 4 * j + r, o[c][r] * inv, a.out_dtype);
-      } else {
-        const int64_t slot = row_id * a.max_partitions + part;
-        float* dst = a.ws_acc + slot * D;
-        const float vs = a.v_scale;
+          for (int c = 0; c < VC; ++c)
 #pragma unroll
-        for (int c = 0; c < VC; ++c) {
-          f32x4_t x = o[c];
+            for (int r = 0; r < 4; ++r)
+              store_elem(a.out, row_id * D + 16 * c + 4 * j + r, o[t][c][r] * inv, a.out_dtype);
+        } else {
+          const int64_t slot = row_id * a.max_partitions + part;
+          float* dst = a.ws_acc + slot * D;
+          const float vs = a.v_scale;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] *= vs;
-          *reinterpret_cast<f32x4_t*>(dst + 16 * c + 4 * j) = x;
-        }
-        if (j == 0) {
-          a.ws_ml[slot * 2] = m;
-          a.ws_ml[slot * 2 + 1] = l;
+          for (int c = 0; c < VC; ++c) {
+            f32x4_t x = o[t][c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] *= vs;
+            *reinterpret_cast<f32x4_t*>(dst + 16 * c + 4 * j) = x;
+          }
+          if (j == 0) {
+            a.ws_ml[slot * 2] = m[t];
+            a.ws_ml[slot * 2 + 1] = l[t];
+          }
         }
       }
     }
@@ -542,11 +577,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
   }  // work items
 }
 
-// LDS of the wave merge: m and l of 16 columns per wave, then every wave's
-// padded accumulators.
-size_t merge_lds_bytes(int waves, int heads, int head_dim) {
+// LDS of the wave merge: m and l of 16 columns per tile for up to 4 waves,
+// then every wave's padded accumulators.
+size_t merge_lds_bytes(int waves, int cols, int head_dim) {
   if (waves <= 1) return 0;
-  return (128 + (size_t)waves * heads * (head_dim + 4)) * sizeof(float);
+  const size_t cw = 16 * (size_t)((cols + 15) / 16);
+  return (8 * cw + (size_t)waves * cols * (head_dim + 4)) * sizeof(float);
 }
 
 template <Elem KV, int D>
@@ -562,7 +598,7 @@ hipError_t dispatch_g(const DecodeArgs& a, int64_t items_x, hipStream_t s) {
             : reinterpret_cast<const void*>(&decode_mfma_kernel<KV, D, GG, false>);   \
     break;
     PA_CASE(1) PA_CASE(2) PA_CASE(4) PA_CASE(8) PA_CASE(16)
-    PA_CASE(3) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(10) PA_CASE(12)
+    PA_CASE(3) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(10) PA_CASE(12) PA_CASE(24) PA_CASE(32)
 #undef PA_CASE
     default:
       return hipErrorInvalidValue;
@@ -575,6 +611,7 @@ hipError_t dispatch_g(const DecodeArgs& a, int64_t items_x, hipStream_t s) {
 bool mfma_supports_heads(int heads_per_item) {
   switch (heads_per_item) {
     case 1: case 2: case 3: case 4: case 5: case 6: case 7: case 8: case 10: case 12: case 16:
+    case 24: case 32:
       return true;
     default:
       return false;

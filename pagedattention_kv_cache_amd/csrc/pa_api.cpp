@@ -42,12 +42,13 @@ int32_t heads_per_item(int32_t g, int32_t cap) {
   return 0;
 }
 
-// Matrix-core tile: the q heads per item h, the largest divisor of g whose Q
-// x h columns (Q query tokens per sequence) fit one 16-column tile with an
-// instantiated width; 0 when there is none.
+// Matrix-core items: the q heads per item h, the largest divisor of g whose Q
+// x h columns (Q query tokens per sequence) fit one or two 16-column tiles
+// with an instantiated width; 0 when there is none.  Two tiles share every
+// key and value load.
 int32_t mfma_heads_per_item(int32_t g, int32_t num_queries) {
-  for (int32_t h = g < 16 ? g : 16; h >= 1; --h)
-    if (g % h == 0 && num_queries * h <= 16 && pa::mfma_supports_heads(num_queries * h))
+  for (int32_t h = g < 32 ? g : 32; h >= 1; --h)
+    if (g % h == 0 && num_queries * h <= 32 && pa::mfma_supports_heads(num_queries * h))
       return h;
   return 0;
 }

@@ -405,6 +405,8 @@ def test_decode_mq_kernel_policy():
     assert k(2, 32, 32, F16, F16, 0) == pa.FORCE_MFMA     # MHA, 2 query tokens: 2 columns
     assert k(4, 32, 8, BF16, BF16, 0) == pa.FORCE_MFMA
     assert k(16, 8, 8, BF16, BF16, 0) == pa.FORCE_MFMA    # 16 columns of one head
+    assert k(4, 64, 8, BF16, BF16, 0) == pa.FORCE_MFMA    # 32 columns: two tiles
+    assert k(16, 16, 8, F16, F16, 0) == pa.FORCE_MFMA     # 16 queries x 2 heads
     assert k(16, 8, 8, BF16, BF16, pa.FORCE_VALU) == EUNSUP
     assert k(8, 8, 8, F32, F32, 0) == pa.FORCE_VALU       # fp32: vector ALUs, up to 8 rows
     assert k(10, 8, 8, F32, F32, 0) == EUNSUP

@@ -107,6 +107,11 @@ MQ_CASES = [
     ("f16", 128, 16, 6, 2, [7, 16, 17, 600], 7),
     ("f16", 128, 16, 3, 1, [12, 40, 333], 12),
     ("f16", 128, 16, 2, 2, [16, 20, 301], 16),
+    # two 16-column tiles over one K/V read: 24 or 32 (query, head) columns per item
+    ("bf16", 128, 16, 32, 4, [4, 100, 1300, 2500], 4),
+    ("bf16", 64, 16, 16, 2, [3, 50, 700], 3),
+    ("f16", 128, 32, 16, 4, [6, 333, 1200], 6),
+    ("bf16", 128, 16, 32, 8, [8, 64, 800, 1700], 8),
     ("f32", 128, 16, 8, 2, [4, 40, 129], 2),
     ("f32", 64, 8, 4, 4, [8, 9, 250], 8),
 ]
@@ -136,9 +141,9 @@ def test_decode_mq_parity_small(case, partition, kernel, waves):
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
-@pytest.mark.parametrize("Q", [2, 4])
-def test_decode_mq_fp8_cache(kernel, Q):
-    cfg = custom_config("mq-fp8", [4, 100, 777, 1300], 16, 4, 128, "bf16", 16, seed=61 + Q,
+@pytest.mark.parametrize("Q,hq", [(2, 16), (4, 16), (4, 32)])
+def test_decode_mq_fp8_cache(kernel, Q, hq):
+    cfg = custom_config("mq-fp8", [4, 100, 777, 1300], hq, 4, 128, "bf16", 16, seed=61 + Q,
                         cache_dtype="fp8", fp8_scales=(2.0 ** -5, 0.0371))
     wl, gs, st = _states(cfg)
     _say(f"mq fp8 decode Q={Q} {kernel}")
@@ -235,7 +240,8 @@ def _sample_rows(wl: Workload, Q: int, n: int, seed: int) -> np.ndarray:
     return rows.astype(np.int64)
 
 
-@pytest.mark.parametrize("cid,Q,fp8", [(4, 4, False), (4, 2, True), (5, 2, False)])
+@pytest.mark.parametrize("cid,Q,fp8", [(4, 4, False), (4, 2, True), (5, 2, False), (5, 4, False),
+                                        (4, 8, False)])
 def test_full_workload_mq_parity(cid, Q, fp8):
     """The GQA workloads at full size with Q query tokens per sequence (library-picked
     launch), on sampled rows and every row of the longest sequence."""
