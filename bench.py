@@ -398,7 +398,8 @@ def run(args):
     slots = [torch.from_numpy(wl.step_slots(s)).to(dev) for s in range(c.steps)]
     ctx = [torch.from_numpy(wl.context_lens(s)).to(dev) for s in range(c.steps)]
     MB = wl.max_blocks_per_seq
-    p_eff = part if part else pa.decode_partition_size(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+    p_eff = part if part else pa.decode_partition_size(c.num_seqs * Q, c.num_q_heads,
+                                                       c.num_kv_heads,
                                                        c.head_dim, c.block_size, MB, kdt, flags)
     ws_bytes = pa.decode_workspace_size(c.num_seqs * Q, c.num_q_heads, c.num_kv_heads,
                                         c.head_dim, c.block_size, MB, part, kdt, flags)

@@ -312,7 +312,9 @@ int pa_decode_step_partitions(const void* k, const void* v, const int64_t* slot_
  *   num_queries    1 .. 16
  *   kv_dtype       any cache dtype; k_scale, v_scale as in pa_decode_fp8 (pass
  *                  1 for the unscaled types)
- *   workspace      pa_decode_workspace_size(num_seqs * num_queries, ...) bytes
+ *   workspace      pa_decode_workspace_size(num_seqs * num_queries, ...) bytes;
+ *                  the other plan queries (partition size, waves, grid) also
+ *                  take num_seqs * num_queries for a multi-query decode
  * Other arguments, errors and the phase split as pa_decode.
  */
 int pa_decode_mq(void* out, const void* q, const void* k_cache, const void* v_cache,

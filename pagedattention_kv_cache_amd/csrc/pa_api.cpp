@@ -135,19 +135,28 @@ int check_shape(const DecodeShape& s) {
   return PA_OK;
 }
 
-// Partition policy for partition_size == 0: about a quarter of the longest
-// context the block table can hold, as a power of two in [256, 4096] tokens.
-// With up to four waves per item (pick_waves) the longest sequence still
-// spreads over ~16 waves, while items stay long enough to amortise their
-// start-up (context length, block-id window and first chunk are dependent
-// loads before a wave streams) and the merge traffic stays near 1% of the KV
-// bytes.  Measured on the MHA, GQA and long-context 16-bit workloads, this
-// lands on the best power-of-two size or within 2% of it.  One pass when the
-// longest context fits a partition.
+// Partition policy for partition_size == 0.
+//  - Mixed lengths: about a quarter of the longest context the block table can
+//    hold, as a power of two in [1024, 8192] tokens, so the longest sequence
+//    spreads over four or more items (16 waves) while items stay long enough
+//    to amortise their start-up (context length, block-id window and first
+//    chunk are dependent loads before a wave streams) and the merge stays near
+//    1% of the KV bytes.
+//  - Small batches: halved (down to 512) until the launch has at least one
+//    (sequence, kv head, partition) item per compute unit of the device (256).
+// Measured (decode kernel, best power of two in parentheses): GQA lognormal
+// batch 2048 (2048), MHA batch of <= 2048 tokens 1024 (1024), 64 x 4k-32k
+// contexts 8192 (8192), 4 x 32k 4096 (4096), 1 x 32k 1024 (1024; 4096 was
+// 1.6x slower), 1 x 4k 512 (512), 16 x 16k 4096 (8192, 1.6% faster).  One
+// pass when the longest context fits a partition.
+constexpr int64_t kItemsTarget = 256;
+
 int32_t pick_partition(const DecodeShape& s) {
   const int64_t max_ctx = (int64_t)s.max_blocks_per_seq * s.block_size;
-  int64_t p = 256;
-  while (p < 4096 && p * 4 < max_ctx) p *= 2;
+  int64_t p = 1024;
+  while (p < 8192 && p * 4 < max_ctx) p *= 2;
+  const int64_t seq_heads = (int64_t)s.num_seqs * s.num_kv_heads;
+  while (p > 512 && seq_heads * ((max_ctx + p - 1) / p) < kItemsTarget) p /= 2;
   if (p % s.block_size) p = ((p + s.block_size - 1) / s.block_size) * s.block_size;
   if (max_ctx <= p) return (int32_t)max_ctx;  // one pass
   return (int32_t)p;
@@ -530,14 +539,16 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
 
-  const int64_t max_ctx = (int64_t)max_blocks_per_seq * block_size;
-  int32_t p = partition_size ? partition_size : pick_partition(s);
-  if (p > max_ctx) p = (int32_t)max_ctx;
-  const int64_t np = n_partitions(s, p);
-  // the workspace holds a (m, l) pair and a partial vector per query row
+  // The workspace holds a (m, l) pair and a partial vector per query row, and
+  // the plan queries take num_seqs * num_queries for a multi-query decode: the
+  // partition is picked on that shape too, so that both agree.
   DecodeShape rows_shape = s;
   if ((int64_t)num_seqs * num_queries > 0x7fffffffLL) return PA_ERR_SHAPE;
   rows_shape.num_seqs = num_seqs * num_queries;
+  const int64_t max_ctx = (int64_t)max_blocks_per_seq * block_size;
+  int32_t p = partition_size ? partition_size : pick_partition(rows_shape);
+  if (p > max_ctx) p = (int32_t)max_ctx;
+  const int64_t np = n_partitions(s, p);
   const size_t need = workspace_bytes_for(rows_shape, p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;

@@ -221,13 +221,18 @@ def test_partition_policy_and_workspace_size():
     # one pass when the longest context fits one partition: no workspace
     assert L.pa_decode_partition_size(4, 4, 4, 64, 16, 13, F32, 0) == 208
     assert L.pa_decode_workspace_size(4, 4, 4, 64, 16, 13, 0, F32, 0) == 0
-    # about a quarter of the longest context, a power of two in [256, 4096]
-    assert L.pa_decode_partition_size(64, 32, 32, 128, 16, 128, F16, 0) == 512     # 2048 max
+    # about a quarter of the longest context, a power of two in [1024, 8192] ...
+    assert L.pa_decode_partition_size(64, 32, 32, 128, 16, 128, F16, 0) == 1024    # 2048 max
     assert L.pa_decode_partition_size(32, 40, 40, 128, 16, 256, F16, 0) == 1024    # 4096 max
     assert L.pa_decode_partition_size(256, 32, 8, 128, 16, 512, BF16, 0) == 2048   # 8192 max
-    assert L.pa_decode_partition_size(64, 64, 8, 128, 32, 1025, BF16, 0) == 4096   # 32800 max
-    assert L.pa_decode_partition_size(1, 8, 8, 128, 16, 100000, BF16, 0) == 4096   # capped
-    assert L.pa_decode_partition_size(4, 8, 8, 128, 16, 40, BF16, 0) == 256        # 640 max
+    assert L.pa_decode_partition_size(64, 64, 8, 128, 32, 1025, BF16, 0) == 8192   # 32800 max
+    assert L.pa_decode_partition_size(16, 8, 8, 128, 16, 100000, BF16, 0) == 8192  # capped
+    # ... halved (down to 512) until sequences x kv heads x partitions >= 256
+    assert L.pa_decode_partition_size(1, 64, 8, 128, 16, 2048, BF16, 0) == 1024    # 1 x 32k
+    assert L.pa_decode_partition_size(4, 64, 8, 128, 16, 2048, BF16, 0) == 4096    # 4 x 32k
+    assert L.pa_decode_partition_size(1, 64, 8, 128, 16, 256, BF16, 0) == 512      # 1 x 4k
+    assert L.pa_decode_partition_size(4, 8, 8, 128, 16, 40, BF16, 0) == 512        # 640 max
+    assert L.pa_decode_partition_size(4, 8, 8, 128, 16, 30, BF16, 0) == 480        # one pass
     # workspace = (m, l) and a head_dim vector per (seq, q head, partition), 256-B aligned
     B, Hq, d, MB, bs, P = 256, 32, 128, 512, 16, 512
     n_part = MB * bs // P
