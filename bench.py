@@ -36,8 +36,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published
-KERNEL_SOURCES = ["decode_valu.hip", "decode_mfma.hip", "pa_device.hpp", "pa_launch.hpp",
-                  "pa_api.cpp", "../build.py"]
+KERNEL_SOURCES = ["decode_valu.hip", "decode_mfma.hip", "decode_order.hip", "work_list.hpp",
+                  "pa_device.hpp", "pa_launch.hpp", "pa_api.cpp", "../build.py"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
 
 
