@@ -330,8 +330,8 @@ def run(args):
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the paged decode "
-                          "path has no multi-GPU mode here (see DESIGN.md for how it would "
-                          "shard)", "n_gpus": args.gpus}))
+                          "path has no multi-GPU mode here (it would shard by sequences or by "
+                          "kv heads, with no exchange inside the path)", "n_gpus": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -417,7 +417,7 @@ def run(args):
         # step i: decode step (i // n_layers) % steps of layer i % n_layers
         s = (i // n_layers) % c.steps
         k_l, v_l = kcs[i % n_layers], vcs[i % n_layers]
-        if ev is not None:
+        if ev is not None and ev[0] is not None:
             ev[0].record(stream)
         if fused:
             if ev is not None:
@@ -444,13 +444,21 @@ def run(args):
         else:
             pa.decode_merge(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
                             flags)
-        if ev is not None:
+        if ev is not None and ev[3] is not None:
             ev[3].record(stream)
+
+    def events():
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                for _ in range(args.steps)]
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: only the decode launches are bracketed by events (each
+    # event record is one more packet between the kernels of a step).
+    evs = events()
+    for e in evs:
+        e[0] = e[3] = None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -458,9 +466,15 @@ def run(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    write_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
     dec_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    # Breakdown pass (after the timed region, same steps): events around every launch.
+    evs = events()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    write_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
     merge_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
+    dec_ms_breakdown = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
 
     kv = statistics.mean(wl.kv_bytes((i // n_layers) % c.steps) for i in range(args.steps))
     value = kv / (ms_step * 1e-3) / 1e9
@@ -510,6 +524,7 @@ def run(args):
         "fused_write": fused,
         "decode_partitions_ms": round(dec_ms, 5),
         "decode_merge_ms": round(merge_ms, 5),
+        "decode_partitions_ms_breakdown_pass": round(dec_ms_breakdown, 5),
         "roofline": {
             "kernel": kname,
             "bound": "hbm",

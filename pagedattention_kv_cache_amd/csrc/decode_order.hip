@@ -42,26 +42,36 @@ __device__ __forceinline__ void order_items(const DecodeArgs& a, int32_t* order)
   const int np = a.max_partitions, P = a.partition_size, B = a.num_seqs;
   for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
   __syncthreads();
+  int L_own = 0;  // the length of sequence tid, kept for the second pass
   for (int b = tid; b < B; b += kThreads) {
     const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
+    if (b == tid) L_own = L;
     const int n = seq_items(L, P, np);
     for (int p = 0; p < n; ++p) atomicAdd(&hist[L <= 0 ? 0 : item_bin(L, p, P)], 1);
   }
   __syncthreads();
-  // start[bin] = items in larger bins (an exclusive scan from the top bin down)
-  int v = hist[kBins - 1 - tid];
-  for (int off = 1; off < kBins; off *= 2) {
-    start[tid] = v;
-    __syncthreads();
-    if (tid >= off) v += start[tid - off];
-    __syncthreads();
+  // start[bin] = items in larger bins: thread tid takes bin kBins - 1 - tid,
+  // so an inclusive prefix sum over the threads counts the tid + 1 largest
+  // bins; within a wave by lane shuffles, across waves through LDS.
+  __shared__ int wave_sum[kThreads / 64];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int own = hist[kBins - 1 - tid];
+  int v = own;
+#pragma unroll
+  for (int off = 1; off < 64; off *= 2) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
   }
-  start[kBins - 1 - tid] = v - hist[kBins - 1 - tid];  // v: the tid + 1 largest bins
+  if (lane == 63) wave_sum[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) v += wave_sum[w];
+  start[kBins - 1 - tid] = v - own;
   __syncthreads();
   const int total = start[0] + hist[0];
   __syncthreads();
   for (int b = tid; b < B; b += kThreads) {
-    const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
+    const int L =
+        b == tid ? L_own : clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
     const int n = seq_items(L, P, np);
     for (int p = 0; p < n; ++p)
       order[atomicAdd(&start[L <= 0 ? 0 : item_bin(L, p, P)], 1)] = b * np + p;

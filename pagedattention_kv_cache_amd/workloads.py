@@ -97,8 +97,9 @@ def _lognormal(median: float, sigma: float, lo: int, hi: int):
     return f
 
 
-# The five decode workloads.  Config 1 is the small case the oracle finishes in
-# seconds; config 4 (Llama-3-8B-shaped GQA) is the throughput workload.
+# The five decode workloads, numbered 1..5.  Number 1 (4 fp32 sequences of at
+# most 200 tokens) is the small case the oracle finishes in seconds; number 4
+# (256 Llama-3-8B-shaped GQA sequences, bf16) is the throughput workload.
 CONFIGS: dict[int, DecodeConfig] = {
     1: DecodeConfig("tiny-fp32", 4, 4, 4, 64, "f32", 16, seed=1,
                     lengths=_fixed([1, 17, 64, 200]), num_blocks=64),
@@ -121,7 +122,7 @@ def fp8_variant(cfg: DecodeConfig, k_scale: float, v_scale: float) -> DecodeConf
                                cache_dtype="fp8", fp8_scales=(k_scale, v_scale))
 
 
-# E4M3-cache variants of the GQA workloads (the KV of configs 4 and 5 are
+# E4M3-cache variants of the two GQA workloads (their KV are
 # N(0, 0.5^2) / N(0, 1) keys and N(0, 1) values: with these scales every drawn
 # value lands well inside the E4M3 range, the largest near 200).
 FP8_CONFIGS: dict[int, DecodeConfig] = {

@@ -220,6 +220,65 @@ def test_grid_modes_agree_bit_for_bit(kernel, dtype, hq, hkv, waves, P):
     _check_decode(modes[pa.SORTED_GRID], st.decode(0, threads=8), dtype)
 
 
+def _order_of_workspace(ws: torch.Tensor, B: int, Hq: int, D: int, n_parts: int) -> np.ndarray:
+    """The item order a sorted-grid decode leaves in its workspace.  Internal
+    layout (not part of the C ABI): (m, l) per (sequence, q head, partition),
+    then the partial outputs, each rounded up to 256 bytes, then the order of
+    B * n_parts int32 entries."""
+    def up(v):
+        return (v + 255) // 256 * 256
+    rows = B * Hq * n_parts
+    off = up(rows * 2 * 4) + up(rows * D * 4)
+    raw = ws.view(torch.uint8)[off:off + B * n_parts * 4].cpu().numpy()
+    return raw.view(np.int32)
+
+
+@pytest.mark.parametrize("P", [256, 1024])
+def test_ordering_kernel_is_longest_first_over_every_item(P):
+    """The ordering kernel's output, read back: every non-empty (sequence,
+    partition) item exactly once, sizes (in 16-token chunks, capped at 1023)
+    never increasing, then -1 for the unused entries.  Items of equal size may
+    come in any order, so the check is on the multiset and the size sequence.
+    Includes empty sequences (one item each, size 0, last among the items)."""
+    rng = np.random.default_rng(77 + P)
+    lens = rng.integers(1, 5000, size=200).tolist()
+    lens[:4] = [1, 4999, 16, 17]
+    cfg = custom_config(f"order-{P}", lens, 8, 2, 128, "bf16", 16, seed=5)
+    wl = Workload(cfg)
+    gs = GpuState(wl)
+    gs.write_step(0)
+    ctx_host = np.array(lens, dtype=np.int32)
+    ctx_host[[7, 50]] = 0  # two empty sequences
+    ctx = torch.from_numpy(ctx_host).cuda()
+    flags = pa.FORCE_MFMA | pa.SORTED_GRID
+    MB = wl.max_blocks_per_seq
+    assert pa.decode_grid(cfg.num_seqs, 8, 2, 128, 16, MB, P, gs.kc.dtype, gs.kc.dtype,
+                          flags) == pa.GRID_NAMES[pa.SORTED_GRID]
+    wsb = pa.decode_workspace_size(cfg.num_seqs, 8, 2, 128, 16, MB, P, gs.kc.dtype, flags)
+    ws = torch.full((wsb,), 0x5A, dtype=torch.uint8, device="cuda")
+    out = torch.empty(gs.q[0].shape, dtype=torch.float32, device="cuda")
+    pa.decode_partitions(out, gs.q[0], gs.kc, gs.vc, gs.block_tables, ctx, cfg.attn_scale(), 16,
+                         P, ws, flags)
+    torch.cuda.synchronize()
+    n_parts = -(-MB * 16 // P)
+    order = _order_of_workspace(ws, cfg.num_seqs, 8, 128, n_parts)
+
+    def size_bin(L, p):
+        return 0 if L == 0 else min((min(L - p * P, P) + 15) // 16, 1023)
+
+    items = []
+    for b, L in enumerate(ctx_host.tolist()):
+        n = 1 if L == 0 else -(-L // P)
+        items += [(b * n_parts + p, size_bin(L, p)) for p in range(n)]
+    k = len(items)
+    head = order[:k]
+    assert sorted(head.tolist()) == sorted(e for e, _ in items), "items missing or repeated"
+    bins = dict(items)
+    sizes = [bins[e] for e in head.tolist()]
+    assert all(x >= y for x, y in zip(sizes, sizes[1:])), "order is not longest first"
+    assert (order[k:] == -1).all(), "unused entries are not -1"
+
+
 def test_sorted_grid_with_empty_sequences():
     """Zero-length sequences are items too (their rows are zeroed), ordered last."""
     lens = [0, 700, 0, 1, 1500, 0]
