@@ -97,12 +97,15 @@ typedef enum pa_status {
  *                           (the items that hold no tokens exit at once);
  *   PA_DECODE_SORTED_GRID   the items that hold tokens, longest first (a
  *                           one-workgroup kernel orders them on the device
- *                           before the decode, in the workspace): one
- *                           workgroup per possible item in that order, or,
- *                           with partitions of 1024 tokens or more, a
- *                           persistent grid whose workgroups take the next
- *                           item of the order from a counter when they
- *                           finish one;
+ *                           before the decode, in the workspace), taken
+ *                           by a persistent grid (as many workgroups as fit
+ *                           on the device): with partitions of 1024 tokens
+ *                           or more each workgroup takes the next item of
+ *                           the order from a counter when it finishes one;
+ *                           with shorter partitions the order is dealt in
+ *                           fixed snake rounds (round r of workgroup i:
+ *                           entry r * workgroups + i, mirrored on odd
+ *                           rounds);
  *   PA_DECODE_WORK_LIST     a persistent grid (as many workgroups as fit on
  *                           the device) walking the list of items that hold
  *                           tokens, which each workgroup builds in LDS.

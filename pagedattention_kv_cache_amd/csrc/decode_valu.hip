@@ -163,6 +163,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
     step = (int)gridDim.x;
   }
   if (args.order_ctr) n_work = 0x7fffffff;  // a dynamic deal: until the order runs out
+  if (args.order_static) {                   // a static deal: until the order runs out
+    n_work = 0x7fffffff;
+    step = (int)gridDim.x;
+  }
   __shared__ int ticket_lds[2];
   // Round r takes entry r * gridDim.x + blockIdx.x, or the mirrored one on
   // odd rounds: the list runs longest first, so a workgroup that drew a long
@@ -205,8 +209,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
       hc = it - item * per_seq;
       work_item(dyn_lds, a.max_partitions, item, cursor, b, part);
     } else if (a.order) {
-      const int64_t lin =
-          a.order_ctr ? (int64_t)it : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+      const int64_t lin = a.order_ctr || a.order_static
+                              ? (int64_t)it
+                              : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
       const int64_t e = lin / per_seq;
       hc = (int)(lin - e * per_seq);
       if (e >= (int64_t)a.num_seqs * a.max_partitions) break;  // past the order: done
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs args) {
       ++round;
       continue;
     }
-    if (!listed) break;
+    if (!listed && !fresh_args()->order_static) break;
     ++round;
     it = round * step + ((round & 1) ? step - 1 - bx : bx);
   }  // work items

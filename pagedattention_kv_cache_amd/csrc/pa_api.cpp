@@ -204,6 +204,16 @@ enum GridMode { kGridNatural = 0, kGridSorted = 1, kGridList = 2 };
 // is paid once per item, and short items are many.
 constexpr int32_t kPersistentOrderMin = 1024;
 
+// Below that, a sorted grid is still persistent, but deals the order in fixed
+// snake rounds (no counter): one workgroup per possible item launched, on a
+// batch of uneven lengths, thousands of empty workgroups that each read their
+// order entry before exiting.  Measured (decode kernel incl. ordering, us,
+// one workgroup per possible item -> static deal, two runs each): skewed
+// batch at 512-token partitions 47.3/47.6 -> 44.8/44.5, GQA lognormal batch
+// forced to 512 321.2/321.1 -> 308.0/307.1; but uniform MHA batch forced to
+// 512 185.0/186.8 -> 190.6/192.1 and to 256 190.4/192.8 -> 193.8/194.2 (items
+// of one size run at uneven speeds, which dynamic dispatch absorbed).
+
 // Grid choice for a launch of np partitions.  One workgroup per possible item
 // launches num_seqs * heads * max_partitions workgroups; on a batch of mixed
 // lengths most of them hold no tokens.  In grid order the empty and short
@@ -555,7 +565,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (np > 65535 || (int64_t)num_seqs * num_queries * num_q_heads > 0x7fffffffLL)
     return PA_ERR_SHAPE;
 
-  pa::DecodeArgs a;
+  pa::DecodeArgs a{};
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
@@ -596,6 +606,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                           ws + order_offset(rows_shape, np) +
                           round_up((size_t)rows_shape.num_seqs * (size_t)np * sizeof(int32_t)))
                     : nullptr;
+  a.order_static = a.order && !a.order_ctr ? 1 : 0;  // shorter partitions: static deal
 
   hipStream_t hs = (hipStream_t)stream;
   if (phase & kPartitions) {
@@ -767,7 +778,7 @@ hipError_t launch_decode_grid(const void* kernel, const DecodeArgs& a, int64_t i
                               size_t lds, hipStream_t s) {
   const dim3 block(64 * a.waves);
   dim3 grid;
-  if (a.list_ints > 0 || a.order_ctr) {
+  if (a.list_ints > 0 || a.order_ctr || a.order_static) {
     const int64_t fit = (int64_t)cu_count() * resident_per_cu(kernel, (int)block.x, lds);
     const int64_t upper = items_x * a.max_partitions;
     const int64_t g = fit < upper ? fit : upper;

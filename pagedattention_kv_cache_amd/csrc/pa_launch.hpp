@@ -69,6 +69,11 @@ struct DecodeArgs {
   // gridDim.x + (the value of this counter, incremented) until the order runs
   // out.  The ordering kernel zeroes it.
   int32_t* order_ctr;
+  // With an order and no counter: 0, one workgroup per grid slot; 1, a
+  // persistent grid deals the order statically, in snake rounds: round r of
+  // workgroup i takes entry r * gridDim.x + i, mirrored (gridDim.x - 1 - i)
+  // on odd rounds, until the order runs out.
+  int32_t order_static;
 };
 
 // LDS ints a workgroup needs for the work list of a persistent launch.

@@ -194,9 +194,9 @@ def _decode_nan_prefilled(gs, wl, P, flags):
 def test_grid_modes_agree_bit_for_bit(kernel, dtype, hq, hkv, waves, P):
     """More sequences than a wave has lanes, 11, 4 or 3 partitions: the persistent
     grid over the work list (several items per workgroup), the sorted grid (items
-    ordered on the device; one workgroup per possible item with the empty ones
-    last, or at 1024-token partitions a persistent grid dealing the order from a
-    counter) and the grid in its own order each compute every item exactly once --
+    ordered on the device, then dealt to a persistent grid in fixed snake rounds,
+    or at 1024-token partitions from a counter) and the grid in its own order
+    each compute every item exactly once --
     bit-identical to one another, into NaN-filled outputs and workspace -- and
     within tolerance of the oracle."""
     rng = np.random.default_rng(90 + waves)
