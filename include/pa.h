@@ -86,7 +86,8 @@ typedef enum pa_status {
 #define PA_DECODE_KERNEL_MASK 3u
 /* Bits 2-3: waves per (sequence, kv head, partition) work item; the waves
  * split the item's tokens and merge their partial results on chip.  0 lets
- * the library pick. */
+ * the library pick: 4 for partitions of 1024 tokens or more, 2 from 256
+ * tokens, else 1. */
 #define PA_DECODE_WAVES_1 4u
 #define PA_DECODE_WAVES_2 8u
 #define PA_DECODE_WAVES_4 12u
@@ -110,7 +111,10 @@ typedef enum pa_status {
  *                           the device) walking the list of items that hold
  *                           tokens, which each workgroup builds in LDS.
  * A choice that does not apply (one pass; a list or order too large) falls
- * back to grid order. */
+ * back to grid order.  The library's pick (0): the sorted grid for
+ * partitions of 1024 tokens or more; below that, the work list for batches
+ * of up to 64 sequences and the sorted grid for larger ones (each where it
+ * fits, else the other, else grid order). */
 #define PA_DECODE_NO_WORK_LIST 16u
 #define PA_DECODE_SORTED_GRID 32u
 #define PA_DECODE_WORK_LIST 48u

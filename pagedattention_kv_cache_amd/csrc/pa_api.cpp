@@ -168,12 +168,14 @@ int64_t n_partitions(const DecodeShape& s, int32_t p) {
 }
 
 // Waves per work item.  An explicit PA_DECODE_WAVES_* choice wins; otherwise
-// as many (1, 2 or 4) as leave every wave at least 8 chunks of 16 tokens of
-// a full partition: splitting shortens the longest items, while a wave with
-// fewer chunks spends too much of its time starting up and merging.  Measured
-// on the MHA (partition 256: 2 waves), skewed (512: 4), GQA (1024: 4) and
-// long-context (4096: 4) 16-bit workloads, this is the best split or within
-// 1% of it.
+// 4 for partitions of 1024 tokens or more, 2 from 256 tokens, else 1:
+// splitting shortens the longest items, while a wave with few chunks spends
+// too much of its time starting up and merging.  Measured (decode kernel,
+// us): 512-token partitions, 4 -> 2 waves: skewed batch 44.5 -> 43.4 (sorted
+// grid) and 42.0 -> 40.0 (work list), GQA lognormal batch 306.9 -> 301.1
+// (sorted), MHA uniform batch 189.1 -> 188.7 (work list); 256-token
+// partitions, MHA batch, 1 -> 2 waves: 197.5 -> 191.2; at 1024 tokens and
+// more (GQA, long contexts) 4 waves stay best.
 int32_t pick_waves(const DecodeShape& s, int32_t p) {
   switch (s.flags & PA_DECODE_WAVES_MASK) {
     case PA_DECODE_WAVES_1: return 1;
@@ -181,9 +183,8 @@ int32_t pick_waves(const DecodeShape& s, int32_t p) {
     case PA_DECODE_WAVES_4: return 4;
     default: break;
   }
-  int32_t w = 1;
-  while (w < 4 && (int64_t)p >= (int64_t)256 * w) w *= 2;
-  return w;
+  if (p >= 1024) return 4;
+  return p >= 256 ? 2 : 1;
 }
 
 // Largest work list a workgroup builds in LDS (ints); beyond it, one
@@ -229,9 +230,19 @@ constexpr int32_t kPersistentOrderMin = 1024;
 // 50.6 us; GQA lognormal batch, 4 partitions 291 -> 273 -> 302 us; long
 // contexts, 9 partitions 768 -> 759 -> 764 us; MHA uniform batch, 4
 // partitions 206.5 -> 207.6 -> 216.9 us; equal lengths 290 -> 295 -> 303 us.
-// So the sorted grid wherever its order fits.  One pass never has empty
-// items.
-int grid_mode(const DecodeShape& s, int64_t np) {
+// So the sorted grid wherever its order fits (for partitions of 1024+
+// tokens since the measurements below).  One pass never has empty items.
+//
+// Below 1024-token partitions, small batches walk the work list each
+// workgroup builds in LDS (its cost grows with the batch), larger ones the
+// sorted grid's static deal.  Measured (decode kernel incl. ordering, us,
+// sorted -> work list, each at its best waves): skewed batch of 32 at 512
+// tokens 43.4 -> 40.0, MHA batch of 64 at 512 190.9 -> 188.7 and at 256
+// 193.5 -> 191.1; GQA batch of 256 at 512 301.1 -> 309.9.
+constexpr int32_t kListMaxSeqs = 64;
+
+int grid_mode(const DecodeShape& s, int32_t p) {
+  const int64_t np = n_partitions(s, p);
   if (np <= 1) return kGridNatural;
   const bool list_fits = pa::work_list_lds_ints(s.num_seqs, (int)np) <= kMaxListInts;
   const bool order_fits = (int64_t)s.num_seqs * np <= kMaxOrder;
@@ -241,12 +252,15 @@ int grid_mode(const DecodeShape& s, int64_t np) {
     case PA_DECODE_WORK_LIST: return list_fits ? kGridList : kGridNatural;
     default: break;
   }
+  if (order_fits && p >= kPersistentOrderMin) return kGridSorted;
+  if (list_fits && s.num_seqs <= kListMaxSeqs) return kGridList;
   if (order_fits) return kGridSorted;
   return list_fits ? kGridList : kGridNatural;
 }
 
-int32_t work_list_ints(const DecodeShape& s, int64_t np) {
-  if (grid_mode(s, np) != kGridList) return 0;
+int32_t work_list_ints(const DecodeShape& s, int32_t p) {
+  if (grid_mode(s, p) != kGridList) return 0;
+  const int64_t np = n_partitions(s, p);
   const int64_t ints = pa::work_list_lds_ints(s.num_seqs, (int)np);
   return (int32_t)((ints + 3) & ~3);  // keep the merge area 16-byte aligned
 }
@@ -265,7 +279,7 @@ size_t workspace_bytes_for(const DecodeShape& s, int32_t p) {
   const int64_t np = n_partitions(s, p);
   if (np <= 1) return 0;
   size_t bytes = order_offset(s, np);
-  if (grid_mode(s, np) == kGridSorted)
+  if (grid_mode(s, p) == kGridSorted)
     bytes += round_up((size_t)s.num_seqs * (size_t)np * sizeof(int32_t)) + kAlign;  // + counter
   return bytes;
 }
@@ -482,7 +496,7 @@ int32_t pa_decode_work_list(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
                 kv_dtype, flags};
   int32_t p = 0;
   const int32_t st = plan_args(s, partition_size, q_dtype, &p);
-  return st != PA_OK ? st : (work_list_ints(s, n_partitions(s, p)) > 0 ? 1 : 0);
+  return st != PA_OK ? st : (work_list_ints(s, p) > 0 ? 1 : 0);
 }
 
 int32_t pa_decode_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -493,7 +507,7 @@ int32_t pa_decode_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   int32_t p = 0;
   const int32_t st = plan_args(s, partition_size, q_dtype, &p);
   if (st != PA_OK) return st;
-  switch (grid_mode(s, n_partitions(s, p))) {
+  switch (grid_mode(s, p)) {
     case kGridSorted: return PA_DECODE_SORTED_GRID;
     case kGridList: return PA_DECODE_WORK_LIST;
     default: return PA_DECODE_NO_WORK_LIST;
@@ -596,8 +610,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.out_dtype = out_dtype;
   a.waves = pick_waves(s, p);
   // one grid decision for the workspace and the launch (both on the query rows' shape)
-  const int mode = grid_mode(rows_shape, np);
-  a.list_ints = mode == kGridList ? work_list_ints(rows_shape, np) : 0;
+  const int mode = grid_mode(rows_shape, p);
+  a.list_ints = mode == kGridList ? work_list_ints(rows_shape, p) : 0;
   a.order = mode == kGridSorted
                 ? reinterpret_cast<const int32_t*>(ws + order_offset(rows_shape, np))
                 : nullptr;

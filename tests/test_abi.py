@@ -184,9 +184,11 @@ def test_waves_flags():
     for w, flag in pa.WAVES_FLAG.items():
         assert L.pa_decode_waves(*args, flag) == w
         assert L.pa_decode_waves(*args, flag | pa.FORCE_VALU) == w
-    # library choice: 1, 2 or 4 waves, at least 8 16-token chunks each of a full partition
+    # library choice: 4 waves from 1024-token partitions, 2 from 256, else 1
     assert L.pa_decode_waves(*args, 0) == 4                                     # 1024 tokens
-    assert L.pa_decode_waves(*args[:6], 512, BF16, BF16, 0) == 4
+    assert L.pa_decode_waves(*args[:6], 4096, BF16, BF16, 0) == 4
+    assert L.pa_decode_waves(*args[:6], 1008, BF16, BF16, 0) == 2
+    assert L.pa_decode_waves(*args[:6], 512, BF16, BF16, 0) == 2
     assert L.pa_decode_waves(*args[:6], 256, BF16, BF16, 0) == 2
     assert L.pa_decode_waves(*args[:6], 384, BF16, BF16, 0) == 2
     assert L.pa_decode_waves(*args[:6], 128, BF16, BF16, 0) == 1
@@ -194,10 +196,17 @@ def test_waves_flags():
     assert L.pa_decode_waves(*args, 64) == EUNSUP
     assert L.pa_decode_waves(*args[:6], 24, BF16, BF16, 0) == ESHAPE  # not a block multiple
     assert L.pa_decode_waves(*args[:7], F16, BF16, pa.WAVES_2) == EDTYPE
-    # grid: the sorted grid for every partitioned launch whose order fits
-    # (num_seqs * partitions <= 65536); the persistent work list only on request
+    # grid: the sorted grid for partitions of 1024+ tokens whose order fits
+    # (num_seqs * partitions <= 65536); below 1024 tokens the work list for
+    # batches of up to 64 sequences (where it fits in LDS), else the sorted grid
     G, S, W = pa.NO_WORK_LIST, pa.SORTED_GRID, pa.WORK_LIST
     assert L.pa_decode_grid(*args, 0) == S                                      # 8 of 1024
+    assert L.pa_decode_grid(*args[:6], 512, BF16, BF16, 0) == S                 # 256 sequences
+    assert L.pa_decode_grid(64, 32, 8, 128, 16, 512, 512, BF16, BF16, 0) == W   # 64 sequences
+    assert L.pa_decode_grid(65, 32, 8, 128, 16, 512, 512, BF16, BF16, 0) == S
+    assert L.pa_decode_grid(64, 32, 8, 128, 16, 512, 1024, BF16, BF16, 0) == S
+    assert L.pa_decode_grid(32, 40, 40, 128, 16, 256, 512, F16, F16, 0) == W    # skewed batch
+    assert L.pa_decode_work_list(32, 40, 40, 128, 16, 256, 512, F16, F16, 0) == 1
     assert L.pa_decode_grid(*args[:6], 2048, BF16, BF16, 0) == S                # 4 partitions
     assert L.pa_decode_grid(*args[:6], 8192, BF16, BF16, 0) == G                # one pass
     assert L.pa_decode_grid(*args[:6], 8192, BF16, BF16, W) == G
