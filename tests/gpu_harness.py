@@ -80,6 +80,23 @@ class GpuState:
         return out
 
 
+def assert_rejected(call, out: torch.Tensor, status: int = -4) -> None:
+    """An argument set the library does not serve (by default a kernel family
+    forced onto dtypes or a column count it has no kernel for): the call
+    raises PAError with `status` (-4, PA_ERR_UNSUPPORTED) before launching
+    anything, so `out`, NaN-filled here, keeps its fill."""
+    out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    try:
+        call()
+    except pa.PAError as e:
+        assert e.status == status, f"status {e.status}, expected {status}"
+    else:
+        raise AssertionError("the library accepted an argument set it does not serve")
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all(), "a rejected call wrote to out"
+
+
 def write_kv(cfg, k, v, slots, kc, vc) -> None:
     """The library's cache write for the config's cache dtype."""
     if cfg.kv_dtype == "fp8":

@@ -22,7 +22,8 @@ import oracle
 import pagedattention_kv_cache_amd as pa
 from pagedattention_kv_cache_amd.workloads import (FP8_CONFIGS, Workload, custom_config,
                                                    raw_bits)
-from tests.gpu_harness import GpuState, max_abs_err, oracle_state_empty
+from tests.gpu_harness import (GpuState, assert_rejected, decode_kv, max_abs_err,
+                               oracle_state_empty)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,8 +115,6 @@ SMALL = [
 @pytest.mark.parametrize("waves", [0, 4])
 def test_decode_fp8_parity_small(case, partition, kernel, waves):
     qd, d, bs, hq, hkv, lens = case
-    if kernel == "mfma" and qd != "bf16":
-        pytest.skip("the matrix-core kernel takes E4M3 caches with bfloat16 queries")
     max_ctx = -(-max(lens) // bs) * bs
     p = {"auto": 0, "one-pass": max_ctx, "min": max(bs, 16) * 2}[partition]
     cfg = custom_config(f"d8-{qd}", lens, hq, hkv, d, qd, bs, seed=sum(lens) + d + 7 * bs,
@@ -128,6 +127,12 @@ def test_decode_fp8_parity_small(case, partition, kernel, waves):
     gs.write_step(0)
     st.write_step(0)
     flags = KERNELS[kernel] | (pa.WAVES_FLAG[waves] if waves else 0)
+    if kernel == "mfma" and qd != "bf16":
+        # the matrix-core kernel takes E4M3 caches with bfloat16 queries only
+        out = torch.empty(gs.q[0].shape, dtype=torch.float32, device="cuda")
+        assert_rejected(lambda: decode_kv(cfg, out, gs.q[0], gs.kc, gs.vc, gs.block_tables,
+                                          gs.ctx[0], p, flags=flags), out)
+        return
     out = gs.decode(0, flags=flags)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()

@@ -20,7 +20,8 @@ import oracle
 import pagedattention_kv_cache_amd as pa
 from pagedattention_kv_cache_amd.workloads import (CONFIGS, DTYPE_TORCH, FP8_CONFIGS, Workload,
                                                    custom_config, raw_bits)
-from tests.gpu_harness import GpuState, max_abs_err, oracle_state_empty, rowwise_rel_err
+from tests.gpu_harness import (GpuState, assert_rejected, max_abs_err, oracle_state_empty,
+                               rowwise_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,10 +126,18 @@ MQ_CASES = [
 def test_decode_mq_parity_small(case, partition, kernel, waves):
     dt, d, bs, hq, hkv, lens, Q = case
     cfg = custom_config(f"mq-{dt}", lens, hq, hkv, d, dt, bs, seed=sum(lens) + Q + d)
-    if not _supported(Q, cfg, kernel):
-        pytest.skip(f"no {kernel} kernel holds {Q} query tokens x group {cfg.group}")
     max_ctx = -(-max(lens) // bs) * bs
     p = {"auto": 0, "one-pass": max_ctx, "min": max(bs, 16) * 2}[partition]
+    if not _supported(Q, cfg, kernel):
+        # no kernel of this family holds Q query tokens x the group: refused at the C ABI
+        gs = GpuState(Workload(cfg))
+        q = Workload(cfg).multi_queries(Q).cuda()
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        flags = KERNELS[kernel] | (pa.WAVES_FLAG[waves] if waves else 0)
+        assert_rejected(lambda: pa.decode_mq(out, q, gs.kc, gs.vc, gs.block_tables, gs.ctx[0],
+                                             cfg.attn_scale(), cfg.block_size, p, None, flags,
+                                             *_scales(cfg)), out)
+        return
     wl, gs, st = _states(cfg)
     _say(f"mq decode {dt} d={d} bs={bs} {hq}x{hkv} lens={lens} Q={Q} P={p} {kernel} "
          f"waves={waves}")

@@ -17,7 +17,8 @@ import torch
 import oracle
 import pagedattention_kv_cache_amd as pa
 from pagedattention_kv_cache_amd.workloads import CONFIGS, Workload, custom_config, raw_bits
-from tests.gpu_harness import GpuState, max_abs_err, oracle_state_empty, rowwise_rel_err
+from tests.gpu_harness import (GpuState, assert_rejected, max_abs_err, oracle_state_empty,
+                               rowwise_rel_err)
 from tests.paged_host import OracleState
 
 pytestmark = pytest.mark.gpu
@@ -138,17 +139,28 @@ SMALL = [
 KERNELS = {"auto": pa.AUTO, "valu": pa.FORCE_VALU, "mfma": pa.FORCE_MFMA}
 
 
+def _check_rejected(cfg, partition_size, flags):
+    """A kernel choice the library has no kernel for on these dtypes: the
+    decode call is refused at the C ABI (PA_ERR_UNSUPPORTED), nothing runs."""
+    gs = GpuState(Workload(cfg))
+    out = torch.empty(gs.q[0].shape, dtype=torch.float32, device="cuda")
+    assert_rejected(lambda: pa.decode(out, gs.q[0], gs.kc, gs.vc, gs.block_tables, gs.ctx[0],
+                                      cfg.attn_scale(), cfg.block_size, partition_size,
+                                      flags=flags), out)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1]}-bs{c[2]}-{c[3]}x{c[4]}")
 @pytest.mark.parametrize("partition", [0, "one-pass", "min"])
 @pytest.mark.parametrize("kernel", ["auto", "valu", "mfma"])
 def test_decode_parity_small(case, partition, kernel):
     dtype, d, bs, hq, hkv, lens = case
-    if kernel == "mfma" and dtype == "f32":
-        pytest.skip("the matrix-core kernel serves 16-bit caches only")
     max_ctx = -(-max(lens) // bs) * bs
     p = {0: 0, "one-pass": max_ctx, "min": max(bs, 16) * 2}[partition]
     cfg = custom_config(f"dp-{dtype}", lens, hq, hkv, d, dtype, bs, seed=sum(lens) + d + bs,
                         partition_size=p)
+    if kernel == "mfma" and dtype == "f32":  # the matrix-core kernel serves 16-bit caches only
+        _check_rejected(cfg, p, KERNELS[kernel])
+        return
     wl, gs, st, res = _run_small(cfg, flags=KERNELS[kernel])
     for out, ref in res:
         assert torch.isfinite(out).all()
@@ -162,12 +174,13 @@ def test_decode_parity_small(case, partition, kernel):
 def test_decode_parity_split_waves(case, partition, kernel, waves):
     """Several waves per work item (tokens split between them, merged on chip)."""
     dtype, d, bs, hq, hkv, lens = case
-    if kernel == "mfma" and dtype == "f32":
-        pytest.skip("the matrix-core kernel serves 16-bit caches only")
     max_ctx = -(-max(lens) // bs) * bs
     p = {"one-pass": max_ctx, "min": max(bs, 16) * 2}[partition]
     cfg = custom_config(f"dw-{dtype}", lens, hq, hkv, d, dtype, bs, seed=sum(lens) + d + 5 * bs,
                         partition_size=p)
+    if kernel == "mfma" and dtype == "f32":  # the matrix-core kernel serves 16-bit caches only
+        _check_rejected(cfg, p, KERNELS[kernel] | pa.WAVES_FLAG[waves])
+        return
     wl, gs, st, res = _run_small(cfg, flags=KERNELS[kernel] | pa.WAVES_FLAG[waves])
     for out, ref in res:
         assert torch.isfinite(out).all()
@@ -342,9 +355,10 @@ def _single_token_state(dtype, d, bs, hq, hkv, n_seqs, seed):
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("waves", [1, 4])
 def test_context_length_one_returns_v_bit_exact(dtype, partition, kernel, waves):
-    if kernel == "mfma" and dtype == "f32":
-        pytest.skip("the matrix-core kernel serves 16-bit caches only")
     cfg, wl = _single_token_state(dtype, 128, 16, 8, 2, 6, seed=3)
+    if kernel == "mfma" and dtype == "f32":  # the matrix-core kernel serves 16-bit caches only
+        _check_rejected(cfg, partition, KERNELS[kernel] | pa.WAVES_FLAG[waves])
+        return
     gs = GpuState(wl)
     gs.write_step(0)
     out = gs.decode(0, partition_size=partition, flags=KERNELS[kernel] | pa.WAVES_FLAG[waves])
@@ -360,9 +374,8 @@ def test_context_length_one_returns_v_bit_exact(dtype, partition, kernel, waves)
 @pytest.mark.parametrize("waves", [1, 4])
 def test_one_hot_probe_bit_exact(dtype, partition, kernel, waves):
     """K = 0 except one target token whose key is c*q (scale*c*|q|^2 >= 200):
-    every other weight underflows, so out == V[t*] exactly, for every t*."""
-    if kernel == "mfma" and dtype == "f32":
-        pytest.skip("the matrix-core kernel serves 16-bit caches only")
+    every other weight underflows, so out == V[t*] exactly, for every t*.  The
+    matrix-core kernel on fp32 caches is refused instead (16-bit caches only)."""
     L, d, bs, H = 96, 64, 16, 1
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
     gen = torch.Generator().manual_seed(17)
@@ -384,8 +397,13 @@ def test_one_hot_probe_bit_exact(dtype, partition, kernel, waves):
         vc = torch.full(pa.value_cache_shape(NB, H, d, bs), float("nan"), dtype=dt, device="cuda")
         pa.cache_write(K.cuda(), V.cuda(), slots, kc, vc)
         out = torch.empty(1, 1, d, device="cuda")
-        pa.decode(out, q.cuda(), kc, vc, bt, torch.tensor([L], dtype=torch.int32, device="cuda"),
-                  scale, bs, p, flags=KERNELS[kernel] | pa.WAVES_FLAG[waves])
+        ctx = torch.tensor([L], dtype=torch.int32, device="cuda")
+        flags = KERNELS[kernel] | pa.WAVES_FLAG[waves]
+        if kernel == "mfma" and dtype == "f32":
+            assert_rejected(lambda: pa.decode(out, q.cuda(), kc, vc, bt, ctx, scale, bs, p,
+                                              flags=flags), out)
+            return
+        pa.decode(out, q.cuda(), kc, vc, bt, ctx, scale, bs, p, flags=flags)
         torch.cuda.synchronize()
         assert torch.equal(out[0, 0].cpu(), V[t, 0].float()), f"t*={t}"
 
