@@ -82,8 +82,8 @@ def parse_args(argv=None):
                          "previous one left in the 256 MB Infinity Cache")
     ap.add_argument("--no-stream-probe", action="store_true")
     ap.add_argument("--graph", action="store_true",
-                    help="multi-step workloads: also time the steps captured in HIP graphs, "
-                         "state advanced on the device by pa_advance_step")
+                    help="also time the step(s) captured in HIP graphs (multi-step "
+                         "workloads: state advanced on the device by pa_advance_step)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -227,7 +227,10 @@ def graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags) -> dic
     """The workload's consecutive decode steps (write -> partitions -> merge ->
     device advance step) captured once per KV-cache layer in a HIP graph;
     each timed replay restores the initial per-sequence state first (four
-    small device copies, as a scheduler would upload it) and runs all steps."""
+    small device copies, as a scheduler would upload it) and runs all steps.
+    A one-step workload captures write -> partitions -> merge only and
+    replays it as is, like the eager timed loop: the same step's inputs each
+    time, nothing to restore."""
     import torch
 
     import pagedattention_kv_cache_amd as pa
@@ -238,18 +241,23 @@ def graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags) -> dic
     sampled = torch.from_numpy(wl.sampled_tokens()).to(dev)
     scale = c.attn_scale()
 
+    multi = c.steps > 1
+
     def steps(k_l, v_l):
         for s in range(c.steps):
             write_kv(c, sk[s], sv[s], state["slot_mapping"], k_l, v_l)
             decode_partitions_kv(c, out, qs[s], k_l, v_l, bt, state["seq_lens"], part, ws, flags)
             pa.decode_merge(out, qs[s], k_l, v_l, bt, state["seq_lens"], scale, c.block_size,
                             part, ws, flags)
-            pa.advance_step(c.num_seqs, c.block_size, state["input_tokens"], sampled[s],
-                            state["input_positions"], state["seq_lens"], state["slot_mapping"], bt)
+            if multi:
+                pa.advance_step(c.num_seqs, c.block_size, state["input_tokens"], sampled[s],
+                                state["input_positions"], state["seq_lens"],
+                                state["slot_mapping"], bt)
 
     def reset():
-        for k in state:
-            state[k].copy_(init[k])
+        if multi:
+            for k in state:
+                state[k].copy_(init[k])
 
     graphs = []
     for k_l, v_l in zip(kcs, vcs):
@@ -481,7 +489,7 @@ def run(args):
     achieved = kv / (dec_ms * 1e-3) / 1e9
 
     graph = None
-    if args.graph and c.steps > 1 and Q == 1:
+    if args.graph and Q == 1:
         graph = graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags)
     attainable = None if args.no_stream_probe else stream_probe(dev)
     traffic = None
