@@ -138,3 +138,52 @@ def test_multistep_graph_replays_match_eager_and_oracle(kernel):
         assert torch.equal(gs.vc.view(torch.int16), eager_v.view(torch.int16)), f"replay {rep}"
         for k in state:
             assert torch.equal(state[k], eager_state[k]), f"replay {rep} {k}"
+
+
+@pytest.mark.parametrize("lens_seed,n_seqs,partition", [(5, 6, 256), (6, 80, 256), (7, 40, 1024)])
+def test_one_step_graph_replays_match_eager(lens_seed, n_seqs, partition):
+    """One decode step (cache write, then decode with its partition merge)
+    captured in a HIP graph and replayed three times, with eager work in
+    between: every replay bit-identical to the eager run.  The three cases
+    take the three deals of a partitioned launch: the LDS work list (6
+    sequences, 256-token partitions), the sorted order dealt in fixed rounds
+    (80 sequences, 256) and dealt from the counter (1024)."""
+    rng = np.random.default_rng(lens_seed)
+    lens = rng.integers(1, 3000, size=n_seqs).tolist()
+    cfg = custom_config(f"g1-{n_seqs}-{partition}", lens, 8, 2, 128, "bf16", 16,
+                        seed=70 + lens_seed, partition_size=partition)
+    wl = Workload(cfg)
+    c = cfg
+    gs = GpuState(wl)
+    B, MB = c.num_seqs, wl.max_blocks_per_seq
+    want = {256: pa.WORK_LIST if n_seqs <= 64 else pa.SORTED_GRID, 1024: pa.SORTED_GRID}[partition]
+    assert pa.decode_grid(B, 8, 2, 128, 16, MB, partition, torch.bfloat16, torch.bfloat16,
+                          pa.AUTO) == pa.GRID_NAMES[want]
+    ws_bytes = pa.decode_workspace_size(B, 8, 2, 128, 16, MB, partition, torch.bfloat16, pa.AUTO)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    slots = torch.from_numpy(wl.step_slots(0)).cuda()
+    torch.cuda.synchronize()
+    kc0, vc0 = gs.kc.clone(), gs.vc.clone()
+
+    def step(out):
+        pa.cache_write(gs.step_k[0], gs.step_v[0], slots, gs.kc, gs.vc)
+        pa.decode(out, gs.q[0], gs.kc, gs.vc, gs.block_tables, gs.ctx[0], c.attn_scale(),
+                  c.block_size, partition, ws)
+
+    eager = torch.empty(gs.q[0].shape, device="cuda")
+    step(eager)
+    torch.cuda.synchronize()
+    assert torch.isfinite(eager).all()
+    graph_out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(graph_out)
+    for rep in range(3):
+        gs.kc.copy_(kc0)  # eager work between replays
+        gs.vc.copy_(vc0)
+        graph_out.fill_(float("nan"))
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(graph_out, eager), f"replay {rep}"
