@@ -212,6 +212,12 @@ def cpu_baseline(wl, okc, ovc, threads):
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     kv = wl.kv_bytes(0)
+    # one more repetition on a single thread, for the per-core rate
+    t1 = time.perf_counter()
+    oracle_write(c, raw_bits(sk[0]), raw_bits(sv[0]), slots, okc, ovc)
+    oracle.decode(q, c.dtype, okc, ovc, c.kv_dtype, wl.block_tables, wl.context_lens(0),
+                  c.attn_scale(), threads=1, k_scale=ks, v_scale=vs)
+    t1 = time.perf_counter() - t1
     return {
         "value": kv / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": (f"one full step of {c.name} (write of {c.num_seqs} new tokens + all "
@@ -220,6 +226,7 @@ def cpu_baseline(wl, okc, ovc, threads):
         "seconds_per_step": t,
         "tokens_per_s": c.num_seqs / t,
         "cpu_model": _cpu_model(),
+        "single_thread": {"seconds_per_step": t1, "value": kv / t1 / 1e9, "unit": "GB/s"},
     }
 
 
@@ -474,7 +481,8 @@ def run(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    dec_times = [e[1].elapsed_time(e[2]) for e in evs]
+    dec_ms = statistics.mean(dec_times)
     # Breakdown pass (after the timed region, same steps): events around every launch.
     evs = events()
     for i in range(args.steps):
@@ -531,6 +539,9 @@ def run(args):
         "write_ms": None if fused else round(write_ms, 5),
         "fused_write": fused,
         "decode_partitions_ms": round(dec_ms, 5),
+        "decode_partitions_ms_median_min_max": [round(statistics.median(dec_times), 5),
+                                                round(min(dec_times), 5),
+                                                round(max(dec_times), 5)],
         "decode_merge_ms": round(merge_ms, 5),
         "decode_partitions_ms_breakdown_pass": round(dec_ms_breakdown, 5),
         "roofline": {
