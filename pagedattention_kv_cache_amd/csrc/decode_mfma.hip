@@ -157,18 +157,18 @@ template <> struct Store<Elem::FP8> {
   static __device__ __forceinline__ VRaw load_v(const char* p) {
     return *reinterpret_cast<const VRaw*>(p);
   }
+  // gfx950 widens two E4M3 codes straight to a bfloat16 pair (scale 1: no
+  // scaling); every E4M3 value is exact in bfloat16.
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
   static __device__ __forceinline__ Math::vec8 k(KRaw r) {
-    float f[8];
-    fp8x4_to_f32(r.x, f);
-    fp8x4_to_f32(r.y, f + 4);
-    const uint4 w = {pack_bf16_exact(f[0], f[1]), pack_bf16_exact(f[2], f[3]),
-                     pack_bf16_exact(f[4], f[5]), pack_bf16_exact(f[6], f[7])};
+    const uint4 w = {pair<false>(r.x), pair<true>(r.x), pair<false>(r.y), pair<true>(r.y)};
     return __builtin_bit_cast(Math::vec8, w);
   }
   static __device__ __forceinline__ Math::vec4 v(VRaw r) {
-    float f[4];
-    fp8x4_to_f32(r, f);
-    const uint2 w = {pack_bf16_exact(f[0], f[1]), pack_bf16_exact(f[2], f[3])};
+    const uint2 w = {pair<false>(r), pair<true>(r)};
     return __builtin_bit_cast(Math::vec4, w);
   }
 };
