@@ -226,6 +226,8 @@ def cpu_baseline(wl, okc, ovc, threads):
         "seconds_per_step": t,
         "tokens_per_s": c.num_seqs / t,
         "cpu_model": _cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "host_cpus_usable": len(os.sched_getaffinity(0)),
         "single_thread": {"seconds_per_step": t1, "value": kv / t1 / 1e9, "unit": "GB/s"},
     }
 
@@ -325,13 +327,22 @@ def stream_probe(dev, gib: int = 4, reps: int = 10) -> float:
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, then family / model /
+    stepping (a virtualised host may report only a short model name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            key, _, val = line.partition(":")
+            key = key.strip()
+            if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                fields[key] = val.strip()
+            if not line.strip() and fields:
+                break
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    ident = "/".join(fields.get(k, "?") for k in ("cpu family", "model", "stepping"))
+    return f"{name} (family/model/stepping {ident})"
 
 
 def run(args):

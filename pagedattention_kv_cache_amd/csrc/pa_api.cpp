@@ -101,10 +101,6 @@ int32_t pick_kernel(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t g
   return valu_ok ? PA_DECODE_FORCE_VALU : 0;
 }
 
-bool use_mfma(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t group) {
-  return pick_kernel(flags, kv_dtype, q_dtype, group, 1) == PA_DECODE_FORCE_MFMA;
-}
-
 // Flag bits this library knows, with a valid kernel choice.
 bool valid_flags(uint32_t flags) {
   if (flags & ~(PA_DECODE_KERNEL_MASK | PA_DECODE_WAVES_MASK | PA_DECODE_GRID_MASK))

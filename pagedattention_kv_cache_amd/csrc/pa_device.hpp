@@ -34,13 +34,6 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
   out[3] = hi[1];
 }
 
-// Two fp32 values that are exact in bfloat16 (every E4M3 value is: at most 4
-// significant bits, exponents -9..8), packed as two bfloat16 by keeping each
-// one's upper half.
-__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
 // fp32 -> E4M3, nearest value with ties to the even significand, magnitudes
 // beyond 448 (infinities too) saturating to +-448, NaN to the NaN pattern of
 // its sign.  Integer/exact-float steps only, so the result does not depend on
@@ -218,13 +211,5 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-
-// Wave index inside the workgroup, as a wave-uniform (scalar) value.
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-}
-__device__ __forceinline__ int waves_per_group() { return (int)(blockDim.x >> 6); }
-
-constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace pa

@@ -114,6 +114,14 @@ CONFIGS: dict[int, DecodeConfig] = {
 }
 
 
+def config3_long_first() -> DecodeConfig:
+    """The skewed 13B-shaped batch (number 3) with its 4096-token sequence at
+    batch index 0 instead of the last index; the short sequences' lengths are
+    the same draws."""
+    return dataclasses.replace(CONFIGS[3], name="llama13b-skew-long-first-fp16",
+                               lengths=_skewed(16, 256, 4096, 0))
+
+
 def fp8_variant(cfg: DecodeConfig, k_scale: float, v_scale: float) -> DecodeConfig:
     """The same workload with E4M3 caches: the 16-bit K/V are written with the
     per-tensor scales k_scale, v_scale (powers of two here, so x / scale is

@@ -153,3 +153,18 @@ def rowwise_rel_err(gpu: torch.Tensor, ref: np.ndarray, rows: np.ndarray | None 
     if rows is not None:
         g, r = g[rows], r[rows]
     return float((np.abs(g - r).max(axis=1) / np.abs(r).max(axis=1)).max())
+
+
+def componentwise_rel_err(gpu: torch.Tensor, ref: np.ndarray, ref_abs: np.ndarray,
+                          rows: np.ndarray | None = None) -> float:
+    """max over elements of |gpu - ref| / ref_abs, where ref_abs is the oracle's
+    decode over |V| (the same softmax weights on the values' magnitudes).  An
+    element's rounding error in a weighted sum scales with the sum of the
+    magnitudes, not with the (possibly cancelled) result, so this is the
+    elementwise relative error with the denominator the arithmetic fixes."""
+    g = gpu.float().cpu().numpy().astype(np.float64).reshape(-1, gpu.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    a = ref_abs.reshape(-1, ref_abs.shape[-1])
+    if rows is not None:
+        g, r, a = g[rows], r[rows], a[rows]
+    return float((np.abs(g - r) / np.maximum(a, 1e-300)).max())

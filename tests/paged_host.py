@@ -39,6 +39,12 @@ def poisoned_pool(wl: Workload, transposed: bool) -> np.ndarray:
     return np.full(shape, POISON_BITS[c.kv_dtype], dtype=_BITS_NP[c.kv_dtype])
 
 
+def abs_values(pool: np.ndarray, dtype: str) -> np.ndarray:
+    """A raw-bit pool with every element's sign bit cleared (|x|; NaN stays NaN)."""
+    top = {"f32": 0x80000000, "f16": 0x8000, "bf16": 0x8000, "fp8": 0x80}[dtype]
+    return pool & pool.dtype.type(~top & (2 * top - 1))
+
+
 def oracle_write(cfg, k: np.ndarray, v: np.ndarray, slots: np.ndarray, kc: np.ndarray,
                  vc: np.ndarray) -> None:
     """The oracle's cache write for the config's cache dtype (k, v raw bits)."""
@@ -100,6 +106,17 @@ class OracleState:
         c = self.wl.cfg
         return oracle_decode(c, raw_bits(self.q[step]), self.kc, self.vc, self.wl.block_tables,
                              self.wl.context_lens(step), rows=rows, threads=threads)
+
+    def decode_abs_values(self, step: int, rows: np.ndarray | None = None,
+                          threads: int = 8) -> np.ndarray:
+        """The oracle's decode with every value replaced by its magnitude:
+        sum_t w_t |v_te| / sum_t w_t with the same softmax weights w_t.  Rounding
+        errors of a weighted sum are bounded relative to this sum of magnitudes,
+        so it is the denominator of the componentwise relative error."""
+        c = self.wl.cfg
+        return oracle_decode(c, raw_bits(self.q[step]), self.kc, abs_values(self.vc, c.kv_dtype),
+                             self.wl.block_tables, self.wl.context_lens(step), rows=rows,
+                             threads=threads)
 
 
 def logical_kv(wl: Workload, b: int, step: int) -> tuple[np.ndarray, np.ndarray]:

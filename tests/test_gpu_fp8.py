@@ -222,32 +222,22 @@ def test_decode_fp8_rejected_by_plain_entry_points():
 
 # ------------------------------------------------------------------ full size
 
-def _sample_rows(wl: Workload, n: int, seed: int) -> np.ndarray:
-    c = wl.cfg
-    rng = np.random.default_rng(seed)
-    rows = rng.choice(c.num_seqs * c.num_q_heads, size=min(n, c.num_seqs * c.num_q_heads),
-                      replace=False)
-    longest = int(np.argmax(wl.lens0))
-    rows = np.union1d(rows, longest * c.num_q_heads + np.arange(c.num_q_heads))
-    return rows.astype(np.int64)
-
-
 @pytest.mark.parametrize("cid", [4, 5])
 def test_full_workload_fp8_parity(cid):
-    """The GQA workloads with E4M3 caches at full size, library-picked launch."""
+    """The GQA workloads with E4M3 caches at full size, library-picked launch:
+    every row of every step (8 steps of the long-context workload) against the
+    oracle, and the whole pools bit for bit."""
     cfg = FP8_CONFIGS[cid]
     wl = Workload(cfg)
     _say(f"full fp8 workload {cid} {cfg.name}: {wl.describe()}")
     st = oracle_state_empty(wl)
     gs = GpuState(wl, oracle_state=st)
-    steps = min(cfg.steps, 2)
-    for s in range(steps):
+    for s in range(cfg.steps):
         gs.write_step(s)
         st.write_step(s)
         out = gs.decode(s)
-        rows = None if cid == 4 else _sample_rows(wl, 96, seed=s)
-        err = max_abs_err(out, st.decode(s, rows=rows, threads=16), rows)
-        _say(f"  step {s}: err {err:.3e} rows {'all' if rows is None else len(rows)}")
+        err = max_abs_err(out, st.decode(s, threads=16))
+        _say(f"  step {s}: err {err:.3e} rows all")
         assert err <= TOL_ABS
     torch.cuda.synchronize()
     _pools_equal(gs, st)
