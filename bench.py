@@ -84,6 +84,11 @@ def parse_args(argv=None):
     ap.add_argument("--graph", action="store_true",
                     help="also time the step(s) captured in HIP graphs (multi-step "
                          "workloads: state advanced on the device by pa_advance_step)")
+    ap.add_argument("--one-pass-ratio", action="store_true",
+                    help="also time the whole decode (partitions + merge) of the same steps in "
+                         "one pass per (sequence, kv head) -- the partition as long as the "
+                         "longest context -- against the partitioned launch, interleaved, and "
+                         "report the ratio")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -292,6 +297,56 @@ def graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags) -> dic
     return {"steps_per_graph": c.steps, "replays": reps, "ms_per_step": round(ms_step, 5),
             "value": round(kv / (ms_step * 1e-3) / 1e9, 2),
             "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1)}
+
+
+def one_pass_ratio(args, wl, kcs, vcs, qs, bt, ctx, out, ws, part_eff, flags) -> dict:
+    """Whole decode (partitions + merge) per step, one pass per (sequence, kv
+    head) against the partitioned launch: the first is one workgroup per
+    (sequence, kv head) walking its whole context, the second the workload's
+    partitions.  Rounds alternate between the two, each round timing every
+    step of the rotation with HIP events on the launch stream."""
+    import torch
+
+    import pagedattention_kv_cache_amd as pa
+    c = wl.cfg
+    full = wl.max_blocks_per_seq * c.block_size
+    stream = torch.cuda.current_stream()
+    n_layers = len(kcs)
+
+    def decode(i, p):
+        s = (i // n_layers) % c.steps
+        k_l, v_l = kcs[i % n_layers], vcs[i % n_layers]
+        decode_partitions_kv(c, out, qs[s], k_l, v_l, bt, ctx[s], p, ws, flags)
+        pa.decode_merge(out, qs[s], k_l, v_l, bt, ctx[s], c.attn_scale(), c.block_size, p, ws,
+                        flags)
+
+    times = {full: [], part_eff: []}
+    for rnd in range(4):
+        for p in ((full, part_eff) if rnd % 2 == 0 else (part_eff, full)):
+            for i in range(2):
+                decode(i, p)  # warm-up of this launch shape
+            for i in range(args.steps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                decode(i, p)
+                e1.record(stream)
+                times[p].append((e0, e1))
+    torch.cuda.synchronize()
+    ms = {p: statistics.median(a.elapsed_time(b) for a, b in ev) for p, ev in times.items()}
+    waves = {p: pa.decode_waves(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                c.block_size, wl.max_blocks_per_seq, p, qs.dtype, kcs[0].dtype,
+                                flags) for p in (full, part_eff)}
+    return {
+        "one_pass_us": round(ms[full] * 1e3, 2),
+        "one_pass_partition_tokens": int(full),
+        "one_pass_waves_per_item": int(waves[full]),
+        "partitioned_us": round(ms[part_eff] * 1e3, 2),
+        "partition_tokens": int(part_eff),
+        "partitioned_waves_per_item": int(waves[part_eff]),
+        "speedup": round(ms[full] / ms[part_eff], 3),
+        "timing": f"median over 4 alternating rounds of {args.steps} steps, decode + merge",
+    }
 
 
 def stream_probe(dev, gib: int = 4, reps: int = 10) -> float:
@@ -510,6 +565,9 @@ def run(args):
     graph = None
     if args.graph and Q == 1:
         graph = graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags)
+    ratio = None
+    if args.one_pass_ratio and Q == 1:
+        ratio = one_pass_ratio(args, wl, kcs, vcs, qs, bt, ctx, out, ws, int(p_eff), flags)
     attainable = None if args.no_stream_probe else stream_probe(dev)
     traffic = None
     tf = TRAFFIC_FILE.format(workload=c.name)
@@ -570,6 +628,8 @@ def run(args):
     }
     if graph:
         result["graph"] = graph
+    if ratio:
+        result["one_pass_vs_partitioned"] = ratio
     if attainable:
         result["attainable_read_gbps"] = round(attainable, 1)
         result["roofline"]["frac_of_attainable"] = round(achieved / attainable, 4)

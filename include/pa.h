@@ -446,6 +446,40 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t partition_size, int32_t kv_dtype, uint32_t flags);
 
+/*
+ * pa_check_tables / pa_check_slots -- opt-in debug checks of the ids the hot
+ * path takes on trust ("[core] Multi Step Scheduling" pull request: the
+ * per-step slot_mapping and block_tables are the scheduler's, and a broken
+ * one surfaced there only as a failed assertion after the merge).  The
+ * decode and write kernels never read or write out of bounds: a block-table
+ * entry of a context outside [0, num_blocks) is clamped into the pool, a
+ * context length beyond max_blocks_per_seq * block_size is cut to it (a
+ * negative one is an empty sequence), and a slot >= num_blocks * block_size
+ * is dropped.  Such a call returns a wrong answer silently.  These checks
+ * evaluate exactly those conditions on the device and OR one bit per kind
+ * into *status:
+ *   PA_CHECK_CONTEXT_LEN  some context_lens[b] < 0 or > max_blocks_per_seq *
+ *                         block_size
+ *   PA_CHECK_BLOCK_ID     some block_tables[b][j], j < ceil(L_b / block_size)
+ *                         (L_b as the kernels cut it), outside [0, num_blocks)
+ *   PA_CHECK_SLOT         some slot_mapping[i] >= num_blocks * block_size
+ * Entries past a context and negative slots (padding) are not errors.
+ * Clean arguments leave *status unchanged; the caller zeroes it before and
+ * reads it after (both on `stream`).  Nothing is allocated.
+ *   block_tables, context_lens, slot_mapping: device, as in pa_decode /
+ *   pa_cache_write; status: device uint32, 4-byte aligned.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, block_size < 1);
+ * num_seqs == 0 or num_tokens == 0 is a valid no-op.
+ */
+#define PA_CHECK_CONTEXT_LEN 1u
+#define PA_CHECK_BLOCK_ID 2u
+#define PA_CHECK_SLOT 4u
+int pa_check_tables(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks,
+                    uint32_t* status, void* stream);
+int pa_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                   int32_t block_size, uint32_t* status, void* stream);
+
 /* Static, library-owned text for a pa_status value. */
 const char* pa_status_string(int32_t status);
 

@@ -107,6 +107,10 @@ def lib() -> ctypes.CDLL:
         for name in ("pa_decode_mq", "pa_decode_mq_partitions", "pa_decode_mq_merge"):
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name).argtypes = decmq_args
+        L.pa_check_tables.restype = ctypes.c_int
+        L.pa_check_tables.argtypes = [vp, vp, i32, i32, i32, i64, vp, vp]
+        L.pa_check_slots.restype = ctypes.c_int
+        L.pa_check_slots.argtypes = [vp, i64, i64, i32, vp, vp]
         step_args = [vp, vp, vp, i64, i64, i64] + dec_args
         for name in ("pa_decode_step", "pa_decode_step_partitions"):
             getattr(L, name).restype = ctypes.c_int
@@ -139,7 +143,9 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def _declare_blocks(L) -> None:
+def _declare_blocks(L, host_only: bool = False) -> None:
+    """Argument types of the block-manager calls (host_only: only the pa_bm_*
+    ones, for a library built from the host block manager alone)."""
     vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     sigs = {
         "pa_bm_create": [i64, i32, i64, u32, vp],
@@ -160,6 +166,8 @@ def _declare_blocks(L) -> None:
         "pa_swap_blocks": [vp, vp, vp, i32, i64, vp],
     }
     for name, args in sigs.items():
+        if host_only and not name.startswith("pa_bm_"):
+            continue
         getattr(L, name).restype = ctypes.c_int
         getattr(L, name).argtypes = args
     L.pa_bm_destroy.restype = None
@@ -351,6 +359,38 @@ def decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     Allocates the workspace with torch when none (or too small a one) is given."""
     _decode_call("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, scale,
                  block_size, partition_size, workspace, flags)
+
+
+# bits of the status word pa_check_tables / pa_check_slots set
+CHECK_CONTEXT_LEN, CHECK_BLOCK_ID, CHECK_SLOT = 1, 2, 4
+
+
+def check_tables(block_tables: torch.Tensor, context_lens: torch.Tensor, num_blocks: int,
+                 block_size: int, status: torch.Tensor) -> None:
+    """OR CHECK_CONTEXT_LEN / CHECK_BLOCK_ID into status (a device int32 [1])
+    where decode would cut a context length or clamp a block id."""
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.is_contiguous(), "block_tables must be contiguous int32 [B][MB]")
+    B, MB = block_tables.shape
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
+             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
+    _require(status.dtype == torch.int32 and status.numel() == 1 and status.is_cuda,
+             "status must be a device int32 [1]")
+    _check(lib().pa_check_tables(block_tables.data_ptr(), context_lens.data_ptr(), B, MB,
+                                 block_size, num_blocks, status.data_ptr(),
+                                 _stream(status.device)))
+
+
+def check_slots(slot_mapping: torch.Tensor, num_blocks: int, block_size: int,
+                status: torch.Tensor) -> None:
+    """OR CHECK_SLOT into status (a device int32 [1]) where cache_write would
+    drop a slot past the pool."""
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1
+             and slot_mapping.is_contiguous(), "slot_mapping must be contiguous int64 [T]")
+    _require(status.dtype == torch.int32 and status.numel() == 1 and status.is_cuda,
+             "status must be a device int32 [1]")
+    _check(lib().pa_check_slots(slot_mapping.data_ptr(), slot_mapping.shape[0], num_blocks,
+                                block_size, status.data_ptr(), _stream(status.device)))
 
 
 def decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,

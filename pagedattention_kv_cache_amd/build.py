@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pa_api.cpp", "cache_write.hip", "decode_valu.hip", "decode_mfma.hip",
            "decode_reduce.hip", "decode_order.hip", "advance_step.hip", "copy_blocks.hip",
-           "block_manager.cpp"]
+           "check_ids.hip", "block_manager.cpp"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -427,6 +427,35 @@ int pa_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
   return pa::launch_advance_step(a, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int pa_check_tables(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks,
+                    uint32_t* status, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size < 1 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if ((int64_t)num_seqs * max_blocks_per_seq > ((int64_t)1 << 38)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !context_lens || !status) return PA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(status) & 3u) return PA_ERR_SHAPE;
+  return pa::launch_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                 block_size, num_blocks, status,
+                                 (hipStream_t)stream) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                   int32_t block_size, uint32_t* status, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || block_size < 1) return PA_ERR_SHAPE;
+  if (num_tokens > ((int64_t)1 << 38)) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !status) return PA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(status) & 3u) return PA_ERR_SHAPE;
+  return pa::launch_check_slots(slot_mapping, num_tokens, num_blocks * (int64_t)block_size,
+                                status, (hipStream_t)stream) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size,
                                  int32_t max_blocks_per_seq, int32_t kv_dtype, uint32_t flags) {
@@ -735,6 +764,7 @@ int pa_decode_fp8_partitions(PA_DECODE_FP8_PARAMS) {
 }
 
 }  // extern "C"
+
 
 namespace pa {
 

@@ -124,4 +124,11 @@ struct AdvanceArgs {
 // One thread per sequence: next token, position, length and slot.
 hipError_t launch_advance_step(const AdvanceArgs& a, hipStream_t s);
 
+// The precondition checks (check_ids.hip): OR PA_CHECK_* bits into *status.
+hipError_t launch_check_tables(const int32_t* block_tables, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                               int64_t num_blocks, uint32_t* status, hipStream_t s);
+hipError_t launch_check_slots(const int64_t* slots, int64_t num_tokens, int64_t capacity,
+                              uint32_t* status, hipStream_t s);
+
 }  // namespace pa

@@ -164,6 +164,34 @@ def test_decode_empty_batch_is_noop():
     assert _dec(B=0, out=None, q=None, bt=None, cl=None) == OK
 
 
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, -1, 4, 16, 10, FAKE), ESHAPE),
+    ((FAKE, FAKE, 4, 0, 16, 10, FAKE), ESHAPE),
+    ((FAKE, FAKE, 4, 4, 0, 10, FAKE), ESHAPE),
+    ((FAKE, FAKE, 4, 4, 16, 0, FAKE), ESHAPE),
+    ((None, FAKE, 4, 4, 16, 10, FAKE), ENULL),
+    ((FAKE, None, 4, 4, 16, 10, FAKE), ENULL),
+    ((FAKE, FAKE, 4, 4, 16, 10, None), ENULL),
+    ((FAKE, FAKE, 4, 4, 16, 10, FAKE + 2), ESHAPE),   # status word misaligned
+    ((None, None, 0, 4, 16, 10, None), OK),            # empty batch: nothing to check
+])
+def test_check_tables_validation(args, status):
+    assert pa.lib().pa_check_tables(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, -1, 10, 16, FAKE), ESHAPE),
+    ((FAKE, 4, 0, 16, FAKE), ESHAPE),
+    ((FAKE, 4, 10, 0, FAKE), ESHAPE),
+    ((None, 4, 10, 16, FAKE), ENULL),
+    ((FAKE, 4, 10, 16, None), ENULL),
+    ((FAKE, 4, 10, 16, FAKE + 1), ESHAPE),
+    ((None, 0, 10, 16, None), OK),
+])
+def test_check_slots_validation(args, status):
+    assert pa.lib().pa_check_slots(*args, None) == status
+
+
 def test_kernel_family_policy():
     L = pa.lib()
     assert L.pa_decode_kernel(32, 8, BF16, BF16, 0) == pa.FORCE_MFMA   # GQA group of 4
