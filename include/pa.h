@@ -25,7 +25,8 @@
  *   - All tensor arguments are DEVICE pointers to densely packed row-major
  *     arrays unless a stride argument says otherwise.  The caller owns every
  *     buffer; the library allocates no device memory and keeps no state
- *     between calls.  Calls from several host threads are safe.
+ *     between calls (one exception: pa_decode_noalloc's static scratch array,
+ *     below).  Calls from several host threads are safe.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
  *     enqueued: PA_OK means "validated and launched", nothing is waited for,
  *     and no device->host copy is made (grids are sized from the maximum
@@ -76,7 +77,8 @@ typedef enum pa_status {
   PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
   PA_ERR_HIP = -6,         /* a HIP launch failed */
   PA_ERR_CAPACITY = -7,    /* block manager: not enough free blocks (nothing changed) */
-  PA_ERR_SEQUENCE = -8     /* block manager: unknown, duplicate or swapped-out sequence */
+  PA_ERR_SEQUENCE = -8,    /* block manager: unknown, duplicate or swapped-out sequence */
+  PA_ERR_SCRATCH = -9      /* pa_decode_noalloc: the workspace would exceed PA_SCRATCH_BYTES */
 } pa_status;
 
 /* pa_decode flags.  Bits 0-1: which decode kernel family to use. */
@@ -479,6 +481,34 @@ int pa_check_tables(const int32_t* block_tables, const int32_t* context_lens, in
                     uint32_t* status, void* stream);
 int pa_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
                    int32_t block_size, uint32_t* status, void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, results and kernels as pa_decode with
+ * flags, minus the workspace, which is instead a static device array of
+ * PA_SCRATCH_BYTES inside the library.  Nothing is allocated by the call (no
+ * hipMalloc, no allocating library routine); each GPU the library runs on
+ * holds its own copy of the array until the process ends (its address is
+ * looked up once per device, on the first call made with that device
+ * current).  Contents left by an earlier call do not matter: what must start
+ * at zero is cleared by the call's own kernels.
+ *   Limit: pa_decode_workspace_size(...) for the same arguments must be at
+ *   most PA_SCRATCH_BYTES, else PA_ERR_SCRATCH and nothing is launched (one
+ *   pass needs no workspace and is always accepted).
+ *   Races: every call on a GPU shares that GPU's array, so two calls that may
+ *   run at the same time on one GPU (different streams, or host threads) race
+ *   on it; serialise them (one stream) or use pa_decode with workspaces of
+ *   their own.
+ * E4M3 caches: PA_ERR_DTYPE (as pa_decode).
+ */
+#define PA_SCRATCH_BYTES (32u << 20) /* 32 MiB */
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t partition_size, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
+                      int32_t kv_dtype, int32_t out_dtype, uint32_t flags, void* stream);
 
 /* Static, library-owned text for a pa_status value. */
 const char* pa_status_string(int32_t status);

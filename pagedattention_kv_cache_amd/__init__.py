@@ -111,6 +111,8 @@ def lib() -> ctypes.CDLL:
         L.pa_check_tables.argtypes = [vp, vp, i32, i32, i32, i64, vp, vp]
         L.pa_check_slots.restype = ctypes.c_int
         L.pa_check_slots.argtypes = [vp, i64, i64, i32, vp, vp]
+        L.pa_decode_noalloc.restype = ctypes.c_int
+        L.pa_decode_noalloc.argtypes = dec_args[:18] + [u32, vp]
         step_args = [vp, vp, vp, i64, i64, i64] + dec_args
         for name in ("pa_decode_step", "pa_decode_step_partitions"):
             getattr(L, name).restype = ctypes.c_int
@@ -391,6 +393,36 @@ def check_slots(slot_mapping: torch.Tensor, num_blocks: int, block_size: int,
              "status must be a device int32 [1]")
     _check(lib().pa_check_slots(slot_mapping.data_ptr(), slot_mapping.shape[0], num_blocks,
                                 block_size, status.data_ptr(), _stream(status.device)))
+
+
+# bytes of the library's static scratch behind decode_noalloc (PA_SCRATCH_BYTES)
+SCRATCH_BYTES = 32 << 20
+
+
+def decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, scale: float, block_size: int,
+                   partition_size: int = 0, flags: int = AUTO) -> None:
+    """decode() with the library's static device scratch as its workspace:
+    nothing is allocated, by the library or here (for callers that cannot
+    allocate).  Raises PAError -9 when the workspace decode() would need
+    exceeds SCRATCH_BYTES.  Calls that overlap on one GPU share the scratch
+    and race."""
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
+    B, Hq, d = q.shape
+    _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
+    NB, Hkv, bs, d2 = _cache_dims(k_cache, v_cache)
+    _require(bs == block_size and d2 == d, "cache shapes do not match block_size / head_dim")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(),
+             "block_tables must be contiguous int32 [B][max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
+             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
+    _check(lib().pa_decode_noalloc(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), block_size,
+        partition_size, B, Hq, Hkv, d, NB, block_tables.shape[1], _dt(q), _dt(k_cache), _dt(out),
+        flags, _stream(q.device)))
 
 
 def decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,

@@ -298,6 +298,8 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_HIP: return "a HIP kernel launch failed";
     case PA_ERR_CAPACITY: return "not enough free KV blocks (nothing was changed)";
     case PA_ERR_SEQUENCE: return "unknown, duplicate or swapped-out sequence id";
+    case PA_ERR_SCRATCH:
+      return "the decode needs more than the library's static scratch (PA_SCRATCH_BYTES)";
     default: return "unknown pa_status";
   }
 }
@@ -551,6 +553,38 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
 
 }  // extern "C"
 
+// ---- pa_decode_noalloc: the partition workspace in a static device array ----
+namespace {
+
+// The library's own partition workspace for pa_decode_noalloc: a file-scope
+// device array, one copy per GPU for the life of the process.  Host code never
+// passes `scratch` itself to a kernel (on the host it is only a stand-in for
+// the symbol): its device address is looked up once per device and kept.
+constexpr size_t kScratchBytes = PA_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+// The device address of the current device's scratch (looked up on the first
+// call on that device, with that device current), or NULL on failure.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> g(scratch_mu);
+  p = scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+  scratch_ptr[dev].store(addr, std::memory_order_release);
+  return addr;
+}
+
+}  // namespace
+
 namespace {
 
 enum Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
@@ -562,7 +596,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream, int phase,
                 float k_scale = 1.0f, float v_scale = 1.0f, int32_t num_queries = 1,
-                const pa::CacheWriteArgs* pre_write = nullptr) {
+                const pa::CacheWriteArgs* pre_write = nullptr, bool use_scratch = false) {
   DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                 kv_dtype, flags};
   int st = check_shape(s);
@@ -599,6 +633,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (p > max_ctx) p = (int32_t)max_ctx;
   const int64_t np = n_partitions(s, p);
   const size_t need = workspace_bytes_for(rows_shape, p);
+  if (use_scratch && need > 0) {  // pa_decode_noalloc: the library's static array
+    if (need > kScratchBytes) return PA_ERR_SCRATCH;
+    if (!(workspace = device_scratch())) return PA_ERR_HIP;
+    workspace_bytes = kScratchBytes;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
   if (np > 65535 || (int64_t)num_seqs * num_queries * num_q_heads > 0x7fffffffLL)
@@ -692,6 +731,21 @@ int pa_decode_partitions(PA_DECODE_PARAMS) {
   return decode_impl(PA_DECODE_ARGS, kPartitions);
 }
 int pa_decode_merge(PA_DECODE_PARAMS) { return decode_impl(PA_DECODE_ARGS, kMerge); }
+
+// pa_decode with the static scratch as its workspace; every argument is
+// validated (and the scratch's limit checked) before the scratch is looked up.
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t partition_size, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
+                      int32_t kv_dtype, int32_t out_dtype, uint32_t flags, void* stream) {
+  if (kv_dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_DTYPE;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                     partition_size, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, q_dtype, kv_dtype, out_dtype, nullptr, 0, flags, stream,
+                     kBoth, 1.0f, 1.0f, 1, nullptr, true);
+}
 
 #define PA_STEP_PARAMS                                                                         \
   const void *k, const void *v, const int64_t *slot_mapping, int64_t num_tokens,              \

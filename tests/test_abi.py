@@ -21,7 +21,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
 
 OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
-ECAP, ESEQ = -7, -8
+ECAP, ESEQ, ESCRATCH = -7, -8, -9
 F32, F16, BF16 = 0, 1, 2
 FAKE = 0x10000  # a 16-byte aligned non-null value; never dereferenced
 
@@ -77,7 +77,7 @@ def test_status_strings_and_version():
     fallback = pa.status_string(-99)
     assert fallback == "unknown pa_status"
     texts = [pa.status_string(st)
-             for st in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ECAP, ESEQ)]
+             for st in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ECAP, ESEQ, ESCRATCH)]
     assert all(t and t != fallback for t in texts)
     assert len(set(texts)) == len(texts)
 
@@ -162,6 +162,55 @@ def test_decode_validation(kw, status):
 
 def test_decode_empty_batch_is_noop():
     assert _dec(B=0, out=None, q=None, bt=None, cl=None) == OK
+
+
+def _dec_noalloc(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, bs=16, P=0, B=4,
+             Hq=32, Hkv=8, d=128, NB=100, MB=64, qd=BF16, kvd=BF16, od=F32, flags=pa.FORCE_VALU)
+    a.update(kw)
+    return pa.lib().pa_decode_noalloc(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"],
+                                      a["scale"], a["bs"], a["P"], a["B"], a["Hq"], a["Hkv"],
+                                      a["d"], a["NB"], a["MB"], a["qd"], a["kvd"], a["od"],
+                                      a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ESHAPE),
+    (dict(Hq=30), ESHAPE),
+    (dict(d=96), EUNSUP),
+    (dict(kvd=3), EDTYPE),                 # E4M3 caches: not through this entry point
+    (dict(qd=F16), EDTYPE),
+    (dict(out=None), ENULL),
+    (dict(P=24), ESHAPE),
+    (dict(flags=64), EUNSUP),
+    # 2048 x 32 rows x 32 partitions of 256 tokens: a workspace of ~1 GB
+    (dict(B=2048, MB=512, P=256), ESCRATCH),
+])
+def test_decode_noalloc_validation(kw, status):
+    """Every argument is validated, and the scratch limit checked, before the
+    static scratch is looked up or anything launched."""
+    assert _dec_noalloc(**kw) == status
+
+
+def test_decode_noalloc_empty_batch_is_noop():
+    assert _dec_noalloc(B=0, out=None, q=None, bt=None, cl=None) == OK
+
+
+def test_decode_noalloc_scratch_covers_the_full_size_workloads():
+    """PA_SCRATCH_BYTES (32 MiB) holds the partition workspace of every
+    full-size decode workload in the launch configuration the benchmark uses."""
+    from pagedattention_kv_cache_amd.workloads import CONFIGS, DTYPE_TORCH, Workload
+    for cid, cfg in CONFIGS.items():
+        wl = Workload(cfg)
+        need = pa.decode_workspace_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
+                                        cfg.head_dim, cfg.block_size, wl.max_blocks_per_seq,
+                                        cfg.partition_size, DTYPE_TORCH[cfg.kv_dtype], pa.AUTO)
+        assert need <= pa.SCRATCH_BYTES, (cid, need)
+
+
+def test_scratch_size_matches_the_header():
+    m = re.search(r"#define PA_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.SCRATCH_BYTES
 
 
 @pytest.mark.parametrize("args,status", [
