@@ -107,6 +107,10 @@ template <Elem KV> struct Store16 {  // f16 / bf16: loaded as the multiply type
   static constexpr int EB = 2;
   static constexpr int kstep = 256;  // bytes between k-chunks (4 key chunks of a quad row)
   static constexpr int vstep = 128;  // bytes between 16-dim value row chunks
+  // one value load per 16-dim row chunk: row chunk rc of lane (n, j) is dim 16 rc + n
+  static constexpr bool kPairDims = false;
+  static constexpr int vloads(int D) { return D / 16; }
+  static __device__ __forceinline__ int dim(int rc, int j, int r) { return 16 * rc + 4 * j + r; }
   // offsets from the chunk's first token quad
   static __device__ __forceinline__ int koff(int n, int j, int D) {
     return ((n >> 2) * (D / 8) + j) * 64 + (n & 3) * 16;
@@ -126,30 +130,40 @@ template <Elem KV> struct Store16 {  // f16 / bf16: loaded as the multiply type
     return *reinterpret_cast<const VRaw*>(p);
   }
   static __device__ __forceinline__ typename Math::vec8 k(KRaw r) { return r; }
-  static __device__ __forceinline__ typename Math::vec4 v(VRaw r) { return r; }
+  static __device__ __forceinline__ typename Math::vec4 v(VRaw r, int) { return r; }
 };
 template <> struct Store<Elem::BF16> : Store16<Elem::BF16> {};
 template <> struct Store<Elem::F16> : Store16<Elem::F16> {};
 // E4M3: half the bytes per operand; widened exactly to bfloat16 (the queries
 // are bfloat16) before the matrix cores see them.  A key chunk of 16 bytes
 // holds 16 dims, so k-chunk c of lane group j is half (j & 1) of key chunk
-// 2c + j/2.
+// 2c + j/2.  Values: one 8-byte load per lane covers two adjacent dims (2n,
+// 2n + 1 of a 32-dim group) of its token quad, so the 16 lanes of a quad read
+// one whole 128-byte line; the two dims feed two P.V products (row chunks 2c
+// and 2c + 1), whose output rows are then the even and odd dims.
 template <> struct Store<Elem::FP8> {
   using Math = Mma<Elem::BF16>;
   using KRaw = uint2;
-  using VRaw = uint32_t;
+  using VRaw = uint2;
   static constexpr int EB = 1;
   static constexpr int kstep = 128;
-  static constexpr int vstep = 64;
+  static constexpr int vstep = 128;  // bytes between 32-dim value groups
+  static constexpr bool kPairDims = true;
+  static constexpr int vloads(int D) { return D / 32; }
+  // row chunk rc = 2c + h holds dims 32c + 2n + h; output row 4j + r of it is
+  // dim 32c + 8j + 2r + h
+  static __device__ __forceinline__ int dim(int rc, int j, int r) {
+    return 32 * (rc >> 1) + 8 * j + 2 * r + (rc & 1);
+  }
   static __device__ __forceinline__ int koff(int n, int j, int D) {
     return ((n >> 2) * (D / 16) + (j >> 1)) * 64 + (n & 3) * 16 + (j & 1) * 8;
   }
-  static __device__ __forceinline__ int voff(int n, int j, int D) { return (j * D + n) * 4; }
+  static __device__ __forceinline__ int voff(int n, int j, int D) { return (j * D + 2 * n) * 4; }
   static __device__ __forceinline__ KRaw load_k(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(KRaw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
   }
   static __device__ __forceinline__ VRaw load_v(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return __builtin_bit_cast(VRaw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
   }
   static __device__ __forceinline__ KRaw load_k(const char* p) {
     return *reinterpret_cast<const KRaw*>(p);
@@ -167,8 +181,10 @@ template <> struct Store<Elem::FP8> {
     const uint4 w = {pair<false>(r.x), pair<true>(r.x), pair<false>(r.y), pair<true>(r.y)};
     return __builtin_bit_cast(Math::vec8, w);
   }
-  static __device__ __forceinline__ Math::vec4 v(VRaw r) {
-    const uint2 w = {pair<false>(r), pair<true>(r)};
+  // the four tokens of dim 2n (h = 0) or 2n + 1 (h = 1)
+  static __device__ __forceinline__ Math::vec4 v(VRaw r, int h) {
+    const uint32_t x = h ? r.y : r.x;
+    const uint2 w = {pair<false>(x), pair<true>(x)};
     return __builtin_bit_cast(Math::vec4, w);
   }
 };
@@ -176,7 +192,7 @@ template <> struct Store<Elem::FP8> {
 template <Elem KV, int D>
 struct Buffers {
   typename Store<KV>::KRaw k[D / 32];  // key row pieces of this lane's token
-  typename Store<KV>::VRaw v[D / 16];  // 4-token value runs, one per 16-dim row chunk
+  typename Store<KV>::VRaw v[Store<KV>::vloads(D)];  // 4-token value runs of the row chunks
 };
 
 // UB: every 16-token chunk lies in one cache block (block_size >= 16), so the
@@ -192,6 +208,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
   using scalar = typename M::scalar;
   constexpr int KC = D / 32;  // QK^T k-chunks
   constexpr int VC = D / 16;  // P.V row chunks
+  constexpr int VL = St::vloads(D);  // value loads per chunk
   constexpr int NT = (G + 15) / 16;  // 16-column tiles: every key and value load feeds all
 
 
@@ -339,10 +356,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         const int range = none ? 0 : 0x7fffffff;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + first_quad, range);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + first_quad, range);
+        // opaque copies of the lane offsets: the per-chunk constants then fold
+        // into the loads' immediate offsets instead of being hoisted out of
+        // the loop into one register per load (12 VGPRs at head_dim 128)
+        int ko = koff, vo = voff;
+        asm volatile("" : "+v"(ko), "+v"(vo));
 #pragma unroll
-        for (int c = 0; c < KC; ++c) buf.k[c] = St::load_k(rk, koff + St::kstep * c);
+        for (int c = 0; c < KC; ++c) buf.k[c] = St::load_k(rk, ko + St::kstep * c);
 #pragma unroll
-        for (int c = 0; c < VC; ++c) buf.v[c] = St::load_v(rv, voff + St::vstep * c);
+        for (int c = 0; c < VL; ++c) buf.v[c] = St::load_v(rv, vo + St::vstep * c);
       } else {
         const int tk = t0 + n;      // this lane's key token
         const int tv = t0 + 4 * j;  // first token of this lane's value quad
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
 #pragma unroll
         for (int c = 0; c < KC; ++c) buf.k[c] = St::load_k(kp + St::kstep * c);
 #pragma unroll
-        for (int c = 0; c < VC; ++c) buf.v[c] = St::load_v(vp + St::vstep * c);
+        for (int c = 0; c < VL; ++c) buf.v[c] = St::load_v(vp + St::vstep * c);
       }
     };
 
@@ -366,6 +388,29 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int c = 0; c < VC; ++c) o[t][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // this lane's accumulators of tile t, times sc, into the D floats at base
+    // (16-byte aligned): dim St::dim(c, j, r) holds o[t][c][r]
+    auto store_acc = [&](float* base, int t, float sc) {
+      if constexpr (!St::kPairDims) {
+#pragma unroll
+        for (int c = 0; c < VC; ++c) {
+          f32x4_t x = o[t][c];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] *= sc;
+          *reinterpret_cast<f32x4_t*>(base + 16 * c + 4 * j) = x;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < VC / 2; ++c) {
+          const f32x4_t& e = o[t][2 * c];
+          const f32x4_t& f = o[t][2 * c + 1];
+          const f32x4_t lo = {e[0] * sc, f[0] * sc, e[1] * sc, f[1] * sc};
+          const f32x4_t hi = {e[2] * sc, f[2] * sc, e[3] * sc, f[3] * sc};
+          *reinterpret_cast<f32x4_t*>(base + 32 * c + 8 * j) = lo;
+          *reinterpret_cast<f32x4_t*>(base + 32 * c + 8 * j + 4) = hi;
+        }
+      }
+    };
     float m[NT];     // running max of column 16t + n (log2 domain), uniform over j
     float lsum[NT];  // this lane's share of that column's sum
 #pragma unroll
@@ -377,7 +422,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     auto compute = [&](Buffers<KV, D>& buf, int t0, int t_stop) {
       vec4 vv[VC];
 #pragma unroll
-      for (int c = 0; c < VC; ++c) vv[c] = St::v(buf.v[c]);
+      for (int c = 0; c < VC; ++c) vv[c] = St::v(buf.v[St::kPairDims ? c >> 1 : c], c & 1);
       // uniform: the chunk reaches the context end, the partition end or a query's limit
       const bool edge = t0 + kChunk > min(t_stop, lim_lo);
       if (edge) {
@@ -498,16 +543,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         float M = -INFINITY;
         for (int w = 0; w < W; ++w) M = fmaxf(M, red_m[w * CW + 16 * t + n]);
         const float sc = fast_exp2(m[t] - (M == -INFINITY ? 0.0f : M));
-        if (16 * t + n < G) {
-#pragma unroll
-          for (int c = 0; c < VC; ++c) {
-            f32x4_t x = o[t][c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] *= sc;
-            *reinterpret_cast<f32x4_t*>(red_o + (wave * G + 16 * t + n) * RS + 16 * c + 4 * j) =
-                x;
-          }
-        }
+        if (16 * t + n < G) store_acc(red_o + (wave * G + 16 * t + n) * RS, t, sc);
       }
       __syncthreads();
       for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
@@ -547,18 +583,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
           for (int c = 0; c < VC; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              store_elem(a.out, row_id * D + 16 * c + 4 * j + r, o[t][c][r] * inv, a.out_dtype);
+              store_elem(a.out, row_id * D + St::dim(c, j, r), o[t][c][r] * inv, a.out_dtype);
         } else {
           const int64_t slot = row_id * a.max_partitions + part;
-          float* dst = a.ws_acc + slot * D;
-          const float vs = a.v_scale;
-#pragma unroll
-          for (int c = 0; c < VC; ++c) {
-            f32x4_t x = o[t][c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] *= vs;
-            *reinterpret_cast<f32x4_t*>(dst + 16 * c + 4 * j) = x;
-          }
+          store_acc(a.ws_acc + slot * D, t, a.v_scale);
           if (j == 0) {
             a.ws_ml[slot * 2] = m[t];
             a.ws_ml[slot * 2 + 1] = l[t];
