@@ -94,43 +94,74 @@ def parse_args(argv=None):
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="post-process two rocprofv3 --pmc counter CSVs into profiles/ (no GPU)")
     ap.add_argument("--pmc-copy-mib", type=int, default=1024)
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="post-process a rocprofv3 kernel trace of this workload into profiles/ "
+                         "(no GPU)")
+    ap.add_argument("--bench-json", metavar="FILE",
+                    help="with --summarize-trace: a file whose last line is a bench JSON line")
     return ap.parse_args(argv)
 
 
 # ----------------------------------------------------------------------------- counters
 
-def _read_counter_csv(path):
+def _read_counter_rows(path):
+    """rocprofv3 counter CSV -> [(kernel name, grid size, counter, value)], one row per
+    (dispatch, counter)."""
     import csv
-    rows = list(csv.DictReader(open(path)))
-    out = {}
-    for r in rows:
+    out = []
+    for r in csv.DictReader(open(path)):
         name = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("KernelName") or ""
         cname = r.get("Counter_Name") or r.get("Counter-Name") or ""
         val = float(r.get("Counter_Value") or r.get("Counter-Value") or 0.0)
-        out.setdefault((name, cname), []).append(val)
+        grid = int(float(r.get("Grid_Size") or r.get("Grid_Size_X") or 0))
+        out.append((name, grid, cname, val))
     return out
 
 
+def _is_decode(k):
+    return "decode_valu_kernel" in k or "decode_mfma_kernel" in k
+
+
+def _is_write(k):
+    return "cache_write_kernel" in k or "cache_write_fp8_kernel" in k
+
+
+def _step_values(rows, counter, pred):
+    """Counter values of the dispatches of kernels matching pred at their most
+    frequent grid size: the per-step launches (the set-up's bulk writes of the
+    prior context use other grid sizes)."""
+    import collections
+    sel = [(g, v) for (k, g, c, v) in rows if c == counter and pred(k)]
+    if not sel:
+        return []
+    grid = collections.Counter(g for g, _ in sel).most_common(1)[0][0]
+    return [v for g, v in sel if g == grid]
+
+
+def _workload_cfg(args):
+    from pagedattention_kv_cache_amd.workloads import CONFIGS, FP8_CONFIGS
+    return FP8_CONFIGS[args.workload] if args.kv_cache == "fp8" else CONFIGS[args.workload]
+
+
 def summarize_pmc(args):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode kernel, scaled
-    by what the same counters read for a plain device copy of known size."""
-    fetch = _read_counter_csv(args.summarize_pmc[0])
-    write = _read_counter_csv(args.summarize_pmc[1])
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode kernel and of the
+    per-step cache write, scaled by what the same counters read for a plain
+    device copy of known size."""
+    from pagedattention_kv_cache_amd.workloads import DTYPE_BYTES, Workload
+    fetch = _read_counter_rows(args.summarize_pmc[0])
+    write = _read_counter_rows(args.summarize_pmc[1])
     copy_bytes = args.pmc_copy_mib * 2**20
-
-    def pick(table, counter, pred):
-        vals = [v for (k, c), vs in table.items() if c == counter and pred(k) for v in vs]
-        return vals
-
     is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
-    is_dec = lambda k: "decode_valu_kernel" in k or "decode_mfma_kernel" in k  # noqa: E731
-    copy_f = max(pick(fetch, "FETCH_SIZE", is_copy))
-    copy_w = max(pick(write, "WRITE_SIZE", is_copy))
-    dec_f = statistics.median(pick(fetch, "FETCH_SIZE", is_dec))
-    dec_w = statistics.median(pick(write, "WRITE_SIZE", is_dec))
+    copy_f = max(v for (k, g, c, v) in fetch if c == "FETCH_SIZE" and is_copy(k))
+    copy_w = max(v for (k, g, c, v) in write if c == "WRITE_SIZE" and is_copy(k))
     f_scale = copy_bytes / (copy_f * 1024.0)
     w_scale = copy_bytes / (copy_w * 1024.0)
+    dec_f = statistics.median(_step_values(fetch, "FETCH_SIZE", _is_decode))
+    dec_w = statistics.median(_step_values(write, "WRITE_SIZE", _is_decode))
+    cfg = _workload_cfg(args)
+    wl = Workload(cfg)
     res = {
+        "workload": cfg.name,
         "kernel_source_hash": kernel_source_hash(),
         "copy_probe_bytes": copy_bytes,
         "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
@@ -138,15 +169,142 @@ def summarize_pmc(args):
         "decode_fetch_kib": dec_f, "decode_write_kib": dec_w,
         "decode_fetch_bytes": dec_f * 1024.0 * f_scale,
         "decode_write_bytes": dec_w * 1024.0 * w_scale,
+        "algorithmic_kv_bytes": wl.kv_bytes(0),
     }
     res["traffic_bytes"] = res["decode_fetch_bytes"] + res["decode_write_bytes"]
-    from pagedattention_kv_cache_amd.workloads import CONFIGS
-    path = TRAFFIC_FILE.format(workload=CONFIGS[args.workload].name)
+    res["fetch_over_algorithmic"] = res["decode_fetch_bytes"] / res["algorithmic_kv_bytes"]
+    wf = _step_values(fetch, "FETCH_SIZE", _is_write)
+    ww = _step_values(write, "WRITE_SIZE", _is_write)
+    if wf and ww:
+        # the step's new K and V rows, read once and written once
+        new_kv = cfg.num_seqs * cfg.num_kv_heads * cfg.head_dim * 2
+        res["cache_write"] = {
+            "source_bytes": new_kv * DTYPE_BYTES[cfg.dtype],
+            "cache_bytes": new_kv * DTYPE_BYTES[cfg.kv_dtype],
+            "fetch_bytes": statistics.median(wf) * 1024.0 * f_scale,
+            "write_bytes": statistics.median(ww) * 1024.0 * w_scale,
+        }
+        cw = res["cache_write"]
+        cw["write_over_cache_bytes"] = cw["write_bytes"] / cw["cache_bytes"]
+    path = TRAFFIC_FILE.format(workload=cfg.name)
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
         f.write("\n")
     print(json.dumps(res, indent=1))
     return res
+
+
+def summarize_trace(args):
+    """profiles/<decode kernel>_<workload>.md from a rocprofv3 kernel trace of
+    `bench.py --workload N [--kv-cache fp8]`, the counter summary of the same
+    workload (profiles/traffic_<workload>.json, when taken on the current kernel
+    sources) and the JSON line of a plain benchmark run (--bench-json)."""
+    import collections
+    import csv
+
+    from pagedattention_kv_cache_amd.workloads import Workload
+    cfg = _workload_cfg(args)
+    wl = Workload(cfg)
+    disp = collections.defaultdict(list)
+    for r in csv.DictReader(open(args.summarize_trace)):
+        name = r["Kernel_Name"]
+        grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0) * \
+            int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        disp[name].append((grid, dur))
+    rows = []
+    for name, ds in disp.items():
+        if not any(tag in name for tag in ("decode_", "cache_write", "advance_step")):
+            continue
+        grid = collections.Counter(g for g, _ in ds).most_common(1)[0][0]
+        d = [x for g, x in ds if g == grid]
+        rows.append((name, len(d), statistics.mean(d), statistics.median(d), min(d), max(d)))
+    rows.sort(key=lambda r: -r[1] * r[2])
+    dec = [r for r in rows if _is_decode(r[0])]
+    kname = dec[0][0].split("<")[0].split("::")[-1].replace("void ", "") if dec else "decode"
+    kv = wl.kv_bytes(0) if cfg.steps == 1 else statistics.mean(wl.kv_bytes(s)
+                                                             for s in range(cfg.steps))
+    lines = [f"# {kname} -- {cfg.name}", ""]
+    d = wl.describe()
+    lines.append(f"Workload: {cfg.num_seqs} sequences, {cfg.num_q_heads}/{cfg.num_kv_heads} q/kv "
+                 f"heads, head_dim {cfg.head_dim}, {cfg.kv_dtype} KV, block_size {cfg.block_size}, "
+                 f"mean context {d['ctx_mean']:.0f} (max {d['ctx_max']}), {cfg.steps} step(s); "
+                 f"{kv:.0f} algorithmic KV bytes per decode launch.")
+    flags = f" --kv-cache {args.kv_cache}" if args.kv_cache != "native" else ""
+    lines += ["", "## Kernel trace", "", "```",
+              f"rocprofv3 --kernel-trace --stats -d <out>/trace -o trace --output-format csv -- \\",
+              f"    python3 bench.py --workload {args.workload}{flags} --steps 20 --warmup 2 "
+              f"--no-cpu-baseline --no-stream-probe",
+              f"python3 bench.py --workload {args.workload}{flags} --summarize-trace "
+              f"<out>/trace/trace_kernel_trace.csv --bench-json <bench line file>", "```", "",
+              "Per-step launches only (each kernel's most frequent grid size; the set-up's bulk "
+              "prefix writes are left out):", "",
+              "| kernel | launches | mean (us) | median (us) | min (us) | max (us) |",
+              "|---|---|---|---|---|---|"]
+    for name, n, mean, med, lo, hi in rows:
+        lines.append(f"| `{name.replace('void ', '').replace('(anonymous namespace)::', '')}` "
+                     f"| {n} | {mean:.1f} | {med:.1f} | {lo:.1f} | {hi:.1f} |")
+    if dec:
+        mean = dec[0][2]
+        lines += ["", f"Decode kernel: {kv:.0f} B / {mean:.1f} us = **{kv / mean / 1e3:.0f} GB/s, "
+                  f"{kv / mean / 1e3 / HBM_PEAK_GBPS:.1%} of 8 TB/s** (rocprofv3 mean)."]
+    tf = TRAFFIC_FILE.format(workload=cfg.name)
+    if os.path.exists(tf):
+        t = json.load(open(tf))
+        t.setdefault("algorithmic_kv_bytes", wl.kv_bytes(0))
+        stamp = "matches" if t.get("kernel_source_hash") == kernel_source_hash() else \
+            "does NOT match"
+        lines += ["", "## HBM traffic (rocprofv3 --pmc)", "", "```"]
+        for ctr, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            lines.append(f"rocprofv3 --pmc {ctr} -d <out>/pmc_{tag} -o {tag} --output-format csv -- "
+                         f"\\")
+            lines.append(f"    python3 bench.py --workload {args.workload}{flags} --steps 4 "
+                         f"--warmup 1 --no-cpu-baseline --no-stream-probe --copy-probe 1024")
+        lines.append(f"python3 bench.py --workload {args.workload}{flags} --summarize-pmc "
+                     f"<out>/pmc_fetch/fetch_counter_collection.csv "
+                     f"<out>/pmc_write/write_counter_collection.csv")
+        lines += ["```", "",
+                  f"Calibration: a 1 GiB device copy reads FETCH_SIZE = {t['copy_fetch_kib']:.0f} "
+                  f"KiB and WRITE_SIZE = {t['copy_write_kib']:.0f} KiB: fetched bytes = FETCH_SIZE "
+                  f"x {t['fetch_scale']:.3f} KiB, written = WRITE_SIZE x {t['write_scale']:.3f} KiB.",
+                  "", "| per launch | bytes | vs algorithmic |", "|---|---|---|",
+                  f"| decode fetched | {t['decode_fetch_bytes']:.4e} | "
+                  f"{t['decode_fetch_bytes'] / t['algorithmic_kv_bytes']:.4f} x KV bytes |",
+                  f"| decode written | {t['decode_write_bytes']:.4e} | partition results and "
+                  f"outputs |"]
+        cw = t.get("cache_write")
+        if cw:
+            lines += [f"| cache write fetched | {cw['fetch_bytes']:.4e} | "
+                      f"{cw['fetch_bytes'] / cw['source_bytes']:.2f} x the new rows "
+                      f"({cw['source_bytes']} B) |",
+                      f"| cache write written | {cw['write_bytes']:.4e} | "
+                      f"{cw['write_over_cache_bytes']:.2f} x the cache bytes of the new rows "
+                      f"({cw['cache_bytes']} B) |"]
+        lines += ["", f"Kernel source hash of the counted build: `{t['kernel_source_hash']}` "
+                  f"({stamp} the current sources)."]
+    if args.bench_json:
+        b = json.loads(open(args.bench_json).read().strip().splitlines()[-1])
+        r = b["roofline"]
+        lines += ["", "## Benchmark line (`python3 bench.py --workload "
+                  f"{args.workload}{flags}`, no profiler)", "",
+                  f"- step {b['ms_per_step'] * 1e3:.1f} us = {b['value']:.0f} GB/s "
+                  f"({b['pct_hbm_peak']:.1f}% of 8 TB/s), {b['tokens_per_s']:.3g} tokens/s;",
+                  f"- decode launch (HIP events around pa_decode_partitions: ordering + decode "
+                  f"kernels where the grid is sorted) {b['decode_partitions_ms'] * 1e3:.1f} us "
+                  f"= {r['achieved']:.0f} GB/s ({r['frac']:.1%} of 8 TB/s"
+                  + (f", {r['frac_of_attainable']:.1%} of the streaming-read probe"
+                     if r.get("frac_of_attainable") else "") + ");",
+                  f"- write {b['write_ms'] * 1e3:.1f} us, merge {b['decode_merge_ms'] * 1e3:.1f} us "
+                  f"between events; partition {b['config']['partition_size']}, grid "
+                  f"{b['config']['grid']}, {b['config']['waves_per_item']} waves per item."]
+        if b.get("one_pass_vs_partitioned"):
+            o = b["one_pass_vs_partitioned"]
+            lines.append(f"- one pass per (sequence, kv head) {o['one_pass_us']:.1f} us against "
+                         f"partitioned {o['partitioned_us']:.1f} us: {o['speedup']:.2f}x.")
+    out = os.path.join(ROOT, "profiles", f"{kname}_{cfg.name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
 
 
 # ----------------------------------------------------------------------------- benchmark
@@ -643,6 +801,9 @@ def main(argv=None):
     args = parse_args(argv)
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
         return
     run(args)
 
