@@ -114,8 +114,16 @@ def _read_counter_rows(path):
         cname = r.get("Counter_Name") or r.get("Counter-Name") or ""
         val = float(r.get("Counter_Value") or r.get("Counter-Value") or 0.0)
         grid = int(float(r.get("Grid_Size") or r.get("Grid_Size_X") or 0))
-        out.append((name, grid, cname, val))
+        out.append((name, grid, cname, val, int(r.get("Dispatch_Id") or 0)))
     return out
+
+
+def _probe_copy_value(rows, counter):
+    """The counter of the calibration copy: the run's first device-to-device copy
+    dispatch (bench.py --copy-probe issues it before anything else)."""
+    copies = sorted((d, v) for (k, g, c, v, d) in rows
+                    if c == counter and "copyBuffer" in k)
+    return copies[0][1]
 
 
 def _is_decode(k):
@@ -131,7 +139,7 @@ def _step_values(rows, counter, pred):
     frequent grid size: the per-step launches (the set-up's bulk writes of the
     prior context use other grid sizes)."""
     import collections
-    sel = [(g, v) for (k, g, c, v) in rows if c == counter and pred(k)]
+    sel = [(g, v) for (k, g, c, v, _) in rows if c == counter and pred(k)]
     if not sel:
         return []
     grid = collections.Counter(g for g, _ in sel).most_common(1)[0][0]
@@ -151,9 +159,8 @@ def summarize_pmc(args):
     fetch = _read_counter_rows(args.summarize_pmc[0])
     write = _read_counter_rows(args.summarize_pmc[1])
     copy_bytes = args.pmc_copy_mib * 2**20
-    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
-    copy_f = max(v for (k, g, c, v) in fetch if c == "FETCH_SIZE" and is_copy(k))
-    copy_w = max(v for (k, g, c, v) in write if c == "WRITE_SIZE" and is_copy(k))
+    copy_f = _probe_copy_value(fetch, "FETCH_SIZE")
+    copy_w = _probe_copy_value(write, "WRITE_SIZE")
     f_scale = copy_bytes / (copy_f * 1024.0)
     w_scale = copy_bytes / (copy_w * 1024.0)
     dec_f = statistics.median(_step_values(fetch, "FETCH_SIZE", _is_decode))
@@ -289,8 +296,9 @@ def summarize_trace(args):
                   f"{args.workload}{flags}`, no profiler)", "",
                   f"- step {b['ms_per_step'] * 1e3:.1f} us = {b['value']:.0f} GB/s "
                   f"({b['pct_hbm_peak']:.1f}% of 8 TB/s), {b['tokens_per_s']:.3g} tokens/s;",
-                  f"- decode launch (HIP events around pa_decode_partitions: ordering + decode "
-                  f"kernels where the grid is sorted) {b['decode_partitions_ms'] * 1e3:.1f} us "
+                  f"- decode launch (HIP events around pa_decode_partitions"
+                  + (": the ordering kernel and the decode kernel" if b["config"]["grid"] ==
+                     "sorted" else "") + f") {b['decode_partitions_ms'] * 1e3:.1f} us "
                   f"= {r['achieved']:.0f} GB/s ({r['frac']:.1%} of 8 TB/s"
                   + (f", {r['frac_of_attainable']:.1%} of the streaming-read probe"
                      if r.get("frac_of_attainable") else "") + ");",
