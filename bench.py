@@ -67,6 +67,12 @@ def parse_args(argv=None):
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per sequence (several: multi-query decode, as when draft "
                          "tokens are verified; the oracle baseline is then skipped)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="a step as pa_cache_write, then pa_decode_partitions (which orders the "
+                         "items itself on the sorted grid), then the merge; default: "
+                         "pa_decode_order (the write and the item order in one launch), then "
+                         "pa_decode_partitions with PA_DECODE_ORDERED (the decode kernel alone), "
+                         "then the merge")
     ap.add_argument("--fused-step", action="store_true",
                     help="one pa_decode_step call for write + decode partitions (its cache write "
                          "shares the launch that orders the decode's items); default: separate "
@@ -298,11 +304,13 @@ def summarize_trace(args):
                   f"({b['pct_hbm_peak']:.1f}% of 8 TB/s), {b['tokens_per_s']:.3g} tokens/s;",
                   f"- decode launch (HIP events around pa_decode_partitions"
                   + (": the ordering kernel and the decode kernel" if b["config"]["grid"] ==
-                     "sorted" else "") + f") {b['decode_partitions_ms'] * 1e3:.1f} us "
+                     "sorted" and not b.get("step_form", "").startswith("write+order,")
+                     else ": the decode kernel") + f") {b['decode_partitions_ms'] * 1e3:.1f} us "
                   f"= {r['achieved']:.0f} GB/s ({r['frac']:.1%} of 8 TB/s"
                   + (f", {r['frac_of_attainable']:.1%} of the streaming-read probe"
                      if r.get("frac_of_attainable") else "") + ");",
-                  f"- write {b['write_ms'] * 1e3:.1f} us, merge {b['decode_merge_ms'] * 1e3:.1f} us "
+                  f"- {'write + item order' if b.get('step_form', '').startswith('write+order,') else 'write'} "
+                  f"{b['write_ms'] * 1e3:.1f} us, merge {b['decode_merge_ms'] * 1e3:.1f} us "
                   f"between events; partition {b['config']['partition_size']}, grid "
                   f"{b['config']['grid']}, {b['config']['waves_per_item']} waves per item."]
         if b.get("one_pass_vs_partitioned"):
@@ -659,6 +667,9 @@ def run(args):
 
     n_layers = len(kcs)
     fused = args.fused_step and Q == 1 and c.kv_dtype != "fp8"
+    # default step form: the write and the item order in one launch before the
+    # decode kernel, which the events then bracket alone
+    split = not fused and not args.separate_write and Q == 1
 
     def step(i, ev=None):
         # step i: decode step (i // n_layers) % steps of layer i % n_layers
@@ -671,12 +682,25 @@ def run(args):
                 ev[1].record(stream)
             pa.decode_step_partitions(sk[s], sv[s], slots[s], out, qs[s], k_l, v_l, bt, ctx[s],
                                       scale, c.block_size, part, ws, flags)
+        elif split:
+            if c.kv_dtype == "fp8":  # a quantizing write of its own, then the order
+                write_kv(c, sk[s], sv[s], slots[s], k_l, v_l)
+                pa.decode_order(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
+                                flags)
+            else:
+                pa.decode_order(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
+                                flags, k=sk[s], v=sv[s], slot_mapping=slots[s])
+            if ev is not None:
+                ev[1].record(stream)
         else:
             write_kv(c, sk[s], sv[s], slots[s], k_l, v_l)
             if ev is not None:
                 ev[1].record(stream)
         if fused:
             pass
+        elif split:
+            decode_partitions_kv(c, out, qs[s], k_l, v_l, bt, ctx[s], part, ws,
+                                 flags | pa.ORDERED)
         elif Q > 1:
             ks, vs = c.fp8_scales if c.kv_dtype == "fp8" else (1.0, 1.0)
             pa.decode_mq_partitions(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part,
@@ -773,6 +797,8 @@ def run(args):
         "kv_bytes_per_step": int(kv),
         "write_ms": None if fused else round(write_ms, 5),
         "fused_write": fused,
+        "step_form": ("write+order, decode kernel, merge" if split else
+                      "write+order+decode, merge" if fused else "write, order+decode, merge"),
         "decode_partitions_ms": round(dec_ms, 5),
         "decode_partitions_ms_median_min_max": [round(statistics.median(dec_times), 5),
                                                 round(min(dec_times), 5),

@@ -121,6 +121,14 @@ typedef enum pa_status {
 #define PA_DECODE_SORTED_GRID 32u
 #define PA_DECODE_WORK_LIST 48u
 #define PA_DECODE_GRID_MASK 48u
+/* Bit 6: the workspace already holds this launch's item order: pa_decode_order
+ * ran with the same arguments on the same stream after the workspace's last
+ * use, so pa_decode / pa_decode_partitions (and the E4M3 forms) launch the
+ * decode kernel alone.  Only meaningful where the grid is the sorted one
+ * (pa_decode_grid); ignored elsewhere.  Single-query calls only:
+ * pa_decode_mq* with num_queries > 1, pa_decode_step* and pa_decode_noalloc
+ * give PA_ERR_UNSUPPORTED. */
+#define PA_DECODE_ORDERED 64u
 
 /*
  * pa_cache_write -- for every token i in [0, num_tokens) whose
@@ -300,6 +308,29 @@ int pa_decode_step_partitions(const void* k, const void* v, const int64_t* slot_
                               int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype,
                               void* workspace, size_t workspace_bytes, uint32_t flags,
                               void* stream);
+
+/*
+ * pa_decode_order -- the part of a decode step that precedes the decode
+ * kernel, in one launch: pa_cache_write of the step's new tokens (k, v,
+ * slot_mapping, num_tokens and the strides as in pa_decode_step; num_tokens =
+ * 0 for none) and, where the decode runs on the sorted grid, the ordering of
+ * its work items into the workspace.  A following pa_decode_partitions (or
+ * pa_decode, or the E4M3 forms) with the same arguments and flags |
+ * PA_DECODE_ORDERED then launches only the decode kernel; the results equal
+ * pa_decode_step's bit for bit.  Callers that time or schedule the decode
+ * kernel on its own use this split.  kv_dtype E4M3 is accepted with
+ * num_tokens = 0 only (its write needs scales: pa_cache_write_fp8).
+ * Arguments, workspace and errors as pa_decode_step.
+ */
+int pa_decode_order(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                    int64_t k_token_stride, int64_t v_token_stride, void* out, const void* q,
+                    void* k_cache, void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, float scale, int32_t block_size,
+                    int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t q_dtype, int32_t kv_dtype,
+                    int32_t out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
+                    void* stream);
 
 /*
  * pa_decode_mq / pa_decode_mq_partitions / pa_decode_mq_merge -- decode of

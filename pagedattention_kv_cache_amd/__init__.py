@@ -38,6 +38,8 @@ SORTED_GRID = 32
 # a persistent grid walking the list of items that hold tokens
 WORK_LIST = 48
 GRID_NAMES = {NO_WORK_LIST: "grid", SORTED_GRID: "sorted", WORK_LIST: "work_list"}
+# the workspace already holds the launch's item order (decode_order ran first)
+ORDERED = 64
 # torch.float8_e4m3fn: the OCP E4M3 KV-cache storage type (caches only)
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3}
 
@@ -114,7 +116,7 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_noalloc.restype = ctypes.c_int
         L.pa_decode_noalloc.argtypes = dec_args[:18] + [u32, vp]
         step_args = [vp, vp, vp, i64, i64, i64] + dec_args
-        for name in ("pa_decode_step", "pa_decode_step_partitions"):
+        for name in ("pa_decode_step", "pa_decode_step_partitions", "pa_decode_order"):
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name).argtypes = step_args
         L.pa_decode_mq_kernel.restype = i32
@@ -499,6 +501,41 @@ def decode_step(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, cont
     _decode_step_call("pa_decode_step", k, v, slot_mapping, out, q, k_cache, v_cache,
                       block_tables, context_lens, scale, block_size, partition_size, workspace,
                       flags)
+
+
+def decode_order(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                 partition_size=0, workspace=None, flags=AUTO, k=None, v=None,
+                 slot_mapping=None) -> None:
+    """The launch before the decode kernel: the step's cache write of k, v at
+    slot_mapping (when given) and, on the sorted grid, the item ordering into the
+    workspace.  decode_partitions / decode (or the E4M3 forms) with the same
+    arguments and flags | ORDERED then launch the decode kernel alone."""
+    if k is not None:
+        _decode_step_call("pa_decode_order", k, v, slot_mapping, out, q, k_cache, v_cache,
+                          block_tables, context_lens, scale, block_size, partition_size,
+                          workspace, flags)
+        return
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
+    B, Hq, d = q.shape
+    _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
+    NB, Hkv, bs, d2 = _cache_dims(k_cache, v_cache)
+    _require(bs == block_size and d2 == d, "cache shapes do not match block_size / head_dim")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(),
+             "block_tables must be contiguous int32 [B][max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
+             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
+    MB = block_tables.shape[1]
+    need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype, flags)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        raise PAError(-5, "decode_order needs the caller's workspace")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode_order(
+        None, None, None, 0, Hkv * d, Hkv * d, out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+        block_size, partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(k_cache), _dt(out),
+        ws_ptr, ws_bytes, flags, _stream(q.device)))
 
 
 def decode_step_partitions(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables,

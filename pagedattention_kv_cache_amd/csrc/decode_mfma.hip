@@ -276,9 +276,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
                               : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
       const int64_t e = lin / per_seq;
       hc = (int)(lin - e * per_seq);
-      if (e >= (int64_t)a.num_seqs * a.max_partitions) break;  // past the order: done
+      if (e < 0 || e >= (int64_t)a.num_seqs * a.max_partitions) break;  // past the order
       const int entry = a.order[e];
-      if (entry < 0) break;  // every item is taken: the rest of the order is empty
+      // -1: every item is taken; an entry out of range (an order the caller
+      // said was prepared and was not) ends the workgroup rather than a read
+      if (entry < 0 || entry >= a.num_seqs * a.max_partitions) break;
       b = entry / a.max_partitions;
       part = entry - b * a.max_partitions;
     } else {

@@ -103,7 +103,8 @@ int32_t pick_kernel(uint32_t flags, int32_t kv_dtype, int32_t q_dtype, int32_t g
 
 // Flag bits this library knows, with a valid kernel choice.
 bool valid_flags(uint32_t flags) {
-  if (flags & ~(PA_DECODE_KERNEL_MASK | PA_DECODE_WAVES_MASK | PA_DECODE_GRID_MASK))
+  if (flags & ~(PA_DECODE_KERNEL_MASK | PA_DECODE_WAVES_MASK | PA_DECODE_GRID_MASK |
+                PA_DECODE_ORDERED))
     return false;
   return (flags & PA_DECODE_KERNEL_MASK) != PA_DECODE_KERNEL_MASK;
 }
@@ -587,7 +588,9 @@ void* device_scratch() {
 
 namespace {
 
-enum Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
+// kOrder: only the launch before the decode kernel (a step's write and/or the
+// item ordering), for pa_decode_order
+enum Phase { kPartitions = 1, kMerge = 2, kBoth = 3, kOrder = 4 };
 
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -610,11 +613,13 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     return PA_ERR_SHAPE;
   if (forces_mfma(flags) && !mfma_eligible(kv_dtype, q_dtype)) return PA_ERR_UNSUPPORTED;
   if (num_queries < 1 || num_queries > 16) return PA_ERR_SHAPE;
+  const bool preordered = (flags & PA_DECODE_ORDERED) != 0 && phase != kOrder;
+  if (preordered && (num_queries > 1 || pre_write || use_scratch)) return PA_ERR_UNSUPPORTED;
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t kernel = pick_kernel(flags, kv_dtype, q_dtype, group, num_queries);
   if (!kernel) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) {  // nothing to attend; a step's cache write still runs
-    if (pre_write && pre_write->num_tokens > 0 && (phase & kPartitions))
+    if (pre_write && pre_write->num_tokens > 0 && (phase & (kPartitions | kOrder)))
       return pa::launch_cache_write(*pre_write, (hipStream_t)stream) == hipSuccess ? PA_OK
                                                                                   : PA_ERR_HIP;
     return PA_OK;
@@ -687,12 +692,22 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.order_static = a.order && !a.order_ctr ? 1 : 0;  // shorter partitions: static deal
 
   hipStream_t hs = (hipStream_t)stream;
-  if (phase & kPartitions) {
-    // a step's cache write goes first: in the launch that orders the items, or on its own
+  if (phase == kOrder) {  // the write and the ordering, no decode
     if (a.order) {
       if (pa::launch_decode_order(a, const_cast<int32_t*>(a.order), pre_write, hs) != hipSuccess)
         return PA_ERR_HIP;
     } else if (pre_write && pre_write->num_tokens > 0 &&
+               pa::launch_cache_write(*pre_write, hs) != hipSuccess) {
+      return PA_ERR_HIP;
+    }
+    return PA_OK;
+  }
+  if (phase & kPartitions) {
+    // a step's cache write goes first: in the launch that orders the items, or on its own
+    if (a.order && !preordered) {
+      if (pa::launch_decode_order(a, const_cast<int32_t*>(a.order), pre_write, hs) != hipSuccess)
+        return PA_ERR_HIP;
+    } else if (!a.order && pre_write && pre_write->num_tokens > 0 &&
                pa::launch_cache_write(*pre_write, hs) != hipSuccess) {
       return PA_ERR_HIP;
     }
@@ -757,9 +772,13 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
       size_t workspace_bytes, uint32_t flags, void *stream
 
 // A decode step: the step's cache write, then the decode; nothing is launched
-// unless both validate.
+// unless both validate.  kOrder (pa_decode_order): the write and the item
+// ordering only; E4M3 caches there only without a write.
 static int step_impl(PA_STEP_PARAMS, int phase) {
+  if (phase == kOrder && kv_dtype == PA_DTYPE_FP8_E4M3 && num_tokens == 0)
+    return decode_impl(PA_DECODE_ARGS, phase);
   if (kv_dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_DTYPE;
+  if (phase != kOrder && (flags & PA_DECODE_ORDERED)) return PA_ERR_UNSUPPORTED;
   pa::CacheWriteArgs w;
   const int st = write_args(k, v, slot_mapping, k_cache, v_cache, num_tokens, k_token_stride,
                             v_token_stride, num_kv_heads, head_dim, num_blocks, block_size,
@@ -775,6 +794,10 @@ int pa_decode_step(PA_STEP_PARAMS) {
 int pa_decode_step_partitions(PA_STEP_PARAMS) {
   return step_impl(k, v, slot_mapping, num_tokens, k_token_stride, v_token_stride, PA_DECODE_ARGS,
                    kPartitions);
+}
+int pa_decode_order(PA_STEP_PARAMS) {
+  return step_impl(k, v, slot_mapping, num_tokens, k_token_stride, v_token_stride, PA_DECODE_ARGS,
+                   kOrder);
 }
 
 #define PA_DECODE_FP8_PARAMS                                                                   \

@@ -144,7 +144,7 @@ def _dec(**kw):
     (dict(P=24), ESHAPE),
     (dict(flags=7), EUNSUP),
     (dict(flags=3), EUNSUP),               # both kernel bits
-    (dict(flags=64), EUNSUP),              # unknown bit
+    (dict(flags=128), EUNSUP),             # unknown bit
     (dict(flags=pa.FORCE_MFMA, kvd=F32, qd=F32), EUNSUP),  # matrix cores: 16-bit caches only
     (dict(flags=pa.FORCE_MFMA, qd=F32), EUNSUP),           # ... queried in the same dtype
     (dict(out=None), ENULL),
@@ -182,7 +182,8 @@ def _dec_noalloc(**kw):
     (dict(qd=F16), EDTYPE),
     (dict(out=None), ENULL),
     (dict(P=24), ESHAPE),
-    (dict(flags=64), EUNSUP),
+    (dict(flags=64), EUNSUP),             # ordered: no order can have been prepared
+    (dict(flags=128), EUNSUP),
     # 2048 x 32 rows x 32 partitions of 256 tokens: a workspace of ~1 GB
     (dict(B=2048, MB=512, P=256), ESCRATCH),
 ])
@@ -270,7 +271,7 @@ def test_waves_flags():
     assert L.pa_decode_waves(*args[:6], 384, BF16, BF16, 0) == 2
     assert L.pa_decode_waves(*args[:6], 128, BF16, BF16, 0) == 1
     assert L.pa_decode_waves(4, 4, 4, 64, 16, 13, 0, F32, F32, 0) == 1          # one pass of 208
-    assert L.pa_decode_waves(*args, 64) == EUNSUP
+    assert L.pa_decode_waves(*args, 128) == EUNSUP
     assert L.pa_decode_waves(*args[:6], 24, BF16, BF16, 0) == ESHAPE  # not a block multiple
     assert L.pa_decode_waves(*args[:7], F16, BF16, pa.WAVES_2) == EDTYPE
     # grid: the sorted grid for partitions of 1024+ tokens whose order fits
@@ -295,8 +296,8 @@ def test_waves_flags():
     assert L.pa_decode_work_list(*args, 0) == 0
     assert L.pa_decode_work_list(*args, W) == 1
     assert L.pa_decode_work_list(*args[:6], 8192, BF16, BF16, W) == 0           # one pass
-    assert L.pa_decode_work_list(*args, 64) == EUNSUP
-    assert L.pa_decode_grid(*args, 64) == EUNSUP
+    assert L.pa_decode_work_list(*args, 128) == EUNSUP
+    assert L.pa_decode_grid(*args, 128) == EUNSUP
     # the waves bits leave the kernel family alone
     assert L.pa_decode_kernel(32, 8, BF16, BF16, pa.WAVES_4) == pa.FORCE_MFMA
     assert L.pa_decode_kernel(32, 8, BF16, BF16, pa.WAVES_4 | pa.FORCE_VALU) == pa.FORCE_VALU
@@ -582,8 +583,34 @@ def _step(**kw):
     (dict(qd=F16), EDTYPE),
     (dict(ws=None, wsb=0, P=256), EWS),
     (dict(fn="pa_decode_step_partitions", ws=None, wsb=0, P=256), EWS),
-    (dict(flags=64), EUNSUP),
+    (dict(flags=64), EUNSUP),             # ordered: a step orders its items itself
+    (dict(flags=128), EUNSUP),
     (dict(T=0, B=0, out=None, q=None, bt=None, cl=None), OK),   # nothing to do
 ])
 def test_decode_step_validation(kw, status):
     assert _step(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kvd=FP8, qd=BF16), EDTYPE),          # an E4M3 write needs its scales ...
+    (dict(kvd=FP8, qd=BF16, T=0, ws=None, wsb=0, P=256), EWS),  # ... no write: decode checks
+    (dict(T=-1), ESHAPE),
+    (dict(k=None), ENULL),
+    (dict(Hq=30), ESHAPE),
+    (dict(ws=None, wsb=0, P=256), EWS),        # the order lives in the workspace
+    (dict(flags=128), EUNSUP),
+    (dict(T=0, B=0, out=None, q=None, bt=None, cl=None), OK),   # nothing to do
+])
+def test_decode_order_validation(kw, status):
+    assert _step(fn="pa_decode_order", **kw) == status
+
+
+def test_ordered_flag_is_known_and_refused_for_multi_query():
+    L = pa.lib()
+    assert L.pa_decode_kernel(32, 8, BF16, BF16, pa.ORDERED) == pa.FORCE_MFMA
+    assert L.pa_decode_workspace_size(4, 32, 8, 128, 16, 64, 256, BF16, pa.ORDERED) == \
+        L.pa_decode_workspace_size(4, 32, 8, 128, 16, 64, 256, BF16, 0)
+    f32 = 1.0
+    st = L.pa_decode_mq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, f32, f32, 16, 0, 4, 2, 32, 8, 128,
+                        100, 64, BF16, BF16, F32, None, 0, pa.ORDERED, None)
+    assert st == EUNSUP
