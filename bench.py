@@ -87,6 +87,8 @@ def parse_args(argv=None):
                     help="KV-cache copies the steps rotate over, so no step re-reads what the "
                          "previous one left in the 256 MB Infinity Cache")
     ap.add_argument("--no-stream-probe", action="store_true")
+    ap.add_argument("--no-size-probe", action="store_true",
+                    help="skip the streaming read of one launch's KV bytes")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step(s) captured in HIP graphs (multi-step "
                          "workloads: state advanced on the device by pa_advance_step)")
@@ -140,6 +142,10 @@ def _is_write(k):
     return "cache_write_kernel" in k or "cache_write_fp8_kernel" in k
 
 
+def _is_prologue(k):
+    return "decode_prologue_kernel" in k
+
+
 def _step_values(rows, counter, pred):
     """Counter values of the dispatches of kernels matching pred at their most
     frequent grid size: the per-step launches (the set-up's bulk writes of the
@@ -186,8 +192,15 @@ def summarize_pmc(args):
     }
     res["traffic_bytes"] = res["decode_fetch_bytes"] + res["decode_write_bytes"]
     res["fetch_over_algorithmic"] = res["decode_fetch_bytes"] / res["algorithmic_kv_bytes"]
-    wf = _step_values(fetch, "FETCH_SIZE", _is_write)
-    ww = _step_values(write, "WRITE_SIZE", _is_write)
+    # the step's cache write: its own kernel where it launches every step (the
+    # separate-write form, E4M3), else the launch that writes and orders the
+    # items (the default step form; its order traffic is a few KiB)
+    n_dec = len(_step_values(fetch, "FETCH_SIZE", _is_decode))
+    write_kernel = _is_write
+    if len(_step_values(fetch, "FETCH_SIZE", _is_write)) < n_dec:
+        write_kernel = _is_prologue
+    wf = _step_values(fetch, "FETCH_SIZE", write_kernel)
+    ww = _step_values(write, "WRITE_SIZE", write_kernel)
     if wf and ww:
         # the step's new K and V rows, read once and written once
         new_kv = cfg.num_seqs * cfg.num_kv_heads * cfg.head_dim * 2
@@ -198,6 +211,8 @@ def summarize_pmc(args):
             "write_bytes": statistics.median(ww) * 1024.0 * w_scale,
         }
         cw = res["cache_write"]
+        cw["kernel"] = "decode_prologue_kernel" if write_kernel is _is_prologue else \
+            "cache_write_kernel"
         cw["write_over_cache_bytes"] = cw["write_bytes"] / cw["cache_bytes"]
     path = TRAFFIC_FILE.format(workload=cfg.name)
     with open(path, "w") as f:
@@ -261,6 +276,21 @@ def summarize_trace(args):
         mean = dec[0][2]
         lines += ["", f"Decode kernel: {kv:.0f} B / {mean:.1f} us = **{kv / mean / 1e3:.0f} GB/s, "
                   f"{kv / mean / 1e3 / HBM_PEAK_GBPS:.1%} of 8 TB/s** (rocprofv3 mean)."]
+        probe = [(name, ds) for name, ds in disp.items() if "stream_read_kernel" in name]
+        if probe:
+            # the bench's size-matched probe: one plain streaming read of the
+            # decode launch's bytes per launch, at a few grid sizes
+            by_grid = collections.defaultdict(list)
+            for g, x in probe[0][1]:
+                by_grid[g].append(x)
+            best_g, best = min(((g, statistics.mean(x)) for g, x in by_grid.items()),
+                               key=lambda t: t[1])
+            lines.append(
+                f"The same run's size-matched streaming read (a plain read of the same bytes in "
+                f"one launch, rotating over the cache copies; {len(probe[0][1])} launches over "
+                f"{len(by_grid)} grid sizes): best mean {best:.1f} us at {best_g // 256} "
+                f"workgroups = {kv / best / 1e3:.0f} GB/s ({kv / best / 1e3 / HBM_PEAK_GBPS:.1%} "
+                f"of 8 TB/s); the decode kernel runs at {best / mean:.1%} of its rate.")
     tf = TRAFFIC_FILE.format(workload=cfg.name)
     if os.path.exists(tf):
         t = json.load(open(tf))
@@ -313,6 +343,13 @@ def summarize_trace(args):
                   f"{b['write_ms'] * 1e3:.1f} us, merge {b['decode_merge_ms'] * 1e3:.1f} us "
                   f"between events; partition {b['config']['partition_size']}, grid "
                   f"{b['config']['grid']}, {b['config']['waves_per_item']} waves per item."]
+        if b.get("size_matched_read"):
+            m = b["size_matched_read"]
+            lines.append(f"- a plain streaming read of the same {m['bytes']:.4g} bytes in one "
+                         f"launch (probe, same event timing, {m['copies']} copies, "
+                         f"{m['blocks']} workgroups): {m['us']:.1f} us = {m['gbps']:.0f} GB/s "
+                         f"({m['gbps'] / 8000:.1%} of 8 TB/s); the decode launch takes "
+                         f"{r['frac_of_size_matched_read']:.1%} of its rate.")
         if b.get("one_pass_vs_partitioned"):
             o = b["one_pass_vs_partitioned"]
             lines.append(f"- one pass per (sequence, kv head) {o['one_pass_us']:.1f} us against "
@@ -555,6 +592,47 @@ def stream_probe(dev, gib: int = 4, reps: int = 10) -> float:
     return best
 
 
+def size_matched_probe(dev, nbytes: int, copies: int, launches: int = 24) -> dict:
+    """A plain streaming read of the bytes one decode launch streams, in one
+    launch, timed like the decode: HIP events around each launch, rotating over
+    `copies` buffers as the decode rotates over its cache copies; best mean
+    over a few grid sizes.  What one launch of this size can reach (dispatch,
+    ramp and drain included), beside the large probe's steady rate."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "pagedattention_kv_cache_amd", "libpa_probe.so"))
+    fn = lib.pa_probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_void_p]
+    n = (int(nbytes) + 255) // 256 * 256
+    buf = torch.ones(copies * n // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best_us, best_blocks = None, None
+    for blocks in (1024, 2048, 4096, 8192):
+        def launch(i):
+            assert fn(buf.data_ptr() + (i % copies) * n, n, sink.data_ptr(), blocks,
+                      stream.cuda_stream) == 0
+        for i in range(copies):
+            launch(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(launches)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            launch(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = statistics.mean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+        if best_us is None or us < best_us:
+            best_us, best_blocks = us, blocks
+    del buf
+    torch.cuda.empty_cache()
+    return {"bytes": n, "us": round(best_us, 2), "gbps": round(n / (best_us * 1e-6) / 1e9, 1),
+            "blocks": best_blocks, "copies": copies}
+
+
 def _cpu_model():
     """The host CPU as /proc/cpuinfo names it: model name, then family / model /
     stepping (a virtualised host may report only a short model name)."""
@@ -759,6 +837,7 @@ def run(args):
     if args.one_pass_ratio and Q == 1:
         ratio = one_pass_ratio(args, wl, kcs, vcs, qs, bt, ctx, out, ws, int(p_eff), flags)
     attainable = None if args.no_stream_probe else stream_probe(dev)
+    same_bytes = None if args.no_size_probe else size_matched_probe(dev, kv, len(kcs))
     traffic = None
     tf = TRAFFIC_FILE.format(workload=c.name)
     if os.path.exists(tf):
@@ -825,6 +904,9 @@ def run(args):
     if attainable:
         result["attainable_read_gbps"] = round(attainable, 1)
         result["roofline"]["frac_of_attainable"] = round(achieved / attainable, 4)
+    if same_bytes:
+        result["size_matched_read"] = same_bytes
+        result["roofline"]["frac_of_size_matched_read"] = round(achieved / same_bytes["gbps"], 4)
     if want_cpu:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(wl, okc, ovc, threads)
