@@ -44,22 +44,31 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(CacheWriteArgs a,
   const int rem = (int)(gid - t * per_token);
   const int h = rem / chunks_per_row;
   const int c = rem - h * chunks_per_row;
-  const int64_t slot = a.slots[t];
-  if (slot < 0 || slot >= a.num_blocks * a.block_size) return;
-  const int64_t blk = slot / a.block_size;
-  const int off = (int)(slot - blk * a.block_size);
   constexpr int SB = ElemTraits<SRC>::bytes;
   constexpr int SPL = 16 / SB;  // source elements per 16-byte load
   const int64_t D = a.head_dim;
   const int e0 = c * 16;
-
-  float kx[16], vx[16];
+  // the source rows and the slot go out together (one round trip, not two)
   const char* ksrc = reinterpret_cast<const char*>(a.k) + ((t * a.k_stride) + h * D + e0) * SB;
   const char* vsrc = reinterpret_cast<const char*>(a.v) + ((t * a.v_stride) + h * D + e0) * SB;
+  uint4 kraw[16 / SPL], vraw[16 / SPL];
 #pragma unroll
   for (int i = 0; i < 16 / SPL; ++i) {
-    widen16<SRC>(ld16(ksrc + 16 * i), kx + SPL * i);
-    widen16<SRC>(ld16(vsrc + 16 * i), vx + SPL * i);
+    kraw[i] = ld16(ksrc + 16 * i);
+    vraw[i] = ld16(vsrc + 16 * i);
+  }
+  const int64_t slot = a.slots[t];
+#pragma unroll
+  for (int i = 0; i < 16 / SPL; ++i) loaded_here(kraw[i], vraw[i], slot);
+  if (slot < 0 || slot >= a.num_blocks * a.block_size) return;
+  const int64_t blk = slot / a.block_size;
+  const int off = (int)(slot - blk * a.block_size);
+
+  float kx[16], vx[16];
+#pragma unroll
+  for (int i = 0; i < 16 / SPL; ++i) {
+    widen16<SRC>(kraw[i], kx + SPL * i);
+    widen16<SRC>(vraw[i], vx + SPL * i);
   }
   uint32_t kw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll

@@ -23,20 +23,22 @@ __device__ __forceinline__ void cache_write_chunk(const CacheWriteArgs& a, int64
   const int rem = (int)(gid - t * per_token);
   const int h = rem / chunks_per_row;
   const int c = rem - h * chunks_per_row;
+  constexpr int EPC = 16 / EB;  // elements per chunk
+  const int64_t D = a.head_dim;
+  const int e0 = c * EPC;
+  // the source rows and the slot go out together (the rows do not depend on
+  // the slot): one round trip before the stores instead of two
+  const char* ksrc = reinterpret_cast<const char*>(a.k) + ((t * a.k_stride) + h * D + e0) * EB;
+  const char* vsrc = reinterpret_cast<const char*>(a.v) + ((t * a.v_stride) + h * D + e0) * EB;
+  const uint4 kraw = ld16(ksrc);
+  const uint4 vraw = ld16(vsrc);
   const int64_t slot = a.slots[t];
+  loaded_here(kraw, vraw, slot);
   // negative = padding; a slot past the pool breaks the caller's contract and
   // is dropped rather than written out of bounds
   if (slot < 0 || slot >= a.num_blocks * a.block_size) return;
   const int64_t blk = slot / a.block_size;
   const int off = (int)(slot - blk * a.block_size);
-  constexpr int EPC = 16 / EB;  // elements per chunk
-  const int64_t D = a.head_dim;
-  const int e0 = c * EPC;
-
-  const char* ksrc = reinterpret_cast<const char*>(a.k) + ((t * a.k_stride) + h * D + e0) * EB;
-  const char* vsrc = reinterpret_cast<const char*>(a.v) + ((t * a.v_stride) + h * D + e0) * EB;
-  const uint4 kraw = ld16(ksrc);
-  const uint4 vraw = ld16(vsrc);
 
   const int64_t quad = (blk * a.num_kv_heads + h) * (a.block_size / 4) + off / 4;
   const int row = off % 4;

@@ -117,6 +117,14 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// Holds loaded values to this point: an empty asm that reads them, so the
+// loads are issued (and waited for) before it and cannot be sunk past a
+// branch that follows, e.g. into the block that alone uses them.
+__device__ __forceinline__ void loaded_here(const uint4& a, const uint4& b, int64_t c) {
+  asm volatile("" ::"v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w), "v"(b.x), "v"(b.y), "v"(b.z),
+               "v"(b.w), "v"(c));
+}
+
 // 16-byte load with the non-temporal hint: cache data that is streamed once
 // (keys and values) without displacing reused lines.
 __device__ __forceinline__ uint4 ld16_nt(const void* p) {
