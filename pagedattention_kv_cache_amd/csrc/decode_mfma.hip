@@ -288,6 +288,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       hc = it - b * per_seq;
       part = (int)gridDim.y - 1 - (int)blockIdx.y;
     }
+    // An item's start-up loads and its first two chunks are issued at the
+    // highest wave priority, then the wave drops back: the hardware otherwise
+    // issues the oldest wave's loads first, and an item that starts on a young
+    // wave waits for its first bytes while older waves stream (on a skewed
+    // batch from HBM, the median item computed its first chunk 12 us into a
+    // 33 us launch).  Measured on the 16-bit
+    // caches, decode kernel: 0.1-2% faster on every workload, most on the
+    // skewed one; on E4M3 caches neutral to 1.2% slower, so they keep it off.
+    constexpr bool kStartPrio = KV != Elem::FP8;
+    if constexpr (kStartPrio) __builtin_amdgcn_s_setprio(3);
     const int h = hc / chunks;
     const int hq0 = h * a.group + (hc % chunks) * Gh;
     // the q / out row of column c: query c / Gh, head hq0 + c % Gh
@@ -509,6 +519,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         compute(b0, t0, w1);
         if (i + 1 >= nk) break;
         issue(b0, min(t0 + 2 * stride, last_t0), t0 + 2 * stride > last_t0);
+        if (kStartPrio && i == 0) __builtin_amdgcn_s_setprio(0);
         compute(b1, t0 + stride, w1);
       }
     }
@@ -598,6 +609,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     }
     }
   next_item:
+    if constexpr (KV != Elem::FP8) __builtin_amdgcn_s_setprio(0);
     if (KernArgs& a = *fresh_args(); a.order_ctr) {
       // A dynamic deal asks for the next item here, at the end of this one:
       // asked for with the start-up loads instead, the counter's latency
