@@ -54,7 +54,7 @@ class PAError(RuntimeError):
 
 def key_chunk(dtype: torch.dtype) -> int:
     """X: elements per 16-byte chunk of the key cache layout."""
-    return 16 // torch.tensor([], dtype=dtype).element_size()
+    return 16 // dtype.itemsize
 
 
 def key_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
@@ -193,13 +193,54 @@ def _dt(t: torch.Tensor) -> int:
     return _DTYPE[t.dtype]
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device) -> int:
+    """The current HIP stream of `device` (torch's raw handle query when it
+    has one: a decode step makes several calls, and the Stream object costs
+    microseconds each)."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None
+                           else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 
 def _require(cond: bool, msg: str) -> None:
     if not cond:
         raise PAError(-2, msg)
+
+
+def _decode_dims(out, q, k_cache, v_cache, block_tables, context_lens, block_size):
+    """(B, Hq, d, NB, Hkv, bs, MB) of a decode call after the layout checks the
+    C ABI cannot make (contiguity, cache layout, index dtypes).  Written out
+    inline: a decode step makes several calls, each paying for these checks."""
+    qs = q.shape
+    if len(qs) != 3 or not q.is_contiguous():
+        raise PAError(-2, "q must be contiguous [B][Hq][d]")
+    if out.shape != qs or not out.is_contiguous():
+        raise PAError(-2, "out must be contiguous [B][Hq][d]")
+    B, Hq, d = qs
+    ks = k_cache.shape
+    if len(ks) != 6 or len(v_cache.shape) != 5:
+        raise PAError(-2, "k_cache must be 6-D, v_cache 5-D")
+    NB, Hkv, nq, dx, four, X = ks
+    if four != 4 or X * k_cache.dtype.itemsize != 16:
+        raise PAError(-2, "k_cache must be [blocks][heads][block_size/4][head_dim/X][4][X]")
+    if v_cache.shape != (NB, Hkv, nq, dx * X, 4):
+        raise PAError(-2, "v_cache shape does not match k_cache")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise PAError(-2, "caches must be contiguous")
+    if nq * 4 != block_size or dx * X != d:
+        raise PAError(-2, "cache shapes do not match block_size / head_dim")
+    bts = block_tables.shape
+    if (block_tables.dtype != torch.int32 or len(bts) != 2 or bts[0] != B
+            or not block_tables.is_contiguous()):
+        raise PAError(-2, "block_tables must be contiguous int32 [B][max_blocks]")
+    if (context_lens.dtype != torch.int32 or context_lens.shape != (B,)
+            or not context_lens.is_contiguous()):
+        raise PAError(-2, "context_lens must be contiguous int32 [B]")
+    return B, Hq, d, NB, Hkv, block_size, bts[1]
 
 
 def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
@@ -322,37 +363,28 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, he
 
 def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                  partition_size, workspace, flags, kv_scales=None):
-    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
-    B, Hq, d = q.shape
-    _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
-    NB, Hkv, bs, d2 = _cache_dims(k_cache, v_cache)
-    _require(bs == block_size and d2 == d, "cache shapes do not match block_size / head_dim")
-    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
-             and block_tables.shape[0] == B and block_tables.is_contiguous(),
-             "block_tables must be contiguous int32 [B][max_blocks]")
-    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
-             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
-    MB = block_tables.shape[1]
-    kvd = k_cache.dtype
-    need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, kvd, flags)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        if fn_name not in ("pa_decode", "pa_decode_fp8"):
-            raise PAError(-5, "the phase entry points need the caller's workspace")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    B, Hq, d, NB, Hkv, bs, MB = _decode_dims(out, q, k_cache, v_cache, block_tables,
+                                             context_lens, block_size)
+    if workspace is None and fn_name in ("pa_decode", "pa_decode_fp8"):
+        # the one-call forms without a workspace: the binding allocates it (the
+        # library checks every workspace it is given against the size it needs)
+        need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype,
+                                     flags)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    fn = getattr(_lib or lib(), fn_name)
     if kv_scales is not None:
-        _check(getattr(lib(), fn_name)(
-            out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), float(kv_scales[0]),
-            float(kv_scales[1]), block_size, partition_size, B, Hq, Hkv, d, NB, MB, _dt(q),
-            _dt(out), ws_ptr, ws_bytes, flags, _stream(q.device)))
+        _check(fn(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                  block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+                  float(kv_scales[0]), float(kv_scales[1]), block_size, partition_size, B, Hq,
+                  Hkv, d, NB, MB, _dt(q), _dt(out), ws_ptr, ws_bytes, flags, _stream(q.device)))
         return
-    _check(getattr(lib(), fn_name)(
-        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), block_size,
-        partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(k_cache), _dt(out), ws_ptr, ws_bytes,
-        flags, _stream(q.device)))
+    _check(fn(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+              block_tables.data_ptr(), context_lens.data_ptr(), float(scale), block_size,
+              partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(k_cache), _dt(out), ws_ptr,
+              ws_bytes, flags, _stream(q.device)))
 
 
 def decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -460,33 +492,27 @@ def decode_fp8_partitions(out, q, k_cache, v_cache, block_tables, context_lens, 
 
 def _decode_step_call(fn_name, k, v, slot_mapping, out, q, k_cache, v_cache, block_tables,
                       context_lens, scale, block_size, partition_size, workspace, flags):
-    _require(k.dim() == 3 and v.dim() == 3 and k.shape == v.shape, "k, v must be [T][Hkv][d]")
-    T = k.shape[0]
-    for t in (k, v):
-        _require(t.stride(2) == 1 and t.stride(1) == k.shape[2], "heads of a token must be packed")
-    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,)
-             and slot_mapping.is_contiguous(), "slot_mapping must be contiguous int64 [T]")
-    _require(k.dtype == v.dtype == k_cache.dtype == v_cache.dtype, "dtype mismatch")
-    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
-    B, Hq, d = q.shape
-    _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
-    NB, Hkv, bs, d2 = _cache_dims(k_cache, v_cache)
-    _require(bs == block_size and d2 == d and tuple(k.shape[1:]) == (Hkv, d),
-             "cache shapes do not match k/v, q or block_size")
-    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
-             and block_tables.shape[0] == B and block_tables.is_contiguous(),
-             "block_tables must be contiguous int32 [B][max_blocks]")
-    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
-             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
-    MB = block_tables.shape[1]
-    need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype, flags)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        if fn_name != "pa_decode_step":
-            raise PAError(-5, "the phase entry points need the caller's workspace")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    B, Hq, d, NB, Hkv, bs, MB = _decode_dims(out, q, k_cache, v_cache, block_tables,
+                                             context_lens, block_size)
+    kshape = k.shape
+    if len(kshape) != 3 or v.shape != kshape or kshape[1] != Hkv or kshape[2] != d:
+        raise PAError(-2, "k, v must be [T][Hkv][d] matching the caches")
+    T = kshape[0]
+    if k.stride(2) != 1 or k.stride(1) != d or v.stride(2) != 1 or v.stride(1) != d:
+        raise PAError(-2, "heads of a token must be packed")
+    if (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,)
+            or not slot_mapping.is_contiguous()):
+        raise PAError(-2, "slot_mapping must be contiguous int64 [T]")
+    if not (k.dtype == v.dtype == k_cache.dtype == v_cache.dtype):
+        raise PAError(-2, "dtype mismatch")
+    if workspace is None and fn_name == "pa_decode_step":
+        need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype,
+                                     flags)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(getattr(lib(), fn_name)(
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    _check(getattr(_lib or lib(), fn_name)(
         k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), T, k.stride(0), v.stride(0),
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), float(scale), block_size,
@@ -515,20 +541,8 @@ def decode_order(out, q, k_cache, v_cache, block_tables, context_lens, scale, bl
                           block_tables, context_lens, scale, block_size, partition_size,
                           workspace, flags)
         return
-    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][d]")
-    B, Hq, d = q.shape
-    _require(out.shape == q.shape and out.is_contiguous(), "out must be contiguous [B][Hq][d]")
-    NB, Hkv, bs, d2 = _cache_dims(k_cache, v_cache)
-    _require(bs == block_size and d2 == d, "cache shapes do not match block_size / head_dim")
-    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
-             and block_tables.shape[0] == B and block_tables.is_contiguous(),
-             "block_tables must be contiguous int32 [B][max_blocks]")
-    _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
-             and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
-    MB = block_tables.shape[1]
-    need = decode_workspace_size(B, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype, flags)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        raise PAError(-5, "decode_order needs the caller's workspace")
+    B, Hq, d, NB, Hkv, bs, MB = _decode_dims(out, q, k_cache, v_cache, block_tables,
+                                             context_lens, block_size)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_decode_order(
@@ -569,11 +583,11 @@ def _decode_mq_call(fn_name, out, q, k_cache, v_cache, block_tables, context_len
     _require(context_lens.dtype == torch.int32 and context_lens.shape == (B,)
              and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
     MB = block_tables.shape[1]
-    need = decode_workspace_size(B * Q, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype, flags)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        if fn_name != "pa_decode_mq":
-            raise PAError(-5, "the phase entry points need the caller's workspace")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None and fn_name == "pa_decode_mq":
+        need = decode_workspace_size(B * Q, Hq, Hkv, d, bs, MB, partition_size, k_cache.dtype,
+                                     flags)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(getattr(lib(), fn_name)(
