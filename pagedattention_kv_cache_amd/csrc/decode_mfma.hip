@@ -91,14 +91,16 @@ constexpr int kChunk = 16;  // tokens per iteration: one 16-row QK^T tile
 // whole, and nothing reads them again in the launch.  Measured (decode
 // kernel): keys on the default policy instead cost 9-10% on the GQA and MHA
 // workloads; values non-temporal gained 0.6% (GQA lognormal batch) and 3% (MHA
-// batch) and lost 0.5% on long contexts.  The E4M3 values keep the default.
+// batch) and lost 0.5% on long contexts; E4M3 values on the default policy
+// cost 3.7% (GQA lognormal batch) and 1.2% (long contexts).
 constexpr int kNonTemporal = 2;
 
 
 // How a lane's matrix operands of one chunk are stored in the caches, loaded
-// and widened to the multiply type.  Per lane and 32-dim k-chunk c: the 8
-// dims 32c + 8j .. 32c + 8j + 7 of key token n; per 16-dim row chunk c: dim
-// 16c + n of value tokens 4j .. 4j + 3 (one token quad).
+// and widened to the multiply type.  16-bit caches, per lane and 32-dim
+// k-chunk c: the 8 dims 32c + 8j .. 32c + 8j + 7 of key token n; per 16-dim
+// row chunk c: dim 16c + n of value tokens 4j .. 4j + 3 (one token quad).
+// E4M3 caches permute the dims within 64-dim groups (below).
 template <Elem KV> struct Store;
 template <Elem KV> struct Store16 {  // f16 / bf16: loaded as the multiply type
   using Math = Mma<KV>;
@@ -107,8 +109,12 @@ template <Elem KV> struct Store16 {  // f16 / bf16: loaded as the multiply type
   static constexpr int EB = 2;
   static constexpr int kstep = 256;  // bytes between k-chunks (4 key chunks of a quad row)
   static constexpr int vstep = 128;  // bytes between 16-dim value row chunks
+  // one key load per 32-dim k-chunk c: lane group j holds dims 32c + 8j .. + 7
+  static constexpr bool kPairK = false;
+  static constexpr int kloads(int D) { return D / 32; }
+  static __device__ __forceinline__ int qdim(int c, int j) { return 32 * c + 8 * j; }
   // one value load per 16-dim row chunk: row chunk rc of lane (n, j) is dim 16 rc + n
-  static constexpr bool kPairDims = false;
+  static constexpr int kVDims = 1;
   static constexpr int vloads(int D) { return D / 16; }
   static __device__ __forceinline__ int dim(int rc, int j, int r) { return 16 * rc + 4 * j + r; }
   // offsets from the chunk's first token quad
@@ -129,61 +135,70 @@ template <Elem KV> struct Store16 {  // f16 / bf16: loaded as the multiply type
   static __device__ __forceinline__ VRaw load_v(const char* p) {
     return *reinterpret_cast<const VRaw*>(p);
   }
-  static __device__ __forceinline__ typename Math::vec8 k(KRaw r) { return r; }
+  static __device__ __forceinline__ typename Math::vec8 k(KRaw r, int) { return r; }
   static __device__ __forceinline__ typename Math::vec4 v(VRaw r, int) { return r; }
 };
 template <> struct Store<Elem::BF16> : Store16<Elem::BF16> {};
 template <> struct Store<Elem::F16> : Store16<Elem::F16> {};
 // E4M3: half the bytes per operand; widened exactly to bfloat16 (the queries
-// are bfloat16) before the matrix cores see them.  A key chunk of 16 bytes
-// holds 16 dims, so k-chunk c of lane group j is half (j & 1) of key chunk
-// 2c + j/2.  Values: one 8-byte load per lane covers two adjacent dims (2n,
-// 2n + 1 of a 32-dim group) of its token quad, so the 16 lanes of a quad read
-// one whole 128-byte line; the two dims feed two P.V products (row chunks 2c
-// and 2c + 1), whose output rows are then the even and odd dims.
+// are bfloat16) before the matrix cores see them.  Every load is 16 bytes, so
+// a chunk takes half the load instructions of 8-byte pieces (measured: 1.6%
+// on the GQA lognormal batch for the keys, 0.6% more for the values).
 template <> struct Store<Elem::FP8> {
   using Math = Mma<Elem::BF16>;
-  using KRaw = uint2;
-  using VRaw = uint2;
+  using KRaw = uint4;
+  using VRaw = uint4;
   static constexpr int EB = 1;
-  static constexpr int kstep = 128;
-  static constexpr int vstep = 128;  // bytes between 32-dim value groups
-  static constexpr bool kPairDims = true;
-  static constexpr int vloads(int D) { return D / 32; }
-  // row chunk rc = 2c + h holds dims 32c + 2n + h; output row 4j + r of it is
-  // dim 32c + 8j + 2r + h
+  // Keys: one 16-byte load per lane covers two k-chunks.  Lane group j loads
+  // key chunk 4p + j (dims 64p + 16j .. + 15) of its token; its first 8
+  // codes feed k-chunk 2p, the last 8 k-chunk 2p + 1, and the queries are
+  // loaded with the same dims (qdim), so each k-chunk still sums 32 dims.
+  static constexpr bool kPairK = true;
+  static constexpr int kloads(int D) { return D / 64; }
+  static __device__ __forceinline__ int qdim(int c, int j) {
+    return 64 * (c >> 1) + 16 * j + 8 * (c & 1);
+  }
+  static constexpr int kstep = 256;  // bytes between key loads (4 key chunks of a quad row)
+  static constexpr int vstep = 256;  // bytes between 64-dim value groups
+  // Values: one 16-byte load per lane covers four adjacent dims (4n .. 4n + 3
+  // of a 64-dim group) of its token quad, so the 16 lanes of a quad read 256
+  // contiguous bytes; the four dims feed four P.V products (row chunks 4c + h)
+  static constexpr int kVDims = 4;
+  static constexpr int vloads(int D) { return D / 64; }
+  // row chunk rc = 4c + h holds dims 64c + 4n + h; output row 4j + r of it is
+  // dim 64c + 16j + 4r + h
   static __device__ __forceinline__ int dim(int rc, int j, int r) {
-    return 32 * (rc >> 1) + 8 * j + 2 * r + (rc & 1);
+    return 64 * (rc >> 2) + 16 * j + 4 * r + (rc & 3);
   }
   static __device__ __forceinline__ int koff(int n, int j, int D) {
-    return ((n >> 2) * (D / 16) + (j >> 1)) * 64 + (n & 3) * 16 + (j & 1) * 8;
+    return ((n >> 2) * (D / 16) + j) * 64 + (n & 3) * 16;
   }
-  static __device__ __forceinline__ int voff(int n, int j, int D) { return (j * D + 2 * n) * 4; }
+  static __device__ __forceinline__ int voff(int n, int j, int D) { return (j * D + 4 * n) * 4; }
   static __device__ __forceinline__ KRaw load_k(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(KRaw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
+    return __builtin_bit_cast(KRaw,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
   }
   static __device__ __forceinline__ VRaw load_v(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(VRaw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
+    return __builtin_bit_cast(VRaw,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
   }
-  static __device__ __forceinline__ KRaw load_k(const char* p) {
-    return *reinterpret_cast<const KRaw*>(p);
-  }
-  static __device__ __forceinline__ VRaw load_v(const char* p) {
-    return *reinterpret_cast<const VRaw*>(p);
-  }
+  static __device__ __forceinline__ KRaw load_k(const char* p) { return ld16_nt(p); }
+  static __device__ __forceinline__ VRaw load_v(const char* p) { return ld16(p); }
   // gfx950 widens two E4M3 codes straight to a bfloat16 pair (scale 1: no
   // scaling); every E4M3 value is exact in bfloat16.
   template <bool HI>
   static __device__ __forceinline__ uint32_t pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   }
-  static __device__ __forceinline__ Math::vec8 k(KRaw r) {
-    const uint4 w = {pair<false>(r.x), pair<true>(r.x), pair<false>(r.y), pair<true>(r.y)};
+  // k-chunk 2p + h: codes 8h .. 8h + 7 of the load
+  static __device__ __forceinline__ Math::vec8 k(KRaw r, int h) {
+    const uint32_t x = h ? r.z : r.x, y = h ? r.w : r.y;
+    const uint4 w = {pair<false>(x), pair<true>(x), pair<false>(y), pair<true>(y)};
     return __builtin_bit_cast(Math::vec8, w);
   }
-  // the four tokens of dim 2n (h = 0) or 2n + 1 (h = 1)
+  // the four tokens of dim 4n + h
   static __device__ __forceinline__ Math::vec4 v(VRaw r, int h) {
-    const uint32_t x = h ? r.y : r.x;
+    const uint32_t x = h == 0 ? r.x : h == 1 ? r.y : h == 2 ? r.z : r.w;
     const uint2 w = {pair<false>(x), pair<true>(x)};
     return __builtin_bit_cast(Math::vec4, w);
   }
@@ -191,7 +206,7 @@ template <> struct Store<Elem::FP8> {
 
 template <Elem KV, int D>
 struct Buffers {
-  typename Store<KV>::KRaw k[D / 32];  // key row pieces of this lane's token
+  typename Store<KV>::KRaw k[Store<KV>::kloads(D)];  // key row pieces of this lane's token
   typename Store<KV>::VRaw v[Store<KV>::vloads(D)];  // 4-token value runs of the row chunks
 };
 
@@ -207,6 +222,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
   using vec4 = typename M::vec4;
   using scalar = typename M::scalar;
   constexpr int KC = D / 32;  // QK^T k-chunks
+  constexpr int KL = St::kloads(D);  // key loads per chunk
   constexpr int VC = D / 16;  // P.V row chunks
   constexpr int VL = St::vloads(D);  // value loads per chunk
   constexpr int NT = (G + 15) / 16;  // 16-column tiles: every key and value load feeds all
@@ -323,7 +339,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       for (int c = 0; c < KC; ++c) {
         if (16 * t + n < G) {
           const char* qp = reinterpret_cast<const char*>(a.q) +
-                           (row_of(16 * t + n) * D + 32 * c + 8 * j) * 2;
+                           (row_of(16 * t + n) * D + St::qdim(c, j)) * 2;
           qv[t][c] = *reinterpret_cast<const vec8*>(qp);
         } else {
 #pragma unroll
@@ -374,7 +390,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         int ko = koff, vo = voff;
         asm volatile("" : "+v"(ko), "+v"(vo));
 #pragma unroll
-        for (int c = 0; c < KC; ++c) buf.k[c] = St::load_k(rk, ko + St::kstep * c);
+        for (int c = 0; c < KL; ++c) buf.k[c] = St::load_k(rk, ko + St::kstep * c);
 #pragma unroll
         for (int c = 0; c < VL; ++c) buf.v[c] = St::load_v(rv, vo + St::vstep * c);
       } else {
@@ -389,7 +405,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
         const char* vp = vc + (int64_t)pv * block_stride + (iv >> 2) * 4 * D * St::EB +
                          St::voff(n, 0, D);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) buf.k[c] = St::load_k(kp + St::kstep * c);
+        for (int c = 0; c < KL; ++c) buf.k[c] = St::load_k(kp + St::kstep * c);
 #pragma unroll
         for (int c = 0; c < VL; ++c) buf.v[c] = St::load_v(vp + St::vstep * c);
       }
@@ -403,7 +419,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     // this lane's accumulators of tile t, times sc, into the D floats at base
     // (16-byte aligned): dim St::dim(c, j, r) holds o[t][c][r]
     auto store_acc = [&](float* base, int t, float sc) {
-      if constexpr (!St::kPairDims) {
+      if constexpr (St::kVDims == 1) {
 #pragma unroll
         for (int c = 0; c < VC; ++c) {
           f32x4_t x = o[t][c];
@@ -412,15 +428,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
           *reinterpret_cast<f32x4_t*>(base + 16 * c + 4 * j) = x;
         }
       } else {
+        // group c: lane group j holds dims 64c + 16j + 4r + h in o[t][4c + h][r]
 #pragma unroll
-        for (int c = 0; c < VC / 2; ++c) {
-          const f32x4_t& e = o[t][2 * c];
-          const f32x4_t& f = o[t][2 * c + 1];
-          const f32x4_t lo = {e[0] * sc, f[0] * sc, e[1] * sc, f[1] * sc};
-          const f32x4_t hi = {e[2] * sc, f[2] * sc, e[3] * sc, f[3] * sc};
-          *reinterpret_cast<f32x4_t*>(base + 32 * c + 8 * j) = lo;
-          *reinterpret_cast<f32x4_t*>(base + 32 * c + 8 * j + 4) = hi;
-        }
+        for (int c = 0; c < VC / 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f32x4_t x = {o[t][4 * c][r] * sc, o[t][4 * c + 1][r] * sc,
+                               o[t][4 * c + 2][r] * sc, o[t][4 * c + 3][r] * sc};
+            *reinterpret_cast<f32x4_t*>(base + 64 * c + 16 * j + 4 * r) = x;
+          }
       }
     };
     float m[NT];     // running max of column 16t + n (log2 domain), uniform over j
@@ -434,7 +450,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     auto compute = [&](Buffers<KV, D>& buf, int t0, int t_stop) {
       vec4 vv[VC];
 #pragma unroll
-      for (int c = 0; c < VC; ++c) vv[c] = St::v(buf.v[St::kPairDims ? c >> 1 : c], c & 1);
+      for (int c = 0; c < VC; ++c) vv[c] = St::v(buf.v[c / St::kVDims], c % St::kVDims);
       // uniform: the chunk reaches the context end, the partition end or a query's limit
       const bool edge = t0 + kChunk > min(t_stop, lim_lo);
       if (edge) {
@@ -450,7 +466,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
       for (int t = 0; t < NT; ++t) {
         f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c = 0; c < KC; ++c) sacc = M::qk(St::k(buf.k[c]), qv[t][c], sacc);
+        for (int c = 0; c < KC; ++c)
+          sacc = M::qk(St::k(buf.k[St::kPairK ? c >> 1 : c], c & 1), qv[t][c], sacc);
         float s[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[r] = sacc[r] * a.scale_log2;
