@@ -98,45 +98,56 @@ constexpr int kNonTemporal = 2;
 
 // How a lane's matrix operands of one chunk are stored in the caches, loaded
 // and widened to the multiply type.  16-bit caches, per lane and 32-dim
-// k-chunk c: the 8 dims 32c + 8j .. 32c + 8j + 7 of key token n; per 16-dim
-// row chunk c: dim 16c + n of value tokens 4j .. 4j + 3 (one token quad).
-// E4M3 caches permute the dims within 64-dim groups (below).
+// k-chunk c: the 8 dims 32c + 8j .. 32c + 8j + 7 of key token n (one 16-byte
+// load); per 32-dim value group c: dims 32c + 2n and 32c + 2n + 1 of value
+// tokens 4j .. 4j + 3 (one token quad, one 16-byte load), which feed the
+// P.V row chunks 2c and 2c + 1.  E4M3 caches permute the dims within 64-dim
+// groups (below).  Every operand load is 16 bytes: 8-byte value loads (one
+// dim per lane) measured 0.3% slower on the GQA lognormal batch and 2.9% on
+// the skewed batch.
 template <Elem KV> struct Store;
 template <Elem KV> struct Store16 {  // f16 / bf16: loaded as the multiply type
   using Math = Mma<KV>;
   using KRaw = typename Math::vec8;
-  using VRaw = typename Math::vec4;
+  using VRaw = uint4;  // two dims x four tokens
   static constexpr int EB = 2;
   static constexpr int kstep = 256;  // bytes between k-chunks (4 key chunks of a quad row)
-  static constexpr int vstep = 128;  // bytes between 16-dim value row chunks
+  static constexpr int vstep = 256;  // bytes between 32-dim value groups
   // one key load per 32-dim k-chunk c: lane group j holds dims 32c + 8j .. + 7
   static constexpr bool kPairK = false;
   static constexpr int kloads(int D) { return D / 32; }
   static __device__ __forceinline__ int qdim(int c, int j) { return 32 * c + 8 * j; }
-  // one value load per 16-dim row chunk: row chunk rc of lane (n, j) is dim 16 rc + n
-  static constexpr int kVDims = 1;
-  static constexpr int vloads(int D) { return D / 16; }
-  static __device__ __forceinline__ int dim(int rc, int j, int r) { return 16 * rc + 4 * j + r; }
+  // one value load per 32-dim group: dims 2n, 2n + 1 of group c feed row
+  // chunks 2c and 2c + 1; output row 4j + r of row chunk 2c + h is dim
+  // 32c + 8j + 2r + h
+  static constexpr int kVDims = 2;
+  static constexpr int vloads(int D) { return D / 32; }
+  static __device__ __forceinline__ int dim(int rc, int j, int r) {
+    return 32 * (rc >> 1) + 8 * j + 2 * r + (rc & 1);
+  }
   // offsets from the chunk's first token quad
   static __device__ __forceinline__ int koff(int n, int j, int D) {
     return ((n >> 2) * (D / 8) + j) * 64 + (n & 3) * 16;
   }
-  static __device__ __forceinline__ int voff(int n, int j, int D) { return (j * D + n) * 8; }
+  static __device__ __forceinline__ int voff(int n, int j, int D) { return (j * D + 2 * n) * 8; }
   static __device__ __forceinline__ KRaw load_k(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(KRaw,
                               __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
   }
   static __device__ __forceinline__ VRaw load_v(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(VRaw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
+    return __builtin_bit_cast(VRaw,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
   }
   static __device__ __forceinline__ KRaw load_k(const char* p) {
     return __builtin_bit_cast(KRaw, ld16_nt(p));
   }
-  static __device__ __forceinline__ VRaw load_v(const char* p) {
-    return *reinterpret_cast<const VRaw*>(p);
-  }
+  static __device__ __forceinline__ VRaw load_v(const char* p) { return ld16(p); }
   static __device__ __forceinline__ typename Math::vec8 k(KRaw r, int) { return r; }
-  static __device__ __forceinline__ typename Math::vec4 v(VRaw r, int) { return r; }
+  // the four tokens of dim 2n + h
+  static __device__ __forceinline__ typename Math::vec4 v(VRaw r, int h) {
+    const uint2 w = h ? uint2{r.z, r.w} : uint2{r.x, r.y};
+    return __builtin_bit_cast(typename Math::vec4, w);
+  }
 };
 template <> struct Store<Elem::BF16> : Store16<Elem::BF16> {};
 template <> struct Store<Elem::F16> : Store16<Elem::F16> {};
@@ -428,15 +439,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
           *reinterpret_cast<f32x4_t*>(base + 16 * c + 4 * j) = x;
         }
       } else {
-        // group c: lane group j holds dims 64c + 16j + 4r + h in o[t][4c + h][r]
+        // group c: lane group j holds the V * 4 dims from 16Vc + 4Vj, dim
+        // 16Vc + 4Vj + Vr + h in o[t][Vc + h][r] (V dims per value load)
+        constexpr int V = St::kVDims;
 #pragma unroll
-        for (int c = 0; c < VC / 4; ++c)
+        for (int c = 0; c < VC / V; ++c) {
+          float x[4 * V];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const f32x4_t x = {o[t][4 * c][r] * sc, o[t][4 * c + 1][r] * sc,
-                               o[t][4 * c + 2][r] * sc, o[t][4 * c + 3][r] * sc};
-            *reinterpret_cast<f32x4_t*>(base + 64 * c + 16 * j + 4 * r) = x;
-          }
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int h = 0; h < V; ++h) x[V * r + h] = o[t][V * c + h][r] * sc;
+#pragma unroll
+          for (int u = 0; u < V; ++u)
+            *reinterpret_cast<f32x4_t*>(base + 16 * V * c + 4 * V * j + 4 * u) =
+                f32x4_t{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
+        }
       }
     };
     float m[NT];     // running max of column 16t + n (log2 domain), uniform over j
