@@ -423,7 +423,16 @@ int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, cons
 /*
  * The partition size pa_decode uses when called with partition_size == 0 and
  * the same arguments (a pure function of them; no device query).  Returns a
- * negative pa_status for invalid arguments.
+ * negative pa_status for invalid arguments.  Where this size is 2048 tokens or
+ * more and the launch runs on the sorted grid (pa_decode_grid) with one query
+ * per sequence, the launch refines it on the device from the actual context
+ * lengths to half, the same or twice this size (the ordering kernel decides;
+ * the result is then that of pa_decode with the refined size passed
+ * explicitly), and pa_decode_workspace_size(partition_size = 0) covers the
+ * half.  The refinement: a batch whose longest context is at most twice the
+ * mean keeps the size; otherwise the largest of the three that is at most a
+ * third of one compute unit's share of the token x kv-head work, twice only
+ * while the longest context still spans two partitions and twice <= 8192.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size,
@@ -470,10 +479,11 @@ int32_t pa_decode_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 
 /*
  * Workspace bytes pa_decode needs for these arguments (partition_size as
- * passed to pa_decode, 0 allowed): per (sequence, q head, partition) the
- * running max and sum, then the partial output vector, each region 256-byte
- * aligned.  0 when a single pass
- * suffices.  Returns 0 for invalid arguments as well; pa_decode reports those.
+ * passed to pa_decode, 0 allowed: then counted for the smallest partition the
+ * launch may refine to, see pa_decode_partition_size): per (sequence, q head,
+ * partition) the running max and sum, then the partial output vector, each
+ * region 256-byte aligned, then on the sorted grid the item order.  0 when a
+ * single pass suffices.  Returns 0 for invalid arguments as well; pa_decode reports those.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
@@ -533,7 +543,7 @@ int pa_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_
  *   their own.
  * E4M3 caches: PA_ERR_DTYPE (as pa_decode).
  */
-#define PA_SCRATCH_BYTES (32u << 20) /* 32 MiB */
+#define PA_SCRATCH_BYTES (64u << 20) /* 64 MiB */
 int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, float scale,
                       int32_t block_size, int32_t partition_size, int32_t num_seqs,

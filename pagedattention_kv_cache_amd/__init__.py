@@ -430,7 +430,7 @@ def check_slots(slot_mapping: torch.Tensor, num_blocks: int, block_size: int,
 
 
 # bytes of the library's static scratch behind decode_noalloc (PA_SCRATCH_BYTES)
-SCRATCH_BYTES = 32 << 20
+SCRATCH_BYTES = 64 << 20
 
 
 def decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,

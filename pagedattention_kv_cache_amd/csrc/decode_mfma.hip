@@ -267,6 +267,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
   int cursor = 0;
   const int bx = (int)blockIdx.x;
   int round = 0, it = bx;
+  // with a partition picked on the device: the number of entries in the
+  // order, from the item before, so that a ticket past it ends the workgroup
+  // without reading the entry (a last dependent load that cost 2% where every
+  // workgroup has one item)
+  int order_total = 0x7fffffff;
   while (it < n_work) {
     {
     KernArgs& a = *fresh_args();
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
     float* red = reinterpret_cast<float*>(dyn_lds + a.list_ints);  // wave merge area
     const int lbs = a.log2_block_size;
     const int bs = a.block_size;
-    const int P = a.partition_size;
+    int P = a.partition_size;  // or the ordering kernel's pick (below)
     const int64_t head_tile = (int64_t)bs * D * St::EB;  // bytes of one (block, head) tile
     const int64_t block_stride = (int64_t)a.num_kv_heads * head_tile;
     const int n = lane & 15;
@@ -303,8 +308,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs args) {
                               : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
       const int64_t e = lin / per_seq;
       hc = (int)(lin - e * per_seq);
-      if (e < 0 || e >= (int64_t)a.num_seqs * a.max_partitions) break;  // past the order
+      if (e < 0 || e >= (int64_t)a.num_seqs * a.max_partitions || e >= order_total)
+        break;  // past the order
       const int entry = a.order[e];
+      if (a.part_dev) {
+        // the partition the ordering kernel picked and its entry count, loaded
+        // beside the entry (a load of their own first cost a round trip)
+        P = partition_of(a);
+        order_total = __builtin_amdgcn_readfirstlane(a.part_dev[1]);
+      }
       // -1: every item is taken; an entry out of range (an order the caller
       // said was prepared and was not) ends the workgroup rather than a read
       if (entry < 0 || entry >= a.num_seqs * a.max_partitions) break;

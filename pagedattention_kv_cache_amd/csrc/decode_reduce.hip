@@ -31,7 +31,8 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArg
   constexpr int kRows = kReduceThreads / D;  // rows per workgroup
   const int b = blockIdx.y;
   const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.block_size);
-  const int n_parts = L > 0 ? (L + a.partition_size - 1) / a.partition_size : 0;
+  const int P = partition_of(a);
+  const int n_parts = L > 0 ? (L + P - 1) / P : 0;
   if (n_parts <= 1) return;
   const int rows = a.num_queries * a.num_q_heads;
   const int qh = (int)blockIdx.x * kRows + (int)threadIdx.x / D;  // query * num_q_heads + q head

@@ -74,7 +74,34 @@ struct DecodeArgs {
   // workgroup i takes entry r * gridDim.x + i, mirrored (gridDim.x - 1 - i)
   // on odd rounds, until the order runs out.
   int32_t order_static;
+  // Where the ordering kernel picks the partition (part_pick), two words it
+  // writes for the launches that follow: [0] the partition, [1] the number of
+  // entries in the order (a ticket past it ends a workgroup without reading
+  // the entry); else NULL.
+  int32_t* part_dev;
+  // 1: the library's own partition choice (partition_size = 0), refined by the
+  // ordering kernel from the actual context lengths -- partition_size / 2,
+  // partition_size or 2 * partition_size (max_partitions is counted for the
+  // half); the decode and merge kernels read it (partition_of).  0:
+  // partition_size is the partition.
+  int32_t part_pick;
+  int32_t num_cus;  // compute units of the device (the ordering kernel's choice)
 };
+
+// The partition a launch uses: the one the ordering kernel picked, when it
+// picks, else partition_size.  A stored value outside the three the ordering
+// kernel may pick (an ordered launch whose ordering never ran) falls back to
+// partition_size, so every partition index stays below max_partitions.
+template <class Args>  // DecodeArgs in any address space (kernel arguments included)
+__device__ __forceinline__ int partition_of(Args& a) {
+  const int p = a.partition_size;
+  if (!a.part_dev || !a.part_pick) return p;
+  // the kernel writes the workspace, so the compiler loads the word with a
+  // vector load; readfirstlane makes it (and everything derived from it)
+  // wave-uniform again (measured: 21% slower decode without)
+  const int d = __builtin_amdgcn_readfirstlane(*a.part_dev);
+  return (d == p / 2 || d == 2 * p) ? d : p;
+}
 
 // LDS ints a workgroup needs for the work list of a persistent launch.
 __host__ __device__ inline int work_list_lds_ints(int num_seqs, int max_partitions) {

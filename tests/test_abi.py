@@ -198,7 +198,7 @@ def test_decode_noalloc_empty_batch_is_noop():
 
 
 def test_decode_noalloc_scratch_covers_the_full_size_workloads():
-    """PA_SCRATCH_BYTES (32 MiB) holds the partition workspace of every
+    """PA_SCRATCH_BYTES (64 MiB) holds the partition workspace of every
     full-size decode workload in the launch configuration the benchmark uses."""
     from pagedattention_kv_cache_amd.workloads import CONFIGS, DTYPE_TORCH, Workload
     for cid, cfg in CONFIGS.items():
@@ -331,6 +331,21 @@ def test_partition_policy_and_workspace_size():
     # partition), and a 256-byte counter
     order = -(-B * n_part * 4 // 256) * 256 + 256
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, P, BF16, 0) == expect + order
+    # the library's own size on the sorted grid from 2048 tokens: the device may
+    # halve it, so the workspace covers the half (here 2048 -> 1024)
+    assert L.pa_decode_partition_size(B, Hq, 8, d, bs, MB, BF16, 0) == 2048
+    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 0, BF16, 0) == \
+        L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 1024, BF16, 0)
+    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 0, BF16, 0) > \
+        L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 2048, BF16, 0)
+    # below 2048 tokens, or off the sorted grid, the size is the one picked
+    assert L.pa_decode_partition_size(64, 32, 32, 128, 16, 128, F16, 0) == 1024
+    assert L.pa_decode_workspace_size(64, 32, 32, 128, 16, 128, 0, F16, 0) == \
+        L.pa_decode_workspace_size(64, 32, 32, 128, 16, 128, 1024, F16, 0)
+    assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 0, BF16, pa.NO_WORK_LIST) == \
+        L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 2048, BF16, pa.NO_WORK_LIST)
+    # one pass: none
+    assert L.pa_decode_workspace_size(4, 8, 8, 128, 16, 30, 0, BF16, 0) == 0
     # forced partition sizes must be multiples of the block size; invalid -> 0
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 24, BF16, 0) == 0
     assert L.pa_decode_partition_size(4, 3, 2, 128, 16, 8, BF16, 0) == ESHAPE

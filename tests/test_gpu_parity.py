@@ -242,6 +242,74 @@ def test_grid_modes_agree_bit_for_bit(kernel, dtype, hq, hkv, waves, P):
     _check_decode(modes[pa.SORTED_GRID], st.decode(0, threads=8), dtype)
 
 
+def _device_partition(lens, num_kv_heads, p, cus):
+    """The ordering kernel's refinement of the library's size p, as include/pa.h
+    states it: kept where the longest context is at most twice the mean, else
+    the largest of p / 2, p, 2p within a third of a compute unit's share of the
+    token x kv-head work (2p only while the longest context spans two
+    partitions and 2p <= 8192)."""
+    total, lmax, B = sum(lens), max(lens), len(lens)
+    if lmax <= 0 or lmax * B <= 2 * total:
+        return p
+    third = total * num_kv_heads // (3 * cus)
+    q = p // 2
+    if third >= p:
+        q = p
+    if third >= 2 * p and 4 * p <= lmax and 2 * p <= 8192:
+        q = 2 * p
+    return q
+
+
+def _lognormal(n, seed):
+    rng = np.random.default_rng(seed)
+    return [int(min(8192, max(1, round(float(np.exp(rng.normal(np.log(1024), 1)))))))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("case", ["skewed", "lognormal", "uniform"])
+def test_device_refined_partition(case):
+    """partition_size = 0 on the sorted grid from 2048 tokens: the ordering
+    kernel refines the library's size from the actual lengths.  The result is
+    bit-identical to the decode with that size passed explicitly, the same
+    through the order / ordered-decode / merge phases, and within tolerance of
+    the oracle.  Shapes: one 8192-token sequence among 63 short ones (refined
+    down), 256 lognormal contexts up to 8192 (up, on a 256-CU device), 16
+    equal 16k contexts (kept)."""
+    rng = np.random.default_rng(21)
+    lens = {"skewed": [int(x) for x in rng.integers(16, 257, 63)] + [8192],
+            "lognormal": _lognormal(256, 4),
+            "uniform": [16384] * 16}[case]
+    cfg = custom_config(f"refine-{case}", lens, 32, 8, 128, "bf16", 16, seed=31)
+    wl = Workload(cfg)
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    gs.write_step(0)
+    st.write_step(0)
+    MB = wl.max_blocks_per_seq
+    p = pa.decode_partition_size(cfg.num_seqs, 32, 8, 128, 16, MB, gs.kc.dtype)
+    assert p >= 2048 and pa.decode_grid(cfg.num_seqs, 32, 8, 128, 16, MB, 0, gs.kc.dtype,
+                                        gs.kc.dtype) == "sorted"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    want = _device_partition(lens, 8, p, cus)
+    _say(f"refined partition {case}: host {p}, expected device pick {want} ({cus} CUs)")
+    auto = _decode_nan_prefilled(gs, wl, 0, pa.AUTO)
+    explicit = _decode_nan_prefilled(gs, wl, want, pa.AUTO)
+    assert torch.isfinite(auto).all()
+    assert torch.equal(auto, explicit), f"differs from the decode at {want}"
+    # the same launch in phases: order (with the refinement), ordered decode, merge
+    c = wl.cfg
+    wsb = pa.decode_workspace_size(c.num_seqs, 32, 8, 128, 16, MB, 0, gs.kc.dtype)
+    ws = torch.full((wsb,), 0x5A, dtype=torch.uint8, device="cuda")
+    out = torch.full(gs.q[0].shape, float("nan"), device="cuda")
+    args = (out, gs.q[0], gs.kc, gs.vc, gs.block_tables, gs.ctx[0], c.attn_scale(), 16, 0, ws)
+    pa.decode_order(*args)
+    pa.decode_partitions(*args, pa.ORDERED)
+    pa.decode_merge(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(out, auto)
+    _check_decode(auto, st.decode(0, threads=16), "bf16")
+
+
 def _order_of_workspace(ws: torch.Tensor, B: int, Hq: int, D: int, n_parts: int) -> np.ndarray:
     """The item order a sorted-grid decode leaves in its workspace.  Internal
     layout (not part of the C ABI): (m, l) per (sequence, q head, partition),
