@@ -830,12 +830,20 @@ def run(args):
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = kv / (dec_ms * 1e-3) / 1e9
 
+    # the partition the timed launches used: the library's pick, or its
+    # refinement on the device from the actual lengths (partition_size 0)
+    p_used = int(p_eff)
+    if not part and Q == 1:
+        p_used = pa.decode_partition_used(ws, c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                          c.head_dim, c.block_size, wl.max_blocks_per_seq, kdt,
+                                          flags)
+
     graph = None
     if args.graph and Q == 1:
         graph = graph_steps(args, wl, kcs, vcs, sk, sv, qs, bt, out, ws, part, flags)
     ratio = None
     if args.one_pass_ratio and Q == 1:
-        ratio = one_pass_ratio(args, wl, kcs, vcs, qs, bt, ctx, out, ws, int(p_eff), flags)
+        ratio = one_pass_ratio(args, wl, kcs, vcs, qs, bt, ctx, out, ws, p_used, flags)
     attainable = None if args.no_stream_probe else stream_probe(dev)
     same_bytes = None if args.no_size_probe else size_matched_probe(dev, kv, len(kcs))
     traffic = None
@@ -862,7 +870,8 @@ def run(args):
         "accumulate": "f32",
         "data": "synthetic (seeded N(0,1) q/K/V, shuffled block pool; no dataset)",
         "config": {"workload": c.name, **{k: v for k, v in wl.describe().items() if k != "workload"},
-                   "partition_size": int(p_eff), "kernel_flags": args.flags,
+                   "partition_size": p_used, "partition_size_host_pick": int(p_eff),
+                   "kernel_flags": args.flags,
                    "queries_per_seq": Q,
                    "grid": pa.decode_grid(c.num_seqs * Q, c.num_q_heads, c.num_kv_heads,
                                           c.head_dim, c.block_size, wl.max_blocks_per_seq,

@@ -439,6 +439,21 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t max_blocks_per_seq, int32_t kv_dtype, uint32_t flags);
 
 /*
+ * The partition the last partition_size == 0 launch with these arguments used
+ * on `workspace` (the workspace it was given): the device's refinement where
+ * the launch refines (see pa_decode_partition_size), read back from the
+ * workspace with a copy on `stream` that the call waits for (a diagnostic, not
+ * for a hot loop), else pa_decode_partition_size's value.  Before any such
+ * launch on the workspace the value is pa_decode_partition_size's.  Negative
+ * pa_status for invalid arguments or a workspace too small for the launch.
+ */
+int32_t pa_decode_partition_used(const void* workspace, size_t workspace_bytes,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int32_t kv_dtype, uint32_t flags,
+                                 void* stream);
+
+/*
  * The decode kernel family pa_decode runs for these arguments:
  * PA_DECODE_FORCE_VALU (1) or PA_DECODE_FORCE_MFMA (2); a negative pa_status
  * for an unsupported combination.  The waves bits of flags are validated but

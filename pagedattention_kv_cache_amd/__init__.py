@@ -126,6 +126,8 @@ def lib() -> ctypes.CDLL:
                                          i32, f32, f32, vp]
         L.pa_decode_partition_size.restype = i32
         L.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, u32]
+        L.pa_decode_partition_used.restype = i32
+        L.pa_decode_partition_used.argtypes = [vp, sz, i32, i32, i32, i32, i32, i32, i32, u32, vp]
         L.pa_decode_workspace_size.restype = sz
         L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, u32]
         L.pa_advance_step.restype = ctypes.c_int
@@ -351,6 +353,19 @@ def decode_grid(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: in
                              _DTYPE[kv_dtype], flags)
     _check(min(r, 0))
     return GRID_NAMES[r]
+
+
+def decode_partition_used(workspace: torch.Tensor, num_seqs: int, num_q_heads: int,
+                          num_kv_heads: int, head_dim: int, block_size: int,
+                          max_blocks_per_seq: int, kv_dtype: torch.dtype, flags: int = AUTO) -> int:
+    """The partition the last partition_size = 0 decode on this workspace used
+    (the device's refinement where there is one; waits for the stream)."""
+    r = lib().pa_decode_partition_used(workspace.data_ptr(), workspace.nbytes, num_seqs,
+                                       num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, _DTYPE[kv_dtype], flags,
+                                       _stream(workspace.device))
+    _check(min(r, 0))
+    return r
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -565,6 +565,30 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   return workspace_bytes_for(s, device_partition(s, p) ? p / 2 : p);
 }
 
+int32_t pa_decode_partition_used(const void* workspace, size_t workspace_bytes,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int32_t kv_dtype, uint32_t flags,
+                                 void* stream) {
+  DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                kv_dtype, flags};
+  const int st = check_shape(s);
+  if (st != PA_OK) return st;
+  const int32_t p = pick_partition(s);
+  if (!device_partition(s, p)) return p;
+  const int64_t np = n_partitions(s, p / 2);
+  // the ordering kernel's words sit a 128-byte line after the ticket counter
+  const size_t off = order_offset(s, np) + round_up((size_t)num_seqs * (size_t)np * 4) + 128;
+  if (!workspace || workspace_bytes < off + 4 || workspace_bytes < workspace_bytes_for(s, p / 2))
+    return PA_ERR_WORKSPACE;
+  int32_t used = 0;
+  if (hipMemcpyAsync(&used, reinterpret_cast<const char*>(workspace) + off, 4,
+                     hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+      hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+    return PA_ERR_HIP;
+  return (used == p / 2 || used == p || used == 2 * p) ? used : p;
+}
+
 }  // extern "C"
 
 // ---- pa_decode_noalloc: the partition workspace in a static device array ----

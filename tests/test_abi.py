@@ -39,7 +39,7 @@ def test_library_loads_and_exports_header_symbols():
     L = pa.lib()
     names = _declared_functions()
     assert {"pa_cache_write", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
-            "pa_decode_workspace_size", "pa_decode_partition_size", "pa_decode_kernel",
+            "pa_decode_workspace_size", "pa_decode_partition_size", "pa_decode_partition_used", "pa_decode_kernel",
             "pa_decode_waves", "pa_decode_work_list",
             "pa_advance_step", "pa_status_string", "pa_abi_version"} <= set(names)
     for n in names:
@@ -346,6 +346,12 @@ def test_partition_policy_and_workspace_size():
         L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 2048, BF16, pa.NO_WORK_LIST)
     # one pass: none
     assert L.pa_decode_workspace_size(4, 8, 8, 128, 16, 30, 0, BF16, 0) == 0
+    # the partition a launch used: no device copy where nothing is refined (the
+    # host's pick); a refining shape needs its workspace
+    used = L.pa_decode_partition_used
+    assert used(None, 0, 64, 32, 32, 128, 16, 128, F16, 0, None) == 1024
+    assert used(None, 0, B, Hq, 8, d, bs, MB, BF16, 0, None) == EWS
+    assert used(None, 0, B, 30, 8, d, bs, MB, BF16, 0, None) == ESHAPE
     # forced partition sizes must be multiples of the block size; invalid -> 0
     assert L.pa_decode_workspace_size(B, Hq, 8, d, bs, MB, 24, BF16, 0) == 0
     assert L.pa_decode_partition_size(4, 3, 2, 128, 16, 8, BF16, 0) == ESHAPE

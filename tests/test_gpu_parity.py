@@ -307,6 +307,7 @@ def test_device_refined_partition(case):
     pa.decode_merge(*args)
     torch.cuda.synchronize()
     assert torch.equal(out, auto)
+    assert pa.decode_partition_used(ws, c.num_seqs, 32, 8, 128, 16, MB, gs.kc.dtype) == want
     _check_decode(auto, st.decode(0, threads=16), "bf16")
 
 
