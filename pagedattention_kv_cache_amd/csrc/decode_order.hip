@@ -42,11 +42,12 @@ __device__ __forceinline__ int seq_items(int L, int P, int np) {
 // unit's share of the token-heads (a CU runs three 4-wave workgroups, so an
 // item then takes at most about as long as the CU's whole share), 2c only
 // while the longest context still spans two partitions and 2c <= 8192.
-// Measured against the host's fixed pick (decode kernel): GQA lognormal batch
-// of 256 (share/3 ~ 4200) 2048 -> 4096, 1.2% faster; the same lengths over 64
-// sequences (share/3 ~ 1000) 2048 -> 1024, 3.5% faster; one 8192-token
-// sequence among 63 short ones 2048 -> 1024, 25% faster; uniform batches keep
-// the host's pick (4 x 32k at 4096, 16 x 16k at 4096, 64 x 4k-32k at 8192).
+// Measured against the host's pick alone: GQA lognormal batch of 256
+// (share/3 ~ 4200) 2048 -> 4096, decode kernel 259.1 -> 256.1 us; the same
+// lengths over 64 sequences (share/3 ~ 1000) 2048 -> 1024, 66.3 -> 65.5 us and
+// one 8192-token sequence among 63 short ones 2048 -> 1024, 38.4 -> 30.4 us
+// (ordering + decode); uniform batches keep the host's pick (4 x 32k and
+// 16 x 16k at 4096, 64 x 4k-32k at 8192) and their time.
 __device__ __forceinline__ int device_partition(const DecodeArgs& a, int64_t total, int lmax) {
   const int c = a.partition_size;
   const int64_t B = a.num_seqs;
