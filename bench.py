@@ -875,7 +875,8 @@ def run(args):
                    "queries_per_seq": Q,
                    "grid": pa.decode_grid(c.num_seqs * Q, c.num_q_heads, c.num_kv_heads,
                                           c.head_dim, c.block_size, wl.max_blocks_per_seq,
-                                          int(p_eff), qdt, kdt, flags),
+                                          int(p_eff), qdt, kdt,
+                                          flags | (pa.ORDERED if split else 0)),
                    "waves_per_item": pa.decode_waves(c.num_seqs, c.num_q_heads, c.num_kv_heads,
                                                      c.head_dim, c.block_size,
                                                      wl.max_blocks_per_seq, int(p_eff), qdt, kdt,

@@ -116,7 +116,12 @@ typedef enum pa_status {
  * back to grid order.  The library's pick (0): the sorted grid for
  * partitions of 1024 tokens or more; below that, the work list for batches
  * of up to 64 sequences and the sorted grid for larger ones (each where it
- * fits, else the other, else grid order). */
+ * fits, else the other, else grid order); except in a decode step's launches
+ * (pa_decode_step*, pa_decode_order, and a decode with PA_DECODE_ORDERED),
+ * which take the sorted grid wherever its order fits, their ordering riding
+ * on the launch that writes the step's tokens.  The plan queries
+ * (pa_decode_grid, pa_decode_work_list) give a step's grid when flags carry
+ * PA_DECODE_ORDERED; pa_decode_workspace_size covers either. */
 #define PA_DECODE_NO_WORK_LIST 16u
 #define PA_DECODE_SORTED_GRID 32u
 #define PA_DECODE_WORK_LIST 48u

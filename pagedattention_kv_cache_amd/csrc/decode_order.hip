@@ -20,8 +20,14 @@
 namespace pa {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kBins = kThreads;  // item sizes in 16-token chunks; larger ones share the last bin
+// One workgroup of 256 threads orders; in the write + order launch the other
+// workgroups write, 256 threads each, as the write kernel does.  With 1024
+// threads per workgroup (the order's histogram scan one bin per thread) the
+// write ran on a quarter as many CUs: the launch took 10.1-10.5 us at the GQA
+// lognormal and MHA batches, 5.8-6.0 us now (rocprofv3).
+constexpr int kThreads = 256;
+constexpr int kBins = 1024;  // item sizes in 16-token chunks; larger ones share the last bin
+constexpr int kBinsPerThread = kBins / kThreads;
 
 // Size bin of partition `part` of a sequence of L tokens: its 16-token chunks.
 __device__ __forceinline__ int item_bin(int L, int part, int P) {
@@ -111,12 +117,19 @@ __device__ __forceinline__ void order_items(const DecodeArgs& a, int32_t* order)
     for (int p = 0; p < n; ++p) atomicAdd(&hist[L <= 0 ? 0 : item_bin(L, p, P)], 1);
   }
   __syncthreads();
-  // start[bin] = items in larger bins: thread tid takes bin kBins - 1 - tid,
-  // so an inclusive prefix sum over the threads counts the tid + 1 largest
-  // bins; within a wave by lane shuffles, across waves through LDS.
+  // start[bin] = items in larger bins.  Thread tid takes the bins at
+  // positions kBinsPerThread * tid .. + kBinsPerThread - 1 of the descending
+  // order (bin kBins - 1 - position), so an inclusive prefix sum of the
+  // threads' totals counts the largest bins up to its own; within a wave by
+  // lane shuffles, across waves through LDS.
   __shared__ int wave_sum[kThreads / 64];
   const int lane = tid & 63, wave = tid >> 6;
-  const int own = hist[kBins - 1 - tid];
+  int cnt[kBinsPerThread], own = 0;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) {
+    cnt[i] = hist[kBins - 1 - (kBinsPerThread * tid + i)];
+    own += cnt[i];
+  }
   int v = own;
 #pragma unroll
   for (int off = 1; off < 64; off *= 2) {
@@ -126,7 +139,12 @@ __device__ __forceinline__ void order_items(const DecodeArgs& a, int32_t* order)
   if (lane == 63) wave_sum[wave] = v;
   __syncthreads();
   for (int w = 0; w < wave; ++w) v += wave_sum[w];
-  start[kBins - 1 - tid] = v - own;
+  int run = v - own;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) {
+    start[kBins - 1 - (kBinsPerThread * tid + i)] = run;
+    run += cnt[i];
+  }
   __syncthreads();
   const int total = start[0] + hist[0];
   __syncthreads();

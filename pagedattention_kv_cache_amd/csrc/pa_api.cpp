@@ -237,8 +237,15 @@ constexpr int32_t kPersistentOrderMin = 1024;
 // tokens 43.4 -> 40.0, MHA batch of 64 at 512 190.9 -> 188.7 and at 256
 // 193.5 -> 191.1; GQA batch of 256 at 512 301.1 -> 309.9.
 constexpr int32_t kListMaxSeqs = 64;
-
-int grid_mode(const DecodeShape& s, int32_t p) {
+//
+// A decode step's launches (pa_decode_step, pa_decode_order and the decode
+// with PA_DECODE_ORDERED) order the items in the launch that writes the step's
+// tokens, which the step pays for anyway, so there the sorted grid is taken
+// for small batches too: the decode kernel then skips the list every
+// workgroup builds.  Measured (skewed batch of 32 at 512 tokens, rocprofv3):
+// decode kernel 34.9-35.1 -> 33.2-34.2 us, the write + order launch as long
+// as the write alone.
+int grid_mode(const DecodeShape& s, int32_t p, bool step = false) {
   const int64_t np = n_partitions(s, p);
   if (np <= 1) return kGridNatural;
   const bool list_fits = pa::work_list_lds_ints(s.num_seqs, (int)np) <= kMaxListInts;
@@ -249,14 +256,18 @@ int grid_mode(const DecodeShape& s, int32_t p) {
     case PA_DECODE_WORK_LIST: return list_fits ? kGridList : kGridNatural;
     default: break;
   }
-  if (order_fits && p >= kPersistentOrderMin) return kGridSorted;
+  if (order_fits && (p >= kPersistentOrderMin || step)) return kGridSorted;
   if (list_fits && s.num_seqs <= kListMaxSeqs) return kGridList;
   if (order_fits) return kGridSorted;
   return list_fits ? kGridList : kGridNatural;
 }
 
-int32_t work_list_ints(const DecodeShape& s, int32_t p) {
-  if (grid_mode(s, p) != kGridList) return 0;
+// A step's launch: PA_DECODE_ORDERED in the flags (the plan queries take it
+// to mean the step's grid).
+bool step_flags(const DecodeShape& s) { return (s.flags & PA_DECODE_ORDERED) != 0; }
+
+int32_t work_list_ints(const DecodeShape& s, int32_t p, bool step = false) {
+  if (grid_mode(s, p, step) != kGridList) return 0;
   const int64_t np = n_partitions(s, p);
   const int64_t ints = pa::work_list_lds_ints(s.num_seqs, (int)np);
   return (int32_t)((ints + 3) & ~3);  // keep the merge area 16-byte aligned
@@ -276,7 +287,9 @@ size_t workspace_bytes_for(const DecodeShape& s, int32_t p) {
   const int64_t np = n_partitions(s, p);
   if (np <= 1) return 0;
   size_t bytes = order_offset(s, np);
-  if (grid_mode(s, p) == kGridSorted)
+  // the order (and its counter) wherever the launch may sort: a step sorts
+  // where a plain decode would walk the work list, with the same workspace
+  if (grid_mode(s, p) == kGridSorted || grid_mode(s, p, true) == kGridSorted)
     bytes += round_up((size_t)s.num_seqs * (size_t)np * sizeof(int32_t)) + kAlign;  // + counter
   return bytes;
 }
@@ -535,7 +548,7 @@ int32_t pa_decode_work_list(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
                 kv_dtype, flags};
   int32_t p = 0;
   const int32_t st = plan_args(s, partition_size, q_dtype, &p);
-  return st != PA_OK ? st : (work_list_ints(s, p) > 0 ? 1 : 0);
+  return st != PA_OK ? st : (work_list_ints(s, p, step_flags(s)) > 0 ? 1 : 0);
 }
 
 int32_t pa_decode_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -546,7 +559,7 @@ int32_t pa_decode_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   int32_t p = 0;
   const int32_t st = plan_args(s, partition_size, q_dtype, &p);
   if (st != PA_OK) return st;
-  switch (grid_mode(s, p)) {
+  switch (grid_mode(s, p, step_flags(s))) {
     case kGridSorted: return PA_DECODE_SORTED_GRID;
     case kGridList: return PA_DECODE_WORK_LIST;
     default: return PA_DECODE_NO_WORK_LIST;
@@ -726,8 +739,10 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.out_dtype = out_dtype;
   a.waves = pick_waves(s, p);
   // one grid decision for the workspace and the launch (both on the query rows' shape)
-  const int mode = grid_mode(rows_shape, p_min);
-  a.list_ints = mode == kGridList ? work_list_ints(rows_shape, p_min) : 0;
+  // a step's launches (its write, its ordering, the decode after them) sort
+  const bool step = pre_write || phase == kOrder || preordered;
+  const int mode = grid_mode(rows_shape, p_min, step);
+  a.list_ints = mode == kGridList ? work_list_ints(rows_shape, p_min, step) : 0;
   a.order = mode == kGridSorted
                 ? reinterpret_cast<const int32_t*>(ws + order_offset(rows_shape, np))
                 : nullptr;

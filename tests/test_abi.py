@@ -285,6 +285,14 @@ def test_waves_flags():
     assert L.pa_decode_grid(64, 32, 8, 128, 16, 512, 1024, BF16, BF16, 0) == S
     assert L.pa_decode_grid(32, 40, 40, 128, 16, 256, 512, F16, F16, 0) == W    # skewed batch
     assert L.pa_decode_work_list(32, 40, 40, 128, 16, 256, 512, F16, F16, 0) == 1
+    # a step's launches sort wherever the order fits (PA_DECODE_ORDERED asks for them)
+    assert L.pa_decode_grid(32, 40, 40, 128, 16, 256, 512, F16, F16, pa.ORDERED) == S
+    assert L.pa_decode_work_list(32, 40, 40, 128, 16, 256, 512, F16, F16, pa.ORDERED) == 0
+    assert L.pa_decode_grid(32, 40, 40, 128, 16, 256, 512, F16, F16, pa.ORDERED | W) == W
+    # the workspace covers the step's order too
+    ws_step = L.pa_decode_workspace_size(32, 40, 40, 128, 16, 256, 512, F16, 0)
+    ws_list = L.pa_decode_workspace_size(32, 40, 40, 128, 16, 256, 512, F16, W)
+    assert ws_step == ws_list + -(-32 * 8 * 4 // 256) * 256 + 256
     assert L.pa_decode_grid(*args[:6], 2048, BF16, BF16, 0) == S                # 4 partitions
     assert L.pa_decode_grid(*args[:6], 8192, BF16, BF16, 0) == G                # one pass
     assert L.pa_decode_grid(*args[:6], 8192, BF16, BF16, W) == G
