@@ -761,10 +761,9 @@ def run(args):
             pa.decode_step_partitions(sk[s], sv[s], slots[s], out, qs[s], k_l, v_l, bt, ctx[s],
                                       scale, c.block_size, part, ws, flags)
         elif split:
-            if c.kv_dtype == "fp8":  # a quantizing write of its own, then the order
-                write_kv(c, sk[s], sv[s], slots[s], k_l, v_l)
-                pa.decode_order(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
-                                flags)
+            if c.kv_dtype == "fp8":  # the quantizing write and the order
+                pa.decode_order_fp8(out, qs[s], k_l, v_l, bt, ctx[s], scale, *c.fp8_scales,
+                                    c.block_size, part, ws, flags, sk[s], sv[s], slots[s])
             else:
                 pa.decode_order(out, qs[s], k_l, v_l, bt, ctx[s], scale, c.block_size, part, ws,
                                 flags, k=sk[s], v=sv[s], slot_mapping=slots[s])

@@ -338,6 +338,29 @@ int pa_decode_order(const void* k, const void* v, const int64_t* slot_mapping, i
                     void* stream);
 
 /*
+ * pa_decode_order_fp8 -- pa_decode_order for E4M3 caches: the quantizing
+ * write of the step's new tokens (as pa_cache_write_fp8: source rows of
+ * src_dtype f32, f16 or bf16, stored value e4m3(x / k_scale) and
+ * e4m3(x / v_scale)) and the ordering of the decode's items in one launch.
+ * A following pa_decode_fp8_partitions (or pa_decode_fp8) with the same
+ * arguments and flags | PA_DECODE_ORDERED launches the decode kernel alone;
+ * caches and results equal pa_cache_write_fp8 followed by pa_decode_fp8 bit
+ * for bit.  The caches are E4M3 (kv_dtype is implied); k_scale and v_scale
+ * are the caches' scales, as the decode takes them.  Errors as
+ * pa_cache_write_fp8 for the write's arguments, as pa_decode_fp8 for the rest.
+ */
+int pa_decode_order_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                        int64_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
+                        int32_t src_dtype, float k_scale, float v_scale, void* out,
+                        const void* q, void* k_cache, void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, float scale,
+                        int32_t block_size, int32_t partition_size, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
+                        int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, void* stream);
+
+/*
  * pa_decode_mq / pa_decode_mq_partitions / pa_decode_mq_merge -- decode of
  * several query tokens per sequence ("vLLM Project Update" talk, roadmap:
  * multi-query attention kernels for speculative decoding, which score the

@@ -116,6 +116,10 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_noalloc.restype = ctypes.c_int
         L.pa_decode_noalloc.argtypes = dec_args[:18] + [u32, vp]
         step_args = [vp, vp, vp, i64, i64, i64] + dec_args
+        L.pa_decode_order_fp8.restype = ctypes.c_int
+        L.pa_decode_order_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i32, f32, f32, vp, vp, vp, vp,
+                                          vp, vp, f32, i32, i32, i32, i32, i32, i32, i64, i32,
+                                          i32, i32, vp, sz, u32, vp]
         for name in ("pa_decode_step", "pa_decode_step_partitions", "pa_decode_order"):
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name).argtypes = step_args
@@ -565,6 +569,36 @@ def decode_order(out, q, k_cache, v_cache, block_tables, context_lens, scale, bl
         v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
         block_size, partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(k_cache), _dt(out),
         ws_ptr, ws_bytes, flags, _stream(q.device)))
+
+
+def decode_order_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                     v_scale, block_size, partition_size, workspace, flags, k, v,
+                     slot_mapping) -> None:
+    """decode_order for E4M3 caches: the quantizing write of k, v (f32 / f16 /
+    bf16 rows) at slot_mapping with the caches' scales, and the item ordering,
+    in one launch; decode_fp8_partitions with flags | ORDERED then launches the
+    decode kernel alone."""
+    B, Hq, d, NB, Hkv, bs, MB = _decode_dims(out, q, k_cache, v_cache, block_tables,
+                                             context_lens, block_size)
+    kshape = k.shape
+    if len(kshape) != 3 or v.shape != kshape or kshape[1] != Hkv or kshape[2] != d:
+        raise PAError(-2, "k, v must be [T][Hkv][d] matching the caches")
+    T = kshape[0]
+    if k.stride(2) != 1 or k.stride(1) != d or v.stride(2) != 1 or v.stride(1) != d:
+        raise PAError(-2, "heads of a token must be packed")
+    if (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,)
+            or not slot_mapping.is_contiguous()):
+        raise PAError(-2, "slot_mapping must be contiguous int64 [T]")
+    if k.dtype != v.dtype:
+        raise PAError(-2, "dtype mismatch")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    _check((_lib or lib()).pa_decode_order_fp8(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), T, k.stride(0), v.stride(0), _dt(k),
+        float(k_scale), float(v_scale), out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+        block_size, partition_size, B, Hq, Hkv, d, NB, MB, _dt(q), _dt(out), ws_ptr, ws_bytes,
+        flags, _stream(q.device)))
 
 
 def decode_step_partitions(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables,

@@ -180,6 +180,20 @@ __global__ __launch_bounds__(kThreads) void decode_prologue_kernel(DecodeArgs a,
   }
 }
 
+// The same with the quantizing write into E4M3 caches (source type SRC).
+template <Elem SRC>
+__global__ __launch_bounds__(kThreads) void decode_prologue_fp8_kernel(DecodeArgs a,
+                                                                       int32_t* order,
+                                                                       CacheWriteArgs w,
+                                                                       int chunks_per_row) {
+  if (blockIdx.x == 0) {
+    order_items(a, order);
+  } else {
+    cache_write_fp8_chunk<SRC>(w, (int64_t)(blockIdx.x - 1) * kThreads + threadIdx.x,
+                               chunks_per_row);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_order(const DecodeArgs& a, int32_t* order, const CacheWriteArgs* write,
@@ -188,11 +202,30 @@ hipError_t launch_decode_order(const DecodeArgs& a, int32_t* order, const CacheW
     hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kThreads), 0, s, a, order);
     return hipGetLastError();
   }
-  const int chunks = write->head_dim * write->elem_bytes / 16;
+  // E4M3: one thread per 16 elements; else per 16 bytes
+  const int chunks = write->elem_bytes == 1 ? write->head_dim / 16
+                                            : write->head_dim * write->elem_bytes / 16;
   const int64_t total = write->num_tokens * write->num_kv_heads * chunks;
   const int64_t blocks = 1 + (total + kThreads - 1) / kThreads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (write->elem_bytes == 4) {
+  if (write->elem_bytes == 1) {
+    switch (write->src_dtype) {
+      case 0:
+        hipLaunchKernelGGL(decode_prologue_fp8_kernel<Elem::F32>, dim3((unsigned)blocks),
+                           dim3(kThreads), 0, s, a, order, *write, chunks);
+        break;
+      case 1:
+        hipLaunchKernelGGL(decode_prologue_fp8_kernel<Elem::F16>, dim3((unsigned)blocks),
+                           dim3(kThreads), 0, s, a, order, *write, chunks);
+        break;
+      case 2:
+        hipLaunchKernelGGL(decode_prologue_fp8_kernel<Elem::BF16>, dim3((unsigned)blocks),
+                           dim3(kThreads), 0, s, a, order, *write, chunks);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (write->elem_bytes == 4) {
     hipLaunchKernelGGL(decode_prologue_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        a, order, *write, chunks);
   } else {

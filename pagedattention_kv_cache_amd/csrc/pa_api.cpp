@@ -368,7 +368,58 @@ int write_args(const void* k, const void* v, const int64_t* slot_mapping, void* 
   a->elem_bytes = eb;
   a->k_scale = 1.0f;
   a->v_scale = 1.0f;
+  a->src_dtype = dtype;
   return PA_OK;
+}
+
+// Validation and arguments of a quantizing write into E4M3 caches
+// (pa_cache_write_fp8): source rows of src_dtype, per-tensor scales.
+int write_args_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int64_t num_tokens, int64_t k_token_stride,
+                   int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
+                   int64_t num_blocks, int32_t block_size, int32_t src_dtype, float k_scale,
+                   float v_scale, pa::CacheWriteArgs* a) {
+  if (src_dtype != PA_DTYPE_F32 && src_dtype != PA_DTYPE_F16 && src_dtype != PA_DTYPE_BF16)
+    return PA_ERR_DTYPE;
+  const int eb = elem_bytes(src_dtype);
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || k_scale > 3.0e38f || v_scale > 3.0e38f)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (!valid_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row) return PA_ERR_SHAPE;
+  if ((k_token_stride * eb) % 16 || (v_token_stride * eb) % 16) return PA_ERR_SHAPE;
+  if (num_tokens > 0) {
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+      return PA_ERR_SHAPE;
+    const int64_t threads = num_tokens * num_kv_heads * ((int64_t)head_dim / 16);
+    if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
+  }
+  a->k = k;
+  a->v = v;
+  a->slots = slot_mapping;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->num_tokens = num_tokens;
+  a->num_blocks = num_blocks;
+  a->k_stride = k_token_stride;
+  a->v_stride = v_token_stride;
+  a->num_kv_heads = num_kv_heads;
+  a->head_dim = head_dim;
+  a->block_size = block_size;
+  a->elem_bytes = 1;
+  a->k_scale = k_scale;
+  a->v_scale = v_scale;
+  a->src_dtype = src_dtype;
+  return PA_OK;
+}
+
+// A cache write on its own launch: quantizing into E4M3 caches, else a copy.
+hipError_t launch_write(const pa::CacheWriteArgs& w, hipStream_t s) {
+  return w.elem_bytes == 1 ? pa::launch_cache_write_fp8(w, w.src_dtype, s)
+                           : pa::launch_cache_write(w, s);
 }
 
 }  // namespace
@@ -392,39 +443,11 @@ int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping
                        int64_t v_token_stride, int32_t num_kv_heads, int32_t head_dim,
                        int64_t num_blocks, int32_t block_size, int32_t src_dtype, float k_scale,
                        float v_scale, void* stream) {
-  if (src_dtype != PA_DTYPE_F32 && src_dtype != PA_DTYPE_F16 && src_dtype != PA_DTYPE_BF16)
-    return PA_ERR_DTYPE;
-  const int eb = elem_bytes(src_dtype);
-  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
-  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || k_scale > 3.0e38f || v_scale > 3.0e38f)
-    return PA_ERR_SHAPE;
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
-  if (!valid_block_size(block_size)) return PA_ERR_UNSUPPORTED;
-  const int64_t row = (int64_t)num_kv_heads * head_dim;
-  if (k_token_stride < row || v_token_stride < row) return PA_ERR_SHAPE;
-  if ((k_token_stride * eb) % 16 || (v_token_stride * eb) % 16) return PA_ERR_SHAPE;
-  if (num_tokens == 0) return PA_OK;
-  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
-    return PA_ERR_SHAPE;
-  const int64_t threads = num_tokens * num_kv_heads * ((int64_t)head_dim / 16);
-  if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
   pa::CacheWriteArgs a;
-  a.k = k;
-  a.v = v;
-  a.slots = slot_mapping;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.num_tokens = num_tokens;
-  a.num_blocks = num_blocks;
-  a.k_stride = k_token_stride;
-  a.v_stride = v_token_stride;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.elem_bytes = 1;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
+  const int st = write_args_fp8(k, v, slot_mapping, k_cache, v_cache, num_tokens, k_token_stride,
+                                v_token_stride, num_kv_heads, head_dim, num_blocks, block_size,
+                                src_dtype, k_scale, v_scale, &a);
+  if (st != PA_OK || num_tokens == 0) return st;
   return pa::launch_cache_write_fp8(a, src_dtype, (hipStream_t)stream) == hipSuccess ? PA_OK
                                                                                       : PA_ERR_HIP;
 }
@@ -676,7 +699,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (!kernel) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) {  // nothing to attend; a step's cache write still runs
     if (pre_write && pre_write->num_tokens > 0 && (phase & (kPartitions | kOrder)))
-      return pa::launch_cache_write(*pre_write, (hipStream_t)stream) == hipSuccess ? PA_OK
+      return launch_write(*pre_write, (hipStream_t)stream) == hipSuccess ? PA_OK
                                                                                   : PA_ERR_HIP;
     return PA_OK;
   }
@@ -766,7 +789,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       if (pa::launch_decode_order(a, const_cast<int32_t*>(a.order), pre_write, hs) != hipSuccess)
         return PA_ERR_HIP;
     } else if (pre_write && pre_write->num_tokens > 0 &&
-               pa::launch_cache_write(*pre_write, hs) != hipSuccess) {
+               launch_write(*pre_write, hs) != hipSuccess) {
       return PA_ERR_HIP;
     }
     return PA_OK;
@@ -777,7 +800,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       if (pa::launch_decode_order(a, const_cast<int32_t*>(a.order), pre_write, hs) != hipSuccess)
         return PA_ERR_HIP;
     } else if (!a.order && pre_write && pre_write->num_tokens > 0 &&
-               pa::launch_cache_write(*pre_write, hs) != hipSuccess) {
+               launch_write(*pre_write, hs) != hipSuccess) {
       return PA_ERR_HIP;
     }
     const hipError_t e = mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, hs)
@@ -867,6 +890,27 @@ int pa_decode_step_partitions(PA_STEP_PARAMS) {
 int pa_decode_order(PA_STEP_PARAMS) {
   return step_impl(k, v, slot_mapping, num_tokens, k_token_stride, v_token_stride, PA_DECODE_ARGS,
                    kOrder);
+}
+
+int pa_decode_order_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                        int64_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
+                        int32_t src_dtype, float k_scale, float v_scale, void* out,
+                        const void* q, void* k_cache, void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, float scale,
+                        int32_t block_size, int32_t partition_size, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int64_t num_blocks, int32_t max_blocks_per_seq, int32_t q_dtype,
+                        int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, void* stream) {
+  pa::CacheWriteArgs w;
+  const int st = write_args_fp8(k, v, slot_mapping, k_cache, v_cache, num_tokens, k_token_stride,
+                                v_token_stride, num_kv_heads, head_dim, num_blocks, block_size,
+                                src_dtype, k_scale, v_scale, &w);
+  if (st != PA_OK) return st;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                     partition_size, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, q_dtype, PA_DTYPE_FP8_E4M3, out_dtype, workspace,
+                     workspace_bytes, flags, stream, kOrder, k_scale, v_scale, 1, &w);
 }
 
 #define PA_DECODE_FP8_PARAMS                                                                   \

@@ -21,9 +21,10 @@ struct CacheWriteArgs {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t block_size;
-  int32_t elem_bytes;
+  int32_t elem_bytes;  // of the cache: 1 for E4M3 (a quantizing write from src_dtype)
   float k_scale;  // E4M3 caches: stored value = x / scale
   float v_scale;
+  int32_t src_dtype;  // E4M3 caches: the source rows' pa_dtype (f32, f16 or bf16)
 };
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);

@@ -39,7 +39,8 @@ def test_library_loads_and_exports_header_symbols():
     L = pa.lib()
     names = _declared_functions()
     assert {"pa_cache_write", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
-            "pa_decode_workspace_size", "pa_decode_partition_size", "pa_decode_partition_used", "pa_decode_kernel",
+            "pa_decode_workspace_size", "pa_decode_partition_size", "pa_decode_partition_used",
+            "pa_decode_order_fp8", "pa_decode_kernel",
             "pa_decode_waves", "pa_decode_work_list",
             "pa_advance_step", "pa_status_string", "pa_abi_version"} <= set(names)
     for n in names:
@@ -632,6 +633,36 @@ def test_decode_step_validation(kw, status):
 ])
 def test_decode_order_validation(kw, status):
     assert _step(fn="pa_decode_order", **kw) == status
+
+
+def _order_fp8(**kw):
+    a = dict(k=FAKE, v=FAKE, slots=FAKE, T=4, ks=1024, vs=1024, src=BF16, ksc=0.25, vsc=0.5,
+             out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, bs=16, P=0, B=4,
+             Hq=32, Hkv=8, d=128, NB=100, MB=64, qd=BF16, od=F32, ws=None, wsb=0,
+             flags=pa.FORCE_VALU)
+    a.update(kw)
+    return pa.lib().pa_decode_order_fp8(
+        a["k"], a["v"], a["slots"], a["T"], a["ks"], a["vs"], a["src"], a["ksc"], a["vsc"],
+        a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["bs"], a["P"],
+        a["B"], a["Hq"], a["Hkv"], a["d"], a["NB"], a["MB"], a["qd"], a["od"], a["ws"], a["wsb"],
+        a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=FP8), EDTYPE),                   # the write's source: f32 / f16 / bf16
+    (dict(ksc=0.0), ESHAPE),                   # scales must be positive and finite
+    (dict(vsc=float("inf")), ESHAPE),
+    (dict(ks=100), ESHAPE),
+    (dict(k=None), ENULL),
+    (dict(T=-1), ESHAPE),
+    (dict(Hq=30), ESHAPE),                     # the decode's arguments
+    (dict(qd=FP8), EDTYPE),                    # queries are f32, f16 or bf16
+    (dict(ws=None, wsb=0, P=256), EWS),        # the order lives in the workspace
+    (dict(flags=128), EUNSUP),
+    (dict(T=0, B=0, out=None, q=None, bt=None, cl=None), OK),   # nothing to do
+])
+def test_decode_order_fp8_validation(kw, status):
+    assert _order_fp8(**kw) == status
 
 
 def test_ordered_flag_is_known_and_refused_for_multi_query():

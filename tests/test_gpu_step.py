@@ -170,3 +170,51 @@ def test_order_then_ordered_decode_fp8_and_refusals():
     assert e.value.status == -4
     torch.cuda.synchronize()
     assert torch.isnan(out2).all()
+
+
+FP8_ORDER_CASES = [
+    # lens, partition, grid flags
+    ([3, 700, 1500, 2600], 1024, pa.AUTO),                       # sorted, counter deal
+    ([3, 700, 1500, 2600, 90, 40], 256, pa.AUTO),                 # a step sorts (static deal)
+    ([3, 700, 1500, 2600, 90, 40], 256, pa.WORK_LIST),            # the write on its own
+    ([7, 90, 200], 0, pa.AUTO),                                   # one pass: the write alone
+    ([int(x) for x in np.random.default_rng(3).integers(16, 257, 63)] + [8192], 0,
+     pa.AUTO),                                                    # the device refines
+]
+
+
+@pytest.mark.parametrize("case", FP8_ORDER_CASES,
+                         ids=lambda c: f"{len(c[0])}seqs-P{c[1]}-flags{c[2]}")
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_order_fp8_with_write_equals_write_then_decode(case, src):
+    """pa_decode_order_fp8 (the quantizing write and the item order in one
+    launch), then the ordered decode and the merge: caches and outputs
+    bit-identical to pa_cache_write_fp8 followed by pa_decode_fp8, from the same
+    prior caches; the source rows in f32 as well as the query dtype."""
+    lens, P, flags = case
+    cfg = custom_config("order-fp8-write", lens, 32, 8, 128, "bf16", 16, seed=14,
+                        cache_dtype="fp8", fp8_scales=(2.0 ** -6, 2.0 ** -5))
+    wl = Workload(cfg)
+    c = cfg
+    ks, vs = c.fp8_scales
+    ref, got = GpuState(wl), GpuState(wl)
+    k = ref.step_k[0].float() if src == "f32" else ref.step_k[0]
+    v = ref.step_v[0].float() if src == "f32" else ref.step_v[0]
+    _say(f"order_fp8 {len(lens)} seqs P={P} flags={flags} src={src}")
+    MB = wl.max_blocks_per_seq
+    a = torch.full(ref.q[0].shape, float("nan"), device="cuda")
+    pa.cache_write_fp8(k, v, ref.step_slots[0], ref.kc, ref.vc, ks, vs)
+    pa.decode_fp8(a, ref.q[0], ref.kc, ref.vc, ref.block_tables, ref.ctx[0], c.attn_scale(), ks,
+                  vs, 16, P, None, flags)
+    need = pa.decode_workspace_size(c.num_seqs, 32, 8, 128, 16, MB, P, got.kc.dtype, flags)
+    ws = torch.full((max(need, 256),), 0x5A, dtype=torch.uint8, device="cuda")
+    b = torch.full(got.q[0].shape, float("nan"), device="cuda")
+    args = (b, got.q[0], got.kc, got.vc, got.block_tables, got.ctx[0], c.attn_scale())
+    pa.decode_order_fp8(*args, ks, vs, 16, P, ws, flags, k, v, got.step_slots[0])
+    pa.decode_fp8_partitions(*args, ks, vs, 16, P, ws, flags | pa.ORDERED)
+    pa.decode_merge(*args, 16, P, ws, flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_bits(ref.kc.cpu()), raw_bits(got.kc.cpu())), "key caches differ"
+    assert np.array_equal(raw_bits(ref.vc.cpu()), raw_bits(got.vc.cpu())), "value caches differ"
+    assert torch.isfinite(b).all()
+    assert torch.equal(a, b)
