@@ -143,7 +143,7 @@ def _is_write(k):
 
 
 def _is_prologue(k):
-    return "decode_prologue_kernel" in k
+    return "decode_prologue" in k
 
 
 def _step_values(rows, counter, pred):
@@ -211,7 +211,7 @@ def summarize_pmc(args):
             "write_bytes": statistics.median(ww) * 1024.0 * w_scale,
         }
         cw = res["cache_write"]
-        cw["kernel"] = "decode_prologue_kernel" if write_kernel is _is_prologue else \
+        cw["kernel"] = "decode_prologue (write + order)" if write_kernel is _is_prologue else \
             "cache_write_kernel"
         cw["write_over_cache_bytes"] = cw["write_bytes"] / cw["cache_bytes"]
     path = TRAFFIC_FILE.format(workload=cfg.name)
