@@ -19,8 +19,8 @@ import oracle
 import pagedattention_kv_cache_amd as pa
 from pagedattention_kv_cache_amd.workloads import (CONFIGS, Workload, config3_long_first,
                                                    custom_config, raw_bits)
-from tests.gpu_harness import (GpuState, assert_rejected, componentwise_rel_err, max_abs_err,
-                               oracle_state_empty, rowwise_rel_err)
+from tests.gpu_harness import (GpuState, assert_rejected, componentwise_rel_err, decode_kv,
+                               max_abs_err, oracle_state_empty, rowwise_rel_err, write_kv)
 from tests.paged_host import OracleState, abs_values
 
 pytestmark = pytest.mark.gpu
@@ -589,6 +589,60 @@ def test_block_permutation_bit_identical(kernel):
               cfg.block_size, 0, flags=KERNELS[kernel])
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_blocks_past_4_gib_of_the_pool(kernel, cache):
+    """Each cache a little over 4 GiB, the sequences' blocks on both sides of the
+    2 GiB and 4 GiB byte offsets and spread over the rest: addresses that need 64
+    bits.  The step's write there equals the write into the small pool bit for bit,
+    and the decode there equals the small pool's decode bit for bit (the block
+    permutation invariant), which is itself within tolerance of the oracle."""
+    fp8 = cache == "fp8"
+    cfg = custom_config("far", [33, 300, 1000], 8, 2, 128, "bf16", 16, seed=48,
+                        cache_dtype="fp8" if fp8 else "",
+                        fp8_scales=(2.0 ** -6, 2.0 ** -5) if fp8 else (1.0, 1.0))
+    wl = Workload(cfg)
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    NB, bs = wl.num_blocks, cfg.block_size
+    block_bytes = gs.kc[0].numel() * gs.kc.element_size()
+    assert block_bytes == gs.vc[0].numel() * gs.vc.element_size()
+    lo, edge = (1 << 31) // block_bytes, (1 << 32) // block_bytes
+    nb_far = edge + 3 * NB
+    spread = torch.randperm(3 * NB - 1, generator=torch.Generator().manual_seed(5))[: NB - 4]
+    ids = torch.cat([torch.tensor([lo - 1, lo, edge - 1, edge]), edge + 1 + spread]).cuda()
+    assert ids.unique().numel() == NB and int(ids.max()) < nb_far
+    _say(f"far pool: {nb_far} blocks of {block_bytes} B per cache, cache {cache}, {kernel}")
+    kf = torch.empty((nb_far,) + tuple(gs.kc.shape[1:]), dtype=gs.kc.dtype, device="cuda")
+    vf = torch.empty((nb_far,) + tuple(gs.vc.shape[1:]), dtype=gs.vc.dtype, device="cuda")
+    kf.view(torch.uint8)[ids] = gs.kc.view(torch.uint8)  # the prior context, moved
+    vf.view(torch.uint8)[ids] = gs.vc.view(torch.uint8)
+
+    slots = gs.step_slots[0].long()
+    s0 = slots.clamp(min=0)
+    far_slots = torch.where(slots >= 0, ids[s0 // bs] * bs + s0 % bs, slots)
+    write_kv(cfg, gs.step_k[0], gs.step_v[0], far_slots, kf, vf)
+    gs.write_step(0)
+    st.write_step(0)
+    torch.cuda.synchronize()
+    _pools_equal(gs, st)
+    assert torch.equal(kf.view(torch.uint8)[ids], gs.kc.view(torch.uint8))
+    assert torch.equal(vf.view(torch.uint8)[ids], gs.vc.view(torch.uint8))
+
+    bt = gs.block_tables.long()
+    bt_far = torch.where(bt >= 0, ids[bt.clamp(min=0)], bt).to(torch.int32).contiguous()
+    ref = st.decode(0)
+    for p in (0, 256):
+        out = gs.decode(0, partition_size=p, flags=KERNELS[kernel])
+        out_far = torch.empty_like(out)
+        decode_kv(cfg, out_far, gs.q[0], kf, vf, bt_far, gs.ctx[0], p, flags=KERNELS[kernel])
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_far), f"partition {p}"
+        _check_decode(out_far, ref, "bf16")
+    del kf, vf
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
