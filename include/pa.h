@@ -229,7 +229,8 @@ int pa_advance_step(int32_t num_seqs, int32_t num_queries, int32_t block_size,
  *                  tokens (a multiple of block_size), merged by a
  *                  log-sum-exp reduction; a value >= max_blocks_per_seq *
  *                  block_size means one pass per (sequence, kv head) with no
- *                  reduction and no workspace
+ *                  reduction and no workspace; at most 65535 partitions of
+ *                  max_blocks_per_seq * block_size (PA_ERR_SHAPE beyond)
  *   head_dim       64 or 128;  num_q_heads % num_kv_heads == 0
  *   workspace      device scratch of at least pa_decode_workspace_size(...)
  *                  bytes for the same arguments (may be NULL when that is 0),

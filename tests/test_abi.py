@@ -156,6 +156,7 @@ def _dec(**kw):
     (dict(ws=None, wsb=0), EWS),           # four partitions of 256 need a workspace
     (dict(ws=FAKE, wsb=1024), EWS),        # too small
     (dict(ws=FAKE + 8, wsb=1 << 30), EWS),  # misaligned
+    (dict(P=16, MB=65536, ws=FAKE, wsb=1 << 40), ESHAPE),  # 65536 partitions of a sequence
 ])
 def test_decode_validation(kw, status):
     assert _dec(**kw) == status
