@@ -142,6 +142,10 @@ SMALL = [
     ("bf16", 128, 8, 7, 1, [9, 250, 600]),
     ("f16", 128, 64, 16, 1, [1, 1000]),
     ("bf16", 128, 16, 32, 8, [1, 2, 1024, 3000]),
+    # large groups (one kv head for many q heads): several items per kv head
+    ("bf16", 128, 16, 64, 1, [1, 40, 700, 1500]),
+    ("f16", 64, 32, 48, 2, [3, 33, 900]),
+    ("f32", 64, 16, 32, 1, [5, 17, 300]),
 ]
 
 
