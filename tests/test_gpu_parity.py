@@ -572,6 +572,29 @@ def test_uniform_weights_give_mean_of_v(dtype, case, partition, kernel, waves):
     assert np.abs(ref - mean).max() <= 1e-12 * max(1.0, np.abs(mean).max())
 
 
+@pytest.mark.parametrize("dtype,scale", [("bf16", -0.0883883), ("bf16", 1.0), ("bf16", 8.0),
+                                         ("f16", 8.0), ("f32", -0.0883883)])
+@pytest.mark.parametrize("partition", [0, 32, "one-pass"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_negative_and_sharp_scales(dtype, scale, partition, kernel):
+    """The softmax scale is any real: negative (the weights favour the smallest
+    scores) or large enough that each row's weights are nearly one-hot (score spreads
+    of several hundred, most weights underflow, partition maxima far apart in the
+    merge).  Within the dtype's tolerance of the oracle."""
+    lens = [1, 31, 700, 2100]
+    max_ctx = -(-max(lens) // 16) * 16
+    p = {0: 0, 32: 32, "one-pass": max_ctx}[partition]
+    cfg = custom_config(f"sc-{dtype}", lens, 8, 2, 128, dtype, 16, seed=71, partition_size=p,
+                        scale=scale)
+    if kernel == "mfma" and dtype == "f32":  # the matrix-core kernel serves 16-bit caches only
+        _check_rejected(cfg, p, KERNELS[kernel])
+        return
+    wl, gs, st, res = _run_small(cfg, flags=KERNELS[kernel])
+    for out, ref, ref_abs in res:
+        assert torch.isfinite(out).all()
+        _check_decode(out, ref, dtype, ref_abs=ref_abs)
+
+
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_block_permutation_bit_identical(kernel):
     """Moving physical blocks (and remapping the table) does not change a bit."""
