@@ -51,6 +51,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary of this
+    workload, or None where there is none or it was taken on other kernel sources."""
+    tf = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(tf):
+        return None
+    rec = json.load(open(tf))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes")
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -845,12 +857,7 @@ def run(args):
         ratio = one_pass_ratio(args, wl, kcs, vcs, qs, bt, ctx, out, ws, p_used, flags)
     attainable = None if args.no_stream_probe else stream_probe(dev)
     same_bytes = None if args.no_size_probe else size_matched_probe(dev, kv, len(kcs))
-    traffic = None
-    tf = TRAFFIC_FILE.format(workload=c.name)
-    if os.path.exists(tf):
-        rec = json.load(open(tf))
-        if rec.get("kernel_source_hash") == kernel_source_hash():
-            traffic = rec.get("traffic_bytes")
+    traffic = measured_traffic(c.name)
 
     family = pa.decode_mq_kernel(Q, c.num_q_heads, c.num_kv_heads, qdt, kdt, flags)
     kname = f"decode_{family}_kernel"

@@ -1,0 +1,126 @@
+"""The benchmark's host logic, on the CPU: the one-GPU guard, the algorithmic bytes
+the roofline divides by, the counter post-processing (calibration against a plain
+copy, the per-step dispatches picked out of a whole run) and the gate that keeps
+counter figures taken on other kernel sources out of the JSON line."""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import shutil
+import statistics
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from pagedattention_kv_cache_amd.workloads import CONFIGS, DTYPE_BYTES, FP8_CONFIGS, Workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 2, r.stderr[-2000:]
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+@pytest.mark.parametrize("cfg", list(CONFIGS.values()) + list(FP8_CONFIGS.values()),
+                         ids=lambda c: c.name)
+def test_algorithmic_bytes(cfg):
+    """Each context position's key and value rows of every kv head, once; the counter
+    summary committed for the workload was taken over the same bytes."""
+    wl = Workload(cfg)
+    lens = wl.context_lens(0)
+    assert (lens >= 1).all() and (lens <= wl.max_blocks_per_seq * cfg.block_size).all()
+    per_token = cfg.num_kv_heads * cfg.head_dim * 2 * DTYPE_BYTES[cfg.kv_dtype]
+    assert wl.kv_bytes(0) == int(lens.sum()) * per_token
+    tf = bench.TRAFFIC_FILE.format(workload=cfg.name)
+    if os.path.exists(tf):
+        assert json.load(open(tf))["algorithmic_kv_bytes"] == wl.kv_bytes(0)
+
+
+def test_algorithmic_bytes_of_the_fixed_workload():
+    """Workload 1 has fixed lengths 1, 17, 64 and 200: 282 positions of 4 kv heads x 64
+    fp32 elements, keys and values."""
+    assert Workload(CONFIGS[1]).kv_bytes(0) == 282 * 4 * 64 * 2 * 4 == 577536
+
+
+def test_kernel_source_hash_follows_the_sources(tmp_path, monkeypatch):
+    src = os.path.join(ROOT, "pagedattention_kv_cache_amd")
+    dst = tmp_path / "pagedattention_kv_cache_amd"
+    (dst / "csrc").mkdir(parents=True)
+    for name in bench.KERNEL_SOURCES:
+        shutil.copy(os.path.join(src, "csrc", name), os.path.normpath(dst / "csrc" / name))
+    h = bench.kernel_source_hash()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.kernel_source_hash() == h
+    with open(dst / "csrc" / "decode_mfma.hip", "a") as f:
+        f.write("\n")
+    assert bench.kernel_source_hash() != h
+
+
+def test_traffic_is_reported_only_for_the_current_kernel_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic_{workload}.json"))
+    assert bench.measured_traffic("w") is None
+    rec = {"kernel_source_hash": bench.kernel_source_hash(), "traffic_bytes": 123.0}
+    (tmp_path / "traffic_w.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("w") == 123.0
+    rec["kernel_source_hash"] = "0" * 16
+    (tmp_path / "traffic_w.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("w") is None
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        for i, (kernel, grid, value) in enumerate(rows):
+            w.writerow([i + 1, kernel, grid, counter, value])
+
+
+DEC = "void pa::decode_mfma_kernel<(pa::Elem)2, 128, 16, 4, true>(pa::DecodeArgs)"
+PRO = "void pa::decode_prologue_kernel<4>(pa::DecodeArgs, int*, pa::CacheWriteArgs)"
+CW = "void pa::cache_write_kernel<4>(pa::CacheWriteArgs)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+@pytest.mark.parametrize("form", ["write+order", "separate write"])
+def test_counter_summary(tmp_path, monkeypatch, form):
+    """FETCH_SIZE / WRITE_SIZE in KiB per dispatch, scaled by what they read for the
+    calibration copy (the run's first copy); the decode's per-step dispatches are those
+    at its most frequent grid size, their median taken; the step's write is the kernel
+    that runs once per decode."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic_{workload}.json"))
+    mib = 1024
+    dec_f, dec_w = [1601000.0, 1604000.0, 1603000.0], [7400.0, 7600.0, 7500.0]
+    step_write = PRO if form == "write+order" else CW
+    fetch = [(COPY, 65536, mib * 1024 / 2.0), (COPY, 65536, 1.0),   # calibration copy first
+             (CW, 999936, 5.0e6), (CW, 999936, 4.0e6),                # set-up fills
+             (DEC, 1024, 9.9e9)]                                       # another grid: not a step
+    write = [(COPY, 65536, mib * 1024 * 1.0), (CW, 999936, 7.0e6), (DEC, 1024, 9.9e9)]
+    for f, w in zip(dec_f, dec_w):
+        fetch += [(step_write, 256, 3000.0), (DEC, 1536, f)]
+        write += [(step_write, 256, 3100.0), (DEC, 1536, w)]
+    fpath, wpath = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(fpath, "FETCH_SIZE", fetch)
+    _counter_csv(wpath, "WRITE_SIZE", write)
+    args = bench.parse_args(["--summarize-pmc", str(fpath), str(wpath), "--workload", "4",
+                             "--pmc-copy-mib", str(mib)])
+    res = bench.summarize_pmc(args)
+    assert res["fetch_scale"] == 2.0 and res["write_scale"] == 1.0
+    assert res["decode_fetch_bytes"] == statistics.median(dec_f) * 1024 * 2.0
+    assert res["decode_write_bytes"] == statistics.median(dec_w) * 1024 * 1.0
+    assert res["traffic_bytes"] == res["decode_fetch_bytes"] + res["decode_write_bytes"]
+    assert res["algorithmic_kv_bytes"] == Workload(CONFIGS[4]).kv_bytes(0)
+    cw = res["cache_write"]
+    assert cw["kernel"].startswith("decode_prologue" if form == "write+order" else "cache_write")
+    assert cw["fetch_bytes"] == 3000.0 * 1024 * 2.0 and cw["write_bytes"] == 3100.0 * 1024
+    c = CONFIGS[4]
+    assert cw["cache_bytes"] == c.num_seqs * c.num_kv_heads * c.head_dim * 2 * 2
+    saved = json.load(open(tmp_path / f"traffic_{c.name}.json"))
+    assert saved["kernel_source_hash"] == bench.kernel_source_hash()
+    assert saved["traffic_bytes"] == res["traffic_bytes"]
