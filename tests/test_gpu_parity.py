@@ -672,6 +672,35 @@ def test_blocks_past_4_gib_of_the_pool(kernel, cache):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("kernel,dtype,hq,hkv", [
+    ("valu", "bf16", 32, 8), ("mfma", "bf16", 32, 8), ("valu", "f16", 16, 2),
+    ("mfma", "f16", 16, 2), ("valu", "f32", 8, 2)])
+@pytest.mark.parametrize("partition", [32, "one-pass"])
+def test_gqa_equals_replicated_mha(kernel, dtype, hq, hkv, partition):
+    """q head hq reads kv head hq / g: the same decode as an MHA batch whose caches hold
+    every kv head g times over, bit for bit (a head's arithmetic does not depend on the
+    other heads of its item), and within tolerance of the oracle."""
+    cfg = custom_config(f"gqa-{dtype}", [1, 29, 300, 1100], hq, hkv, 128, dtype, 16, seed=81)
+    wl = Workload(cfg)
+    st = oracle_state_empty(wl)
+    gs = GpuState(wl, oracle_state=st)
+    gs.write_step(0)
+    st.write_step(0)
+    p = wl.max_blocks_per_seq * cfg.block_size if partition == "one-pass" else partition
+    flags = KERNELS[kernel] | pa.WAVES_2
+    out = gs.decode(0, partition_size=p, flags=flags)
+    g = hq // hkv
+    kc_mha = gs.kc.repeat_interleave(g, dim=1).contiguous()
+    vc_mha = gs.vc.repeat_interleave(g, dim=1).contiguous()
+    out_mha = torch.empty_like(out)
+    pa.decode(out_mha, gs.q[0], kc_mha, vc_mha, gs.block_tables, gs.ctx[0], cfg.attn_scale(),
+              cfg.block_size, p, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_mha)
+    ref_abs = st.decode_abs_values(0) if dtype == "f32" else None
+    _check_decode(out, st.decode(0), dtype, ref_abs=ref_abs)
+
+
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_partition_sweep_within_tolerance(kernel):
     cfg = custom_config("sweep", [1, 100, 1000, 4000], 8, 2, 128, "bf16", 16, seed=45)
