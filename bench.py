@@ -63,6 +63,26 @@ def measured_traffic(workload: str):
     return rec.get("traffic_bytes")
 
 
+def side_bytes(wl, queries: int = 1) -> dict:
+    """Bytes a decode step moves besides the KV stream, which alone is the
+    algorithmic figure: the queries, the fp32 outputs, the block-table entries and
+    context lengths the decode reads, and the cache write of one new token per
+    sequence (its rows read, the cache bytes written)."""
+    import numpy as np
+
+    from pagedattention_kv_cache_amd.workloads import DTYPE_BYTES
+    c = wl.cfg
+    lens = np.asarray(wl.context_lens(0), dtype=np.int64)
+    rows = c.num_seqs * queries * c.num_q_heads
+    new = c.num_seqs * c.num_kv_heads * c.head_dim * 2
+    return {"q": rows * c.head_dim * DTYPE_BYTES[c.dtype],
+            "out_f32": rows * c.head_dim * 4,
+            "block_tables": int(((lens + c.block_size - 1) // c.block_size).sum()) * 4,
+            "context_lens": 4 * c.num_seqs,
+            "cache_write_read": new * DTYPE_BYTES[c.dtype],
+            "cache_write_written": new * DTYPE_BYTES[c.kv_dtype]}
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -890,6 +910,7 @@ def run(args):
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(c.num_seqs * Q / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(kv),
+        "other_bytes_per_step": side_bytes(wl, Q),
         "write_ms": None if fused else round(write_ms, 5),
         "fused_write": fused,
         "step_form": ("write+order, decode kernel, merge" if split else

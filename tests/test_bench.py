@@ -49,6 +49,24 @@ def test_algorithmic_bytes_of_the_fixed_workload():
     assert Workload(CONFIGS[1]).kv_bytes(0) == 282 * 4 * 64 * 2 * 4 == 577536
 
 
+@pytest.mark.parametrize("cid,write", [(1, 8 << 10), (2, 1 << 20), (3, 640 << 10),
+                                       (4, 1 << 20), (5, 256 << 10)])
+def test_side_bytes(cid, write):
+    """The cache write moves 8 KiB, 1 MiB, 640 KiB, 1 MiB and 256 KiB per step on the five
+    workloads (one token per sequence: its key and value rows of every kv head); workload
+    1 reads 20 block-table entries (1, 2, 4 and 13 blocks of 16 tokens)."""
+    wl = Workload(CONFIGS[cid])
+    c = wl.cfg
+    sb = bench.side_bytes(wl)
+    assert sb["cache_write_read"] == sb["cache_write_written"] == write
+    assert sb["q"] == c.num_seqs * c.num_q_heads * c.head_dim * DTYPE_BYTES[c.dtype]
+    assert sb["out_f32"] == c.num_seqs * c.num_q_heads * c.head_dim * 4
+    assert sb["context_lens"] == 4 * c.num_seqs
+    if cid == 1:
+        assert sb["block_tables"] == 20 * 4 and sb["q"] == 4096
+    assert bench.side_bytes(wl, 4)["q"] == 4 * sb["q"]
+
+
 def test_kernel_source_hash_follows_the_sources(tmp_path, monkeypatch):
     src = os.path.join(ROOT, "pagedattention_kv_cache_amd")
     dst = tmp_path / "pagedattention_kv_cache_amd"
