@@ -191,8 +191,8 @@ def _step_values(rows, counter, pred):
 
 
 def _workload_cfg(args):
-    from pagedattention_kv_cache_amd.workloads import CONFIGS, FP8_CONFIGS
-    return FP8_CONFIGS[args.workload] if args.kv_cache == "fp8" else CONFIGS[args.workload]
+    from pagedattention_kv_cache_amd.workloads import WORKLOADS, FP8_WORKLOADS
+    return FP8_WORKLOADS[args.workload] if args.kv_cache == "fp8" else WORKLOADS[args.workload]
 
 
 def summarize_pmc(args):
@@ -689,7 +689,7 @@ def run(args):
     import torch
 
     import pagedattention_kv_cache_amd as pa
-    from pagedattention_kv_cache_amd.workloads import (CONFIGS, DTYPE_TORCH, FP8_CONFIGS,
+    from pagedattention_kv_cache_amd.workloads import (WORKLOADS, DTYPE_TORCH, FP8_WORKLOADS,
                                                        Workload)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -704,13 +704,13 @@ def run(args):
     pa.lib()
     dev = torch.device("cuda:0")
     if args.kv_cache == "fp8":
-        if args.workload not in FP8_CONFIGS:
+        if args.workload not in FP8_WORKLOADS:
             print(json.dumps({"error": f"no E4M3-cache variant of workload {args.workload}; "
-                              f"have {sorted(FP8_CONFIGS)}"}))
+                              f"have {sorted(FP8_WORKLOADS)}"}))
             sys.exit(2)
-        cfg = FP8_CONFIGS[args.workload]
+        cfg = FP8_WORKLOADS[args.workload]
     else:
-        cfg = CONFIGS[args.workload]
+        cfg = WORKLOADS[args.workload]
     wl = Workload(cfg)
     c = cfg
     flags = {"auto": pa.AUTO, "valu": pa.FORCE_VALU, "mfma": pa.FORCE_MFMA}[args.flags]

@@ -100,7 +100,7 @@ def _lognormal(median: float, sigma: float, lo: int, hi: int):
 # The five decode workloads, numbered 1..5.  Number 1 (4 fp32 sequences of at
 # most 200 tokens) is the small case the oracle finishes in seconds; number 4
 # (256 Llama-3-8B-shaped GQA sequences, bf16) is the throughput workload.
-CONFIGS: dict[int, DecodeConfig] = {
+WORKLOADS: dict[int, DecodeConfig] = {
     1: DecodeConfig("tiny-fp32", 4, 4, 4, 64, "f32", 16, seed=1,
                     lengths=_fixed([1, 17, 64, 200]), num_blocks=64),
     2: DecodeConfig("llama7b-mha-fp16", 64, 32, 32, 128, "f16", 16, seed=2,
@@ -118,7 +118,7 @@ def config3_long_first() -> DecodeConfig:
     """The skewed 13B-shaped batch (number 3) with its 4096-token sequence at
     batch index 0 instead of the last index; the short sequences' lengths are
     the same draws."""
-    return dataclasses.replace(CONFIGS[3], name="llama13b-skew-long-first-fp16",
+    return dataclasses.replace(WORKLOADS[3], name="llama13b-skew-long-first-fp16",
                                lengths=_skewed(16, 256, 4096, 0))
 
 
@@ -133,9 +133,9 @@ def fp8_variant(cfg: DecodeConfig, k_scale: float, v_scale: float) -> DecodeConf
 # E4M3-cache variants of the two GQA workloads (their KV are
 # N(0, 0.5^2) / N(0, 1) keys and N(0, 1) values: with these scales every drawn
 # value lands well inside the E4M3 range, the largest near 200).
-FP8_CONFIGS: dict[int, DecodeConfig] = {
-    4: fp8_variant(CONFIGS[4], 2.0 ** -6, 2.0 ** -5),
-    5: fp8_variant(CONFIGS[5], 2.0 ** -5, 2.0 ** -5),
+FP8_WORKLOADS: dict[int, DecodeConfig] = {
+    4: fp8_variant(WORKLOADS[4], 2.0 ** -6, 2.0 ** -5),
+    5: fp8_variant(WORKLOADS[5], 2.0 ** -5, 2.0 ** -5),
 }
 
 

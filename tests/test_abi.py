@@ -202,8 +202,8 @@ def test_decode_noalloc_empty_batch_is_noop():
 def test_decode_noalloc_scratch_covers_the_full_size_workloads():
     """PA_SCRATCH_BYTES (64 MiB) holds the partition workspace of every
     full-size decode workload in the launch configuration the benchmark uses."""
-    from pagedattention_kv_cache_amd.workloads import CONFIGS, DTYPE_TORCH, Workload
-    for cid, cfg in CONFIGS.items():
+    from pagedattention_kv_cache_amd.workloads import WORKLOADS, DTYPE_TORCH, Workload
+    for cid, cfg in WORKLOADS.items():
         wl = Workload(cfg)
         need = pa.decode_workspace_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
                                         cfg.head_dim, cfg.block_size, wl.max_blocks_per_seq,

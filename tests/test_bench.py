@@ -15,7 +15,7 @@ import sys
 import pytest
 
 import bench
-from pagedattention_kv_cache_amd.workloads import CONFIGS, DTYPE_BYTES, FP8_CONFIGS, Workload
+from pagedattention_kv_cache_amd.workloads import WORKLOADS, DTYPE_BYTES, FP8_WORKLOADS, Workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -28,7 +28,7 @@ def test_more_than_one_gpu_is_refused():
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
 
 
-@pytest.mark.parametrize("cfg", list(CONFIGS.values()) + list(FP8_CONFIGS.values()),
+@pytest.mark.parametrize("cfg", list(WORKLOADS.values()) + list(FP8_WORKLOADS.values()),
                          ids=lambda c: c.name)
 def test_algorithmic_bytes(cfg):
     """Each context position's key and value rows of every kv head, once; the counter
@@ -46,7 +46,7 @@ def test_algorithmic_bytes(cfg):
 def test_algorithmic_bytes_of_the_fixed_workload():
     """Workload 1 has fixed lengths 1, 17, 64 and 200: 282 positions of 4 kv heads x 64
     fp32 elements, keys and values."""
-    assert Workload(CONFIGS[1]).kv_bytes(0) == 282 * 4 * 64 * 2 * 4 == 577536
+    assert Workload(WORKLOADS[1]).kv_bytes(0) == 282 * 4 * 64 * 2 * 4 == 577536
 
 
 @pytest.mark.parametrize("cid,write", [(1, 8 << 10), (2, 1 << 20), (3, 640 << 10),
@@ -55,7 +55,7 @@ def test_side_bytes(cid, write):
     """The cache write moves 8 KiB, 1 MiB, 640 KiB, 1 MiB and 256 KiB per step on the five
     workloads (one token per sequence: its key and value rows of every kv head); workload
     1 reads 20 block-table entries (1, 2, 4 and 13 blocks of 16 tokens)."""
-    wl = Workload(CONFIGS[cid])
+    wl = Workload(WORKLOADS[cid])
     c = wl.cfg
     sb = bench.side_bytes(wl)
     assert sb["cache_write_read"] == sb["cache_write_written"] == write
@@ -133,11 +133,11 @@ def test_counter_summary(tmp_path, monkeypatch, form):
     assert res["decode_fetch_bytes"] == statistics.median(dec_f) * 1024 * 2.0
     assert res["decode_write_bytes"] == statistics.median(dec_w) * 1024 * 1.0
     assert res["traffic_bytes"] == res["decode_fetch_bytes"] + res["decode_write_bytes"]
-    assert res["algorithmic_kv_bytes"] == Workload(CONFIGS[4]).kv_bytes(0)
+    assert res["algorithmic_kv_bytes"] == Workload(WORKLOADS[4]).kv_bytes(0)
     cw = res["cache_write"]
     assert cw["kernel"].startswith("decode_prologue" if form == "write+order" else "cache_write")
     assert cw["fetch_bytes"] == 3000.0 * 1024 * 2.0 and cw["write_bytes"] == 3100.0 * 1024
-    c = CONFIGS[4]
+    c = WORKLOADS[4]
     assert cw["cache_bytes"] == c.num_seqs * c.num_kv_heads * c.head_dim * 2 * 2
     saved = json.load(open(tmp_path / f"traffic_{c.name}.json"))
     assert saved["kernel_source_hash"] == bench.kernel_source_hash()

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import pagedattention_kv_cache_amd as pa
-from pagedattention_kv_cache_amd.workloads import CONFIGS, Workload, custom_config, raw_bits
+from pagedattention_kv_cache_amd.workloads import WORKLOADS, Workload, custom_config, raw_bits
 from tests.gpu_harness import GpuState
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +49,7 @@ def _slots_status(slots, NB, bs):
 def test_clean_workloads_leave_the_word_zero(cid):
     """The five workloads' tables (-1 past each context), lengths and slots
     (prior context and every step) are within contract."""
-    wl = Workload(CONFIGS[cid])
+    wl = Workload(WORKLOADS[cid])
     c = wl.cfg
     bt = torch.from_numpy(wl.block_tables).cuda()
     for s in range(c.steps):

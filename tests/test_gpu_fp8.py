@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import pagedattention_kv_cache_amd as pa
-from pagedattention_kv_cache_amd.workloads import (FP8_CONFIGS, Workload, custom_config,
+from pagedattention_kv_cache_amd.workloads import (FP8_WORKLOADS, Workload, custom_config,
                                                    raw_bits)
 from tests.gpu_harness import (GpuState, assert_rejected, decode_kv, max_abs_err,
                                oracle_state_empty)
@@ -227,7 +227,7 @@ def test_full_workload_fp8_parity(cid):
     """The GQA workloads with E4M3 caches at full size, library-picked launch:
     every row of every step (8 steps of the long-context workload) against the
     oracle, and the whole pools bit for bit."""
-    cfg = FP8_CONFIGS[cid]
+    cfg = FP8_WORKLOADS[cid]
     wl = Workload(cfg)
     _say(f"full fp8 workload {cid} {cfg.name}: {wl.describe()}")
     st = oracle_state_empty(wl)

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import pagedattention_kv_cache_amd as pa
-from pagedattention_kv_cache_amd.workloads import (CONFIGS, DTYPE_TORCH, FP8_CONFIGS, Workload,
+from pagedattention_kv_cache_amd.workloads import (WORKLOADS, DTYPE_TORCH, FP8_WORKLOADS, Workload,
                                                    custom_config, raw_bits)
 from tests.gpu_harness import (GpuState, assert_rejected, max_abs_err, oracle_state_empty,
                                rowwise_rel_err)
@@ -244,7 +244,7 @@ def test_decode_mq_phases_match_one_call():
 def test_full_workload_mq_parity(cid, Q, fp8):
     """The GQA workloads at full size with Q query tokens per sequence (library-picked
     launch): every (sequence, query, head) row against the oracle."""
-    cfg = FP8_CONFIGS[cid] if fp8 else CONFIGS[cid]
+    cfg = FP8_WORKLOADS[cid] if fp8 else WORKLOADS[cid]
     wl = Workload(cfg)
     assert int(wl.context_lens(0).min()) >= Q
     _say(f"full mq workload {cfg.name} Q={Q}")

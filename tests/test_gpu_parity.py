@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import pagedattention_kv_cache_amd as pa
-from pagedattention_kv_cache_amd.workloads import (CONFIGS, Workload, config3_long_first,
+from pagedattention_kv_cache_amd.workloads import (WORKLOADS, Workload, config3_long_first,
                                                    custom_config, raw_bits)
 from tests.gpu_harness import (GpuState, assert_rejected, componentwise_rel_err, decode_kv,
                                max_abs_err, oracle_state_empty, rowwise_rel_err, write_kv)
@@ -786,7 +786,7 @@ def test_zero_length_sequence_gives_zero_row_and_empty_batch_is_noop():
 
 # ------------------------------------------------------------------ full-size workloads
 
-FULL = dict(CONFIGS)
+FULL = dict(WORKLOADS)
 # the skewed batch with its long sequence first instead of last (the first item
 # of grid order, the last dispatched partition of the others)
 FULL["3-long-first"] = config3_long_first()

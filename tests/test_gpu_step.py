@@ -137,7 +137,7 @@ def test_order_then_ordered_decode_fp8_and_refusals():
     """E4M3 caches: pa_decode_order without a write, then the ordered decode,
     equals pa_decode_fp8.  The ordered flag is refused where no order can have
     been prepared: multi-query decodes, steps, the allocation-free decode."""
-    from pagedattention_kv_cache_amd.workloads import FP8_CONFIGS  # noqa: F401
+    from pagedattention_kv_cache_amd.workloads import FP8_WORKLOADS  # noqa: F401
     cfg = custom_config("order-fp8", [3, 700, 1500, 2600], 32, 8, 128, "bf16", 16, seed=12,
                         cache_dtype="fp8", fp8_scales=(2.0 ** -6, 2.0 ** -5))
     wl = Workload(cfg)

@@ -18,7 +18,7 @@ import scipy.special
 import torch
 
 import oracle
-from pagedattention_kv_cache_amd.workloads import CONFIGS, Workload, custom_config, raw_bits
+from pagedattention_kv_cache_amd.workloads import WORKLOADS, Workload, custom_config, raw_bits
 from tests.paged_host import (OracleState, key_pool_shape, key_rows, logical_kv, offset_major,
                                poisoned_pool, value_pool_shape, value_rows)
 
@@ -404,7 +404,7 @@ def test_decode_rejects_bad_inputs():
 
 
 def test_config1_end_to_end_against_brute_force():
-    wl = Workload(CONFIGS[1])
+    wl = Workload(WORKLOADS[1])
     st = OracleState(wl)
     st.write_step(0)
     got = st.decode(0)
