@@ -472,9 +472,11 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * on `workspace` (the workspace it was given): the device's refinement where
  * the launch refines (see pa_decode_partition_size), read back from the
  * workspace with a copy on `stream` that the call waits for (a diagnostic, not
- * for a hot loop), else pa_decode_partition_size's value.  Before any such
- * launch on the workspace the value is pa_decode_partition_size's.  Negative
- * pa_status for invalid arguments or a workspace too small for the launch.
+ * for a hot loop), else pa_decode_partition_size's value.  Meaningful after
+ * such a launch on the workspace; a word holding none of the three candidates
+ * (p / 2, p, 2p), as a zeroed workspace does, reads as pa_decode_partition_size's
+ * value.  Negative pa_status for invalid arguments or a workspace too small for
+ * the launch.
  */
 int32_t pa_decode_partition_used(const void* workspace, size_t workspace_bytes,
                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
