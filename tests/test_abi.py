@@ -35,6 +35,16 @@ def _declared_functions(header=HEADER):
     return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libpa.so every entry point raises: there is no fallback path."""
+    monkeypatch.setattr(pa, "_lib", None)
+    monkeypatch.setattr(pa, "LIB_PATH", str(tmp_path / "libpa.so"))
+    with pytest.raises(RuntimeError, match="has not been built"):
+        pa.lib()
+    with pytest.raises(RuntimeError, match="has not been built"):
+        pa.decode_workspace_size(4, 32, 8, 128, 16, 64, 256, torch.bfloat16)
+
+
 def test_library_loads_and_exports_header_symbols():
     L = pa.lib()
     names = _declared_functions()
