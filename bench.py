@@ -57,7 +57,8 @@ def measured_traffic(workload: str):
     tf = TRAFFIC_FILE.format(workload=workload)
     if not os.path.exists(tf):
         return None
-    rec = json.load(open(tf))
+    with open(tf) as f:
+        rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("traffic_bytes")
